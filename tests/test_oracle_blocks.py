@@ -1,0 +1,132 @@
+"""Pins of the block-metadata oracle: closed forms, brute force, pruning soundness."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from gen import WORKLOADS, keep_set
+from oracle import attention as A
+from oracle import blocks as Bk
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tile_pairs(mask, i, j, block):
+    return mask[i * block : (i + 1) * block, j * block : (j + 1) * block]
+
+
+@pytest.mark.parametrize("T,block", [(64, 64), (179, 64), (1000, 64), (300, 128)])
+def test_identity_positions_closed_form(T, block):
+    pos = np.arange(T)
+    _, _, live, free = Bk.metadata(pos, pos, None, None, block)
+    n = Bk.n_blocks(T, block)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    np.testing.assert_array_equal(live, j <= i)
+    np.testing.assert_array_equal(free, j < i)
+
+
+def test_shared_increasing_keep_set_closed_form():
+    rng = np.random.default_rng(1)
+    keep = np.sort(rng.choice(5000, 1333, replace=False))
+    _, _, live, free = Bk.metadata(keep, keep, None, None, 64)
+    n = Bk.n_blocks(1333, 64)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    np.testing.assert_array_equal(live, j <= i)
+    np.testing.assert_array_equal(free, j < i)
+
+
+def test_workload1_golden_lists():
+    g = json.load(open(os.path.join(GOLDEN, "workload1_blocks.json")))
+    keep, _ = keep_set(WORKLOADS[1], 0, 0)
+    assert keep.shape == (g["Tq"],)
+    qs, ks, live, free = Bk.metadata(keep, keep, None, None, g["block"])
+    assert [min(g["block"], g["Tq"] - b * g["block"]) for b in range(qs.shape[0])] == g["block_rows"]
+    assert Bk.row_lists(live, free) == [[tuple(e) for e in r] for r in g["row_lists"]]
+    assert Bk.col_lists(live, free) == [[tuple(e) for e in r] for r in g["col_lists"]]
+    assert int(live.sum()) == g["live_tiles"]
+
+
+def _random_case(rng, hashed, Tq, Tk, nb=4, sort_by_hash=True):
+    qi = np.sort(rng.choice(3 * max(Tq, Tk), Tq, replace=False))
+    ki = np.sort(rng.choice(3 * max(Tq, Tk), Tk, replace=False))
+    qh = kh = None
+    if hashed:
+        qh, kh = rng.integers(0, nb, Tq), rng.integers(0, nb, Tk)
+        if sort_by_hash:
+            oq, ok = np.lexsort((qi, qh)), np.lexsort((ki, kh))
+            qi, qh, ki, kh = qi[oq], qh[oq], ki[ok], kh[ok]
+    return qi, ki, qh, kh
+
+
+@pytest.mark.parametrize("hashed", [False, True])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_liveness_is_sound_and_maskfree_is_exact(hashed, seed):
+    """Every tile holding an admissible pair is live; mask-free iff all real pairs admissible."""
+    rng = np.random.default_rng(seed)
+    Tq, Tk, block = 333, 291, 32
+    qi, ki, qh, kh = _random_case(rng, hashed, Tq, Tk, sort_by_hash=(seed != 2))
+    mask = A.element_mask(qi, ki, qh, kh)
+    _, _, live, free = Bk.metadata(qi, ki, qh, kh, block)
+    for i in range(live.shape[0]):
+        for j in range(live.shape[1]):
+            t = _tile_pairs(mask, i, j, block)
+            if t.any():
+                assert live[i, j]
+            assert free[i, j] == bool(t.all())
+            if free[i, j]:
+                assert live[i, j]
+    if not hashed:
+        # without buckets the block rule is exact: live iff some pair admissible
+        for i in range(live.shape[0]):
+            for j in range(live.shape[1]):
+                assert live[i, j] == bool(_tile_pairs(mask, i, j, block).any())
+
+
+def test_single_bucket_blocks_make_liveness_exact():
+    """When every block holds one bucket, live iff the tile holds an admissible pair."""
+    rng = np.random.default_rng(8)
+    block = 16
+    qh = np.repeat(rng.integers(0, 3, 12), block)
+    kh = np.repeat(rng.integers(0, 3, 12), block)
+    qi = rng.permutation(400)[: qh.size]
+    ki = rng.permutation(400)[: kh.size]
+    mask = A.element_mask(qi, ki, qh, kh)
+    _, _, live, _ = Bk.metadata(qi, ki, qh, kh, block)
+    for i in range(12):
+        for j in range(12):
+            assert live[i, j] == bool(_tile_pairs(mask, i, j, block).any())
+
+
+@pytest.mark.parametrize("hashed", [False, True])
+def test_pruned_evaluation_equals_full_mask(hashed):
+    rng = np.random.default_rng(12 + hashed)
+    Tq, Tk, d, block = 410, 390, 16, 64
+    qi, ki, qh, kh = _random_case(rng, hashed, Tq, Tk, nb=6)
+    q, k, v = (rng.standard_normal((n, d)) for n in (Tq, Tk, Tk))
+    o, lse = A.forward(q, k, v, qi, ki, qh, kh)
+    o2, lse2 = Bk.forward_live_tiles_only(q, k, v, qi, ki, qh, kh, block)
+    np.testing.assert_allclose(o2, o, atol=1e-12, rtol=0)
+    finite = np.isfinite(lse)
+    np.testing.assert_array_equal(np.isfinite(lse2), finite)
+    np.testing.assert_allclose(lse2[finite], lse[finite], atol=1e-12, rtol=0)
+
+
+def test_block_stats_use_real_rows_only():
+    idx = np.array([5, 1, 9, 3, 7, 2, 8])
+    hs = np.array([2, 2, 0, 1, 3, 3, 1])
+    st = Bk.block_stats(idx, hs, 3)
+    np.testing.assert_array_equal(st, [[1, 9, 0, 2], [2, 7, 1, 3], [8, 8, 1, 1]])
+
+
+def test_lists_are_ascending_and_consistent():
+    rng = np.random.default_rng(4)
+    qi, ki, qh, kh = _random_case(rng, True, 500, 500, nb=3)
+    _, _, live, free = Bk.metadata(qi, ki, qh, kh, 32)
+    rows, cols = Bk.row_lists(live, free), Bk.col_lists(live, free)
+    pairs_r = {(i, j, f) for i, r in enumerate(rows) for j, f in r}
+    pairs_c = {(i, j, f) for j, c in enumerate(cols) for i, f in c}
+    assert pairs_r == pairs_c and len(pairs_r) == int(live.sum())
+    for r in rows:
+        assert [j for j, _ in r] == sorted(j for j, _ in r)
