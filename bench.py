@@ -1,0 +1,306 @@
+"""Benchmark: one Hash-sparse SCFA training step per iteration on one MI355X.
+
+Workload (synthetic, seeded): B=2, H=12, T=16384, d=64, 32 LSH buckets,
+block 64, bf16 -- the GPT-2-small attention shape at 16k tokens.  One step is
+the whole hot path over one batch, with every input already in HBM:
+
+  LSH bucket ids + (bucket, position) sort of Q (dO gathered alongside),
+  the same for K (V gathered alongside), block metadata (row and column
+  live-tile lists), forward, backward dQ (+ rowsum(dO*O)), backward dK/dV.
+
+Reported value: effective TFLOP/s on executed tiles (forward 4*bq*bk*d and
+backward 10*bq*bk*d flops per executed tile of real extent bq x bk) over the
+whole step.  Also reported: the same library's dense causal forward+backward
+at the original shape and the speedup over it, per-kernel HIP-event times, the
+roofline of the dominant kernel, and the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
+PEAK_FP64_TFLOPS = 78.6  # MI355X fp64 vector (published)
+WORKLOAD_ID = 4
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_inputs(w, torch):
+    import numpy as np
+
+    from gen import head_inputs, lsh_rotation
+
+    heads = [[head_inputs(w, b, h) for h in range(w.H)] for b in range(w.B)]
+
+    def st(f):
+        return np.stack([np.stack([f(x) for x in row]) for row in heads])
+
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
+    q, k, v, do = to(st(lambda x: x.q)), to(st(lambda x: x.k)), to(st(lambda x: x.v)), to(st(lambda x: x.do))
+    R = torch.from_numpy(np.stack([lsh_rotation(w, h) for h in range(w.H)])).to(dev)
+    return q, k, v, do, R
+
+
+def tile_work(meta, Tq, Tk, block, torch):
+    """Sum over executed tiles of bq*bk (real extents), from the row lists."""
+    cnt = meta["row_count"].long()  # [B,H,nq]
+    lst = meta["row_list"].long() & 0x7FFFFFFF  # [B,H,nq,nk]
+    nq, nk = lst.shape[2], lst.shape[3]
+    valid = torch.arange(nk, device=lst.device)[None, None, None, :] < cnt[..., None]
+    bq = torch.clamp(Tq - torch.arange(nq, device=lst.device) * block, max=block)  # [nq]
+    bk_all = torch.clamp(Tk - torch.arange(nk, device=lst.device) * block, max=block)  # [nk]
+    bk = bk_all[lst.clamp(max=nk - 1)] * valid
+    return int((bk.sum(-1) * bq[None, None, :]).sum().item()), int(cnt.sum().item())
+
+
+class Timer:
+    """HIP events between the calls of one step (torch's current stream, which the library uses)."""
+
+    def __init__(self, torch, names):
+        self.torch = torch
+        self.names = names
+        self.samples = {n: [] for n in names}
+        self.pending = []
+
+    def begin(self):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pending.append([ev])
+
+    def mark(self):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pending[-1].append(ev)
+
+    def collect(self):
+        for evs in self.pending:
+            for n, a, b in zip(self.names, evs[:-1], evs[1:]):
+                self.samples[n].append(a.elapsed_time(b))
+        self.pending = []
+
+    def mean_ms(self, n):
+        s = self.samples[n]
+        return sum(s) / len(s) if s else float("nan")
+
+
+def run_step(scfa, w, q, k, v, do, R, timer=None):
+    nb, blk, sc = w.n_buckets, w.block, w.scale
+    if timer:
+        timer.begin()
+    qh, qi, _, qs, dos = scfa.lsh_bucket_sort(q, R, nb, companion=do)
+    if timer:
+        timer.mark()
+    kh, ki, _, ks, vs = scfa.lsh_bucket_sort(k, R, nb, companion=v)
+    if timer:
+        timer.mark()
+    meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=True)
+    if timer:
+        timer.mark()
+    o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc)
+    if timer:
+        timer.mark()
+    dq, delta = scfa.attn_bwd_dq_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, block=blk, scale=sc)
+    if timer:
+        timer.mark()
+    dk, dv = scfa.attn_bwd_dkdv_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, block=blk, scale=sc)
+    if timer:
+        timer.mark()
+    return meta, (o, lse, dq, dk, dv)
+
+
+STEP_CALLS = ["lsh_sort_q", "lsh_sort_k", "block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
+
+
+def run_dense(scfa, w, q, k, v, do, timer=None):
+    blk, sc = w.block, w.scale
+    if timer:
+        timer.begin()
+    o, lse = scfa.attn_fwd_lists(q, k, v, None, None, None, None, None, block=blk, scale=sc)
+    if timer:
+        timer.mark()
+    dq, delta = scfa.attn_bwd_dq_lists(q, k, v, o, lse, do, None, None, None, None, None, block=blk, scale=sc)
+    if timer:
+        timer.mark()
+    scfa.attn_bwd_dkdv_lists(q, k, v, lse, do, delta, None, None, None, None, None, block=blk, scale=sc)
+    if timer:
+        timer.mark()
+
+
+DENSE_CALLS = ["dense_fwd", "dense_bwd_dq", "dense_bwd_dkdv"]
+
+
+def cpu_baseline(w, tile_units_per_head):
+    """The fp64 oracle on one head of the workload (LSH, sort, masked attention fwd + bwd)."""
+    import numpy as np
+
+    from gen import head_inputs, lsh_rotation
+    from oracle import attention as A
+    from oracle import lsh
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    hi = head_inputs(w, 0, 0)
+    R = lsh_rotation(w, 0)
+    t0 = time.perf_counter()
+    bq, bk = lsh.buckets(hi.q, R), lsh.buckets(hi.k, R)
+    pq, hq, iq = lsh.bucket_sort(bq, hi.q_pos)
+    pk, hk, ik = lsh.bucket_sort(bk, hi.k_pos)
+    A.forward(hi.q[pq], hi.k[pk], hi.v[pk], iq, ik, hq, hk, w.scale)
+    A.backward(hi.q[pq], hi.k[pk], hi.v[pk], hi.do[pq], iq, ik, hq, hk, w.scale)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * tile_units_per_head * w.d
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"one head (b=0, h=0) of the workload: LSH + sort of Q and K, dense masked fp64 forward "
+                  f"and backward over {w.T} tokens; {dt:.2f} s, credited with that head's executed-tile flops",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the hot path has no multi-GPU code); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_causal_attention_amd as scfa
+    from gen import WORKLOADS
+
+    w = WORKLOADS[WORKLOAD_ID]
+    _log(f"[bench] workload {w.name}: generating inputs")
+    q, k, v, do, R = make_inputs(w, torch)
+    torch.cuda.synchronize()
+
+    _log("[bench] warmup")
+    for _ in range(args.warmup):
+        run_step(scfa, w, q, k, v, do, R)
+    torch.cuda.synchronize()
+
+    _log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        meta, _ = run_step(scfa, w, q, k, v, do, R)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # per-call HIP-event times (separate pass so the events do not sit in the wall-clock region)
+    timer = Timer(torch, STEP_CALLS)
+    for _ in range(args.steps):
+        meta, _ = run_step(scfa, w, q, k, v, do, R, timer)
+    torch.cuda.synchronize()
+    timer.collect()
+
+    units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
+    step_flops = 14.0 * units * w.d
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    _log("[bench] dense causal reference")
+    dtimer = Timer(torch, DENSE_CALLS)
+    for _ in range(max(1, args.warmup)):
+        run_dense(scfa, w, q, k, v, do)
+    torch.cuda.synchronize()
+    nd = max(3, args.steps // 4)
+    t1 = time.perf_counter()
+    for _ in range(nd):
+        run_dense(scfa, w, q, k, v, do)
+    torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - t1) / nd * 1e3
+    for _ in range(nd):
+        run_dense(scfa, w, q, k, v, do, dtimer)
+    torch.cuda.synchronize()
+    dtimer.collect()
+
+    per_call = {n: round(timer.mean_ms(n), 4) for n in STEP_CALLS}
+    attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
+    # algorithmic flops per launch of each attention kernel (tile units x d)
+    kernel_flops = {"fwd": 4.0 * units * w.d, "bwd_dq": 6.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
+    dominant = max(kernel_flops, key=lambda n: per_call[n])
+    achieved = kernel_flops[dominant] / (per_call[dominant] * 1e-3) / 1e12
+    roofline = {
+        "kernel": {"fwd": "k_fwd_bf16<kHash,64,64>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64>",
+                   "bwd_dkdv": "k_bwd_dkdv_bf16<kHash,64,64>"}[dominant],
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+        "avg_launch_ms": per_call[dominant],
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("[bench] cpu oracle baseline (one head)")
+        cpu = cpu_baseline(w, units / (w.B * w.H))
+
+    out = {
+        "metric": "effective TFLOP/s (executed tiles, % bf16 MFMA peak) + speedup vs dense causal",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, seeded Gaussian LSH rotations)",
+        "config": {
+            "workload": w.name,
+            "B": w.B,
+            "H": w.H,
+            "T": w.T,
+            "d": w.d,
+            "block": w.block,
+            "n_buckets": w.n_buckets,
+            "step": "lsh+sort(Q,dO) + lsh+sort(K,V) + block lists + fwd + bwd",
+        },
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "executed_tiles": tiles,
+        "dense_causal_tiles": w.B * w.H * (w.T // w.block) * (w.T // w.block + 1) // 2,
+        "attention_only_tflops": round(step_flops / (attn_ms * 1e-3) / 1e12, 3),
+        "dense_causal_ms": round(dense_ms, 4),
+        "speedup_vs_dense_causal": round(dense_ms / ms_per_step, 3),
+        "speedup_vs_dense_causal_excl_lsh": round(dense_ms / attn_ms, 3),
+        "per_call_ms": per_call,
+        "dense_per_call_ms": {n: round(dtimer.mean_ms(n), 4) for n in DENSE_CALLS},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

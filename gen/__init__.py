@@ -15,4 +15,6 @@ from .workloads import (  # noqa: F401
     head_inputs,
     lsh_rotation,
     keep_set,
+    SyntheticCase,
+    synthetic_case,
 )

@@ -172,3 +172,85 @@ def head_inputs(w: Workload, b: int, h: int, *, with_do: Optional[bool] = None) 
         if do is not None:
             do = bf16_round(do)
     return HeadInputs(q=q, k=k, v=v, do=do, q_pos=q_pos, k_pos=k_pos)
+
+
+@dataclasses.dataclass
+class SyntheticCase:
+    """Arrays [B, H, ...] for a small attention case (float32 values, bf16-exact if bf16)."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    q_idx: Optional[np.ndarray]
+    k_idx: Optional[np.ndarray]
+    q_hash: Optional[np.ndarray]
+    k_hash: Optional[np.ndarray]
+    dtype: str
+
+
+def _grouped(rng, T_orig, n, nb, layout):
+    """n distinct positions of [0, T_orig) with random bucket ids in [0, nb).
+
+    layout "grouped": rows listed bucket by bucket, positions ascending inside a
+    bucket (the layout LSH reordering produces); "ascending": positions
+    ascending; "shuffled": random row order.
+    """
+    pos = np.sort(rng.choice(T_orig, n, replace=False)).astype(np.int32)
+    hs = rng.integers(0, nb, n).astype(np.int32) if nb else np.zeros(n, np.int32)
+    if layout == "grouped":
+        rows = np.concatenate([np.nonzero(hs == c)[0] for c in range(max(nb, 1))])
+    elif layout == "shuffled":
+        rows = rng.permutation(n)
+    else:
+        rows = np.arange(n)
+    return pos[rows], hs[rows]
+
+
+def synthetic_case(
+    seed: int,
+    *,
+    B: int = 1,
+    H: int = 1,
+    Tq: int,
+    Tk: int,
+    d: int = 64,
+    dtype: str = "bf16",
+    mode: str = "qk",  # "dense", "qk" or "hash"
+    nb: int = 0,
+    layout: str = "ascending",
+    shared: bool = False,
+    T_orig: Optional[int] = None,
+) -> SyntheticCase:
+    """Seeded Gaussian Q/K/V/dO with random original positions and bucket ids.
+
+    ``shared`` uses one position (and bucket) vector for Q and K (requires
+    Tq == Tk).  Dense mode returns no positions (the library then uses row
+    numbers).
+    """
+    g = _rng(seed, 4)
+    if T_orig is None:
+        T_orig = 2 * max(Tq, Tk, 1)
+    q = g.standard_normal((B, H, Tq, d), dtype=np.float32)
+    k = g.standard_normal((B, H, Tk, d), dtype=np.float32)
+    v = g.standard_normal((B, H, Tk, d), dtype=np.float32)
+    do = g.standard_normal((B, H, Tq, d), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v, do = (bf16_round(a) for a in (q, k, v, do))
+    if mode == "dense":
+        return SyntheticCase(q, k, v, do, None, None, None, None, dtype)
+    qi = np.zeros((B, H, Tq), np.int32)
+    ki = np.zeros((B, H, Tk), np.int32)
+    qh = np.zeros((B, H, Tq), np.int32)
+    kh = np.zeros((B, H, Tk), np.int32)
+    nbk = nb if mode == "hash" else 0
+    for b in range(B):
+        for h in range(H):
+            qi[b, h], qh[b, h] = _grouped(g, T_orig, Tq, nbk, layout)
+            if shared:
+                ki[b, h], kh[b, h] = qi[b, h], qh[b, h]
+            else:
+                ki[b, h], kh[b, h] = _grouped(g, T_orig, Tk, nbk, layout)
+    if mode == "qk":
+        return SyntheticCase(q, k, v, do, qi, ki, None, None, dtype)
+    return SyntheticCase(q, k, v, do, qi, ki, qh, kh, dtype)

@@ -1,0 +1,258 @@
+/*
+ * scfa.h - C ABI of the MI355X (gfx950) sparse causal flash attention library.
+ *
+ * Sparse Causal Flash Attention (SCFA) is tiled, online-softmax causal
+ * attention over COMPACTED tensors: rows of Q, K and V may have been dropped
+ * or reordered, and every row carries its ORIGINAL position (q_idx, k_idx) and,
+ * in Hash-sparse mode, an LSH bucket id (q_hash, k_hash).  Source: the
+ * deep-paper.org summary of arXiv 2306.01160, "Faster Causal Attention Over
+ * Large Sequences Through Sparse Flash Attention" (page title
+ * "超越 FlashAttention：利用动态稀疏性让 Transformer 再提速"), sections
+ * "SCFA solution > 1. QK-Sparse" and "2. Hash-Sparse".
+ *
+ * What every attention entry point computes, per (batch b, head h):
+ *   valid(i, j) = k_idx[j] <= q_idx[i]                 (causality on original
+ *                                                       positions, "1. QK-Sparse"
+ *                                                       rule 2; a token sees itself)
+ *               && q_hash[i] == k_hash[j]              (Hash-sparse only,
+ *                                                       "2. Hash-Sparse" rule 3)
+ *   O[i]   = sum_j softmax_j(scale * q_i . k_j over valid j) v_j
+ *   lse[i] = log sum_{valid j} exp(scale * q_i . k_j)   (natural log)
+ *   A row with no valid key gets O[i] = 0 and lse[i] = -inf (the page leaves
+ *   this case open; this is the library's definition).
+ * Tiles of `block` query rows x `block` key rows are skipped when every query
+ * precedes every key ("1. QK-Sparse" rule 1) or, in Hash-sparse mode, when the
+ * two blocks' bucket ranges do not overlap ("2. Hash-Sparse" rules 1-2); the
+ * skipped tiles hold no valid pair, so the result is exact.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Memory.  Every data pointer is DEVICE memory owned by the caller.  The
+ *   library never allocates, never frees, keeps no state between calls, and is
+ *   safe to call from several host threads.  Scratch memory comes from the
+ *   caller's `workspace` (device memory, >= scfa_workspace_size(...) bytes,
+ *   256-byte aligned); it may be reused freely between calls that are ordered
+ *   on one stream.
+ * Layout.  Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, T, d] (d fastest),
+ *   16-byte aligned.  q_idx, q_hash, lse are contiguous [B, H, Tq]; k_idx,
+ *   k_hash are [B, H, Tk]; all int32 or float32, 4-byte aligned.
+ * Values.  Original positions satisfy 0 <= idx < 2147483647.  Bucket ids are
+ *   any int32 (attention only compares them).  Inputs need not be sorted by
+ *   position or bucket: sorting only changes speed, never the result.
+ * Types.  dtype SCFA_DTYPE_BF16: tensors are bfloat16, products accumulate in
+ *   float32 on the matrix cores, softmax is float32, P is rounded to bf16
+ *   before the P.V product, outputs are rounded once.  SCFA_DTYPE_FP32: every
+ *   tensor and every operation is float32.
+ * Supported sizes.  d in {64, 128}; block in {64, 128}; B, H >= 1; Tq, Tk >= 0
+ *   with B*H*max(Tq,Tk)*d < 2^31; scale finite and > 0 (the usual choice is
+ *   1/sqrt(d)).
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *   enqueued asynchronously; the call returns without synchronising and
+ *   device-side faults surface at the caller's next synchronisation.
+ * Errors.  Every argument is validated on the host before anything is
+ *   enqueued.  On a non-zero status nothing has been enqueued and every output
+ *   is untouched (except SCFA_ERR_HIP, raised by a failing launch, after
+ *   which earlier kernels of the same call may have run).
+ *   scfa_last_error() returns a message for the calling thread's last error.
+ */
+#ifndef SCFA_H
+#define SCFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SCFA_OK 0
+#define SCFA_ERR_INVALID_ARGUMENT 1   /* null pointer, bad size, misalignment */
+#define SCFA_ERR_UNSUPPORTED 2        /* d, block, dtype or n_buckets outside the supported set */
+#define SCFA_ERR_WORKSPACE_TOO_SMALL 3
+#define SCFA_ERR_HIP 4                /* a HIP launch failed; see scfa_last_error() */
+
+/* Element types. */
+#define SCFA_DTYPE_BF16 0
+#define SCFA_DTYPE_FP32 1
+
+/* Flags (bitwise OR). */
+#define SCFA_FLAG_NO_PRUNE (1u << 0)      /* visit every tile, masking each one; the result is
+                                             bit-identical to the pruned run (test aid) */
+#define SCFA_FLAG_FORCE_MASK (1u << 1)    /* apply the element mask on mask-free tiles too;
+                                             bit-identical results (test aid) */
+#define SCFA_FLAG_IDX_ASCENDING (1u << 2) /* scfa_lsh_bucket_sort: the caller guarantees idx is
+                                             strictly ascending within each (b, h), which lets the
+                                             sort run one pass instead of five */
+
+/* Operation ids for scfa_workspace_size. */
+#define SCFA_OP_QK_FWD 0
+#define SCFA_OP_QK_BWD 1
+#define SCFA_OP_HASH_FWD 2
+#define SCFA_OP_HASH_BWD 3
+#define SCFA_OP_LSH_SORT 4
+
+/*
+ * QK-sparse forward ("1. QK-Sparse": compact Q/K/V plus the original indices
+ * of the kept queries and keys).
+ *   q [B,H,Tq,d], k and v [B,H,Tk,d] (dtype); q_idx [B,H,Tq], k_idx [B,H,Tk].
+ *   Passing q_idx == k_idx == NULL selects dense causal attention with
+ *   positions 0..Tq-1 and 0..Tk-1 (the library's dense-causal baseline; it needs
+ *   no workspace).  Exactly one of them NULL is an error.
+ *   Outputs: o [B,H,Tq,d] (dtype), lse [B,H,Tq] float32, natural log.
+ */
+int scfa_qk_sparse_fwd(const void *q, const void *k, const void *v,
+                       const int32_t *q_idx, const int32_t *k_idx,
+                       void *o, float *lse,
+                       int B, int H, int Tq, int Tk, int d, int block, float scale,
+                       int dtype, unsigned flags,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * QK-sparse backward: gradients of sum(O * dout) with respect to q, k, v,
+ * recomputing P from the forward's lse (no T x T state is kept).
+ *   o and lse must be the forward's outputs for the same inputs; dout is
+ *   [B,H,Tq,d].  Outputs dq [B,H,Tq,d], dk and dv [B,H,Tk,d] (dtype), fully
+ *   overwritten.  Rows with no valid key contribute nothing.
+ */
+int scfa_qk_sparse_bwd(const void *q, const void *k, const void *v,
+                       const void *o, const float *lse, const void *dout,
+                       const int32_t *q_idx, const int32_t *k_idx,
+                       void *dq, void *dk, void *dv,
+                       int B, int H, int Tq, int Tk, int d, int block, float scale,
+                       int dtype, unsigned flags,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Hash-sparse forward ("2. Hash-Sparse": original indices plus bucket ids;
+ * attention is exact within buckets).  Same as scfa_qk_sparse_fwd plus
+ * q_hash [B,H,Tq] and k_hash [B,H,Tk] (required, int32).  q_idx and k_idx are
+ * required here.
+ */
+int scfa_hash_sparse_fwd(const void *q, const void *k, const void *v,
+                         const int32_t *q_idx, const int32_t *k_idx,
+                         const int32_t *q_hash, const int32_t *k_hash,
+                         void *o, float *lse,
+                         int B, int H, int Tq, int Tk, int d, int block, float scale,
+                         int dtype, unsigned flags,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Hash-sparse backward; arguments as scfa_qk_sparse_bwd plus q_hash, k_hash. */
+int scfa_hash_sparse_bwd(const void *q, const void *k, const void *v,
+                         const void *o, const float *lse, const void *dout,
+                         const int32_t *q_idx, const int32_t *k_idx,
+                         const int32_t *q_hash, const int32_t *k_hash,
+                         void *dq, void *dk, void *dv,
+                         int B, int H, int Tq, int Tk, int d, int block, float scale,
+                         int dtype, unsigned flags,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * LSH bucketing and the (bucket, original position) reordering that feeds
+ * Hash-sparse attention ("why dynamic sparsity breaks it": LSH groups similar
+ * tokens into buckets; tokens reordered by hash keep their original positions
+ * for causality).
+ *   x [B,H,T,d] (dtype) in any row order; idx [B,H,T] int32 original positions
+ *   of the rows (NULL = 0..T-1); R [H,d,n_buckets/2] float32, one random
+ *   rotation per head shared by the batch.
+ *   bucket(x) = first index of the maximum of [x.R, -x.R], where each x.R[:,c]
+ *   is accumulated in float64 in increasing coordinate order (products of a
+ *   bf16/fp32 by an fp32 are exact in float64, so the result is bit-exact and
+ *   reproducible).  n_buckets is even, 2 <= n_buckets <= 1024.
+ *   Rows are then ordered by (bucket, idx) ascending (unique: positions are
+ *   distinct within a sequence).  Outputs [B,H,T] int32:
+ *     perm[s]        = source row of sorted slot s,
+ *     hash_sorted[s] = bucket(x[perm[s]]),  idx_sorted[s] = idx[perm[s]].
+ *   x_sorted (nullable) receives x[perm] and companion_sorted (nullable)
+ *   receives companion[perm] for a second [B,H,T,d] tensor of the same dtype
+ *   (e.g. V with K's order, or dO with Q's order).
+ *   flags: SCFA_FLAG_IDX_ASCENDING as above (implied when idx is NULL).
+ */
+int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int n_buckets,
+                         int B, int H, int T, int d, int dtype, unsigned flags,
+                         int32_t *hash_sorted, int32_t *idx_sorted, int32_t *perm,
+                         void *x_sorted, const void *companion, void *companion_sorted,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Block metadata, exposed for inspection and bit-exact testing.  Block b of a
+ * sequence covers compact rows [b*block, min((b+1)*block, T)).
+ *   q_stats [B,H,nq,4], k_stats [B,H,nk,4] int32: (min idx, max idx, min hash,
+ *   max hash) over the block's real rows (hash entries 0 without hashes).
+ *   Tile (i,j) is live iff qmax_idx(i) >= kmin_idx(j) and, with hashes, the
+ *   bucket ranges [min,max] of blocks i and j overlap ("1. QK-Sparse" rule 1,
+ *   "2. Hash-Sparse" rules 1-2).  It is mask-free iff kmax_idx(j) <=
+ *   qmin_idx(i) and, with hashes, both blocks hold one and the same bucket.
+ *   row_count [B,H,nq]; row_list [B,H,nq,nk]: the first row_count entries of
+ *   each row are the live key blocks j, ascending, each stored as
+ *   j | (mask_free << 31); the rest of the row is unspecified.
+ *   col_count [B,H,nk]; col_list [B,H,nk,nq]: the same per key block (query
+ *   blocks i ascending).  col_count/col_list may both be NULL.
+ *   q_hash and k_hash are both NULL (QK-sparse) or both non-NULL.
+ */
+int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx,
+                    const int32_t *q_hash, const int32_t *k_hash,
+                    int B, int H, int Tq, int Tk, int block,
+                    int32_t *q_stats, int32_t *k_stats,
+                    int32_t *row_count, int32_t *row_list,
+                    int32_t *col_count, int32_t *col_list, void *stream);
+
+/*
+ * Attention over precomputed block lists: the single-kernel building blocks of
+ * the entry points above.  A training step can build the lists once with
+ * scfa_block_meta (with columns) and share them between the forward and both
+ * backward kernels; each call below enqueues exactly one kernel and needs no
+ * workspace.
+ *   Mode: q_idx == k_idx == NULL selects dense causal (lists ignored, may be
+ *   NULL); q_hash == k_hash == NULL selects QK-sparse; otherwise Hash-sparse.
+ *   row_count/row_list and col_count/col_list must be scfa_block_meta's output
+ *   for the same positions, buckets and block (list entries naming a block
+ *   outside the sequence are skipped, never dereferenced).
+ *   Other arguments, layouts and flags as in scfa_*_sparse_fwd / _bwd.
+ */
+int scfa_attn_fwd_lists(const void *q, const void *k, const void *v,
+                        const int32_t *q_idx, const int32_t *k_idx,
+                        const int32_t *q_hash, const int32_t *k_hash,
+                        const int32_t *row_count, const int32_t *row_list,
+                        void *o, float *lse,
+                        int B, int H, int Tq, int Tk, int d, int block, float scale,
+                        int dtype, unsigned flags, void *stream);
+
+/* Backward, first kernel: dq [B,H,Tq,d] and delta [B,H,Tq] float32 =
+ * rowsum(dout * o), which the second kernel reads. */
+int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v,
+                           const void *o, const float *lse, const void *dout,
+                           const int32_t *q_idx, const int32_t *k_idx,
+                           const int32_t *q_hash, const int32_t *k_hash,
+                           const int32_t *row_count, const int32_t *row_list,
+                           void *dq, float *delta,
+                           int B, int H, int Tq, int Tk, int d, int block, float scale,
+                           int dtype, unsigned flags, void *stream);
+
+/* Backward, second kernel: dk, dv [B,H,Tk,d] from delta written by
+ * scfa_attn_bwd_dq_lists (enqueue that one first on the same stream). */
+int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
+                             const float *lse, const void *dout, const float *delta,
+                             const int32_t *q_idx, const int32_t *k_idx,
+                             const int32_t *q_hash, const int32_t *k_hash,
+                             const int32_t *col_count, const int32_t *col_list,
+                             void *dk, void *dv,
+                             int B, int H, int Tq, int Tk, int d, int block, float scale,
+                             int dtype, unsigned flags, void *stream);
+
+/*
+ * Bytes of workspace an operation needs (0 for invalid arguments).  For the
+ * attention ops d and n_buckets are ignored; for SCFA_OP_LSH_SORT Tq is the
+ * sequence length T and Tk, d, block are ignored.  The size is an upper
+ * bound valid for every flag combination.
+ */
+size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int block, int n_buckets);
+
+/* Message for the calling thread's most recent non-zero status ("" if none). */
+const char *scfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCFA_H */

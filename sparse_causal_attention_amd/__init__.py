@@ -1,0 +1,279 @@
+"""Sparse causal flash attention (SCFA) for MI355X / gfx950.
+
+Thin PyTorch binding over the C ABI of ``libscfa.so`` (include/scfa.h).  The
+functions below only marshal arguments: they check devices, shapes and dtypes,
+allocate outputs and workspace with torch (device memory), and pass raw
+pointers plus torch's current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU or PyTorch
+fallback, and importing this package fails if the library is not built.
+
+Semantics follow the deep-paper.org summary of arXiv 2306.01160 ("Faster
+Causal Attention Over Large Sequences Through Sparse Flash Attention"):
+compact Q/K/V with original positions (QK-sparse) and bucket ids
+(Hash-sparse), exact attention under the element mask
+``k_idx <= q_idx [and q_hash == k_hash]``.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    FLAG_FORCE_MASK,
+    FLAG_IDX_ASCENDING,
+    FLAG_NO_PRUNE,
+    ScfaError,
+)
+
+_LIB = _lib.load()
+
+__all__ = [
+    "qk_sparse_fwd",
+    "qk_sparse_bwd",
+    "hash_sparse_fwd",
+    "hash_sparse_bwd",
+    "lsh_bucket_sort",
+    "block_meta",
+    "attn_fwd_lists",
+    "attn_bwd_dq_lists",
+    "attn_bwd_dkdv_lists",
+    "workspace_size",
+    "ScfaError",
+    "FLAG_NO_PRUNE",
+    "FLAG_FORCE_MASK",
+    "FLAG_IDX_ASCENDING",
+]
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None) -> None:
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def workspace_size(op: int, B: int, H: int, Tq: int, Tk: int, d: int, block: int, n_buckets: int = 0) -> int:
+    return int(_LIB.scfa_workspace_size(op, B, H, Tq, Tk, d, block, n_buckets))
+
+
+def _workspace(op, B, H, Tq, Tk, d, block, device, n_buckets=0, workspace=None):
+    n = workspace_size(op, B, H, Tq, Tk, d, block, n_buckets)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+        return workspace, workspace.numel()
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def _attn_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, H, Tq, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Tk, d] matching q")
+    return B, H, Tq, k.shape[2], d
+
+
+def _fwd(fn_name, op, q, k, v, idx_args, block, scale, flags, workspace):
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    for t, n, T in zip(idx_args, ("q_idx", "k_idx", "q_hash", "k_hash"), (Tq, Tk, Tq, Tk)):
+        _need(t, n, torch.int32, (B, H, T))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(op, B, H, Tq, Tk, d, block, q.device, workspace=workspace)
+    fn = getattr(_LIB, fn_name)
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in idx_args], _ptr(o), _ptr(lse),
+            B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags), _ptr(ws), nws, _stream())
+    _lib.check(fn_name, rc)
+    return o, lse
+
+
+def _bwd(fn_name, op, q, k, v, o, lse, dout, idx_args, block, scale, flags, workspace):
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, q.dtype)
+    _need(o, "o", shape=q.shape)
+    _need(dout, "dout", shape=q.shape)
+    _need(lse, "lse", torch.float32, (B, H, Tq))
+    for t, n, T in zip(idx_args, ("q_idx", "k_idx", "q_hash", "k_hash"), (Tq, Tk, Tq, Tk)):
+        _need(t, n, torch.int32, (B, H, T))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws, nws = _workspace(op, B, H, Tq, Tk, d, block, q.device, workspace=workspace)
+    fn = getattr(_LIB, fn_name)
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), *[_ptr(t) for t in idx_args],
+            _ptr(dq), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags),
+            _ptr(ws), nws, _stream())
+    _lib.check(fn_name, rc)
+    return dq, dk, dv
+
+
+def qk_sparse_fwd(q, k, v, q_idx=None, k_idx=None, *, block=64, scale=None, flags=0, workspace=None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """QK-sparse forward; q_idx = k_idx = None gives dense causal attention."""
+    return _fwd("scfa_qk_sparse_fwd", _lib.OP_QK_FWD, q, k, v, (q_idx, k_idx), block, scale, flags, workspace)
+
+
+def qk_sparse_bwd(q, k, v, o, lse, dout, q_idx=None, k_idx=None, *, block=64, scale=None, flags=0, workspace=None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for the QK-sparse forward."""
+    return _bwd("scfa_qk_sparse_bwd", _lib.OP_QK_BWD, q, k, v, o, lse, dout, (q_idx, k_idx), block, scale,
+                flags, workspace)
+
+
+def hash_sparse_fwd(q, k, v, q_idx, k_idx, q_hash, k_hash, *, block=64, scale=None, flags=0, workspace=None):
+    """Hash-sparse forward: causal on positions and restricted to equal bucket ids."""
+    return _fwd("scfa_hash_sparse_fwd", _lib.OP_HASH_FWD, q, k, v, (q_idx, k_idx, q_hash, k_hash), block, scale,
+                flags, workspace)
+
+
+def hash_sparse_bwd(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, *, block=64, scale=None, flags=0,
+                    workspace=None):
+    """Gradients (dq, dk, dv) for the Hash-sparse forward."""
+    return _bwd("scfa_hash_sparse_bwd", _lib.OP_HASH_BWD, q, k, v, o, lse, dout, (q_idx, k_idx, q_hash, k_hash),
+                block, scale, flags, workspace)
+
+
+def lsh_bucket_sort(x, R, n_buckets, idx=None, companion=None, *, idx_ascending=False, want_x=True,
+                    workspace=None):
+    """Bucket ids of x's rows and their (bucket, idx) order.
+
+    Returns (hash_sorted, idx_sorted, perm, x_sorted, companion_sorted); the last
+    two are None when not requested.
+    """
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, T, d]")
+    B, H, T, d = x.shape
+    _need(x, "x")
+    _need(R, "R", torch.float32, (H, d, n_buckets // 2))
+    _need(idx, "idx", torch.int32, (B, H, T))
+    _need(companion, "companion", x.dtype, x.shape)
+    hs = torch.empty((B, H, T), dtype=torch.int32, device=x.device)
+    ids = torch.empty_like(hs)
+    perm = torch.empty_like(hs)
+    xs = torch.empty_like(x) if want_x else None
+    cs = torch.empty_like(companion) if companion is not None else None
+    ws, nws = _workspace(_lib.OP_LSH_SORT, B, H, T, 0, d, 0, x.device, n_buckets=n_buckets, workspace=workspace)
+    flags = _lib.FLAG_IDX_ASCENDING if idx_ascending else 0
+    rc = _LIB.scfa_lsh_bucket_sort(_ptr(x), _ptr(idx), _ptr(R), n_buckets, B, H, T, d, _dtype_code(x), flags,
+                                   _ptr(hs), _ptr(ids), _ptr(perm), _ptr(xs), _ptr(companion), _ptr(cs),
+                                   _ptr(ws), nws, _stream())
+    _lib.check("scfa_lsh_bucket_sort", rc)
+    return hs, ids, perm, xs, cs
+
+
+def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=True):
+    """Block statistics and live-tile lists (see include/scfa.h, scfa_block_meta)."""
+    B, H, Tq = q_idx.shape
+    Tk = k_idx.shape[2]
+    _need(q_idx, "q_idx", torch.int32)
+    _need(k_idx, "k_idx", torch.int32, (B, H, Tk))
+    _need(q_hash, "q_hash", torch.int32, (B, H, Tq))
+    _need(k_hash, "k_hash", torch.int32, (B, H, Tk))
+    nq, nk = -(-Tq // block), -(-Tk // block)
+    dev = q_idx.device
+    out = {
+        "q_stats": torch.empty((B, H, nq, 4), dtype=torch.int32, device=dev),
+        "k_stats": torch.empty((B, H, nk, 4), dtype=torch.int32, device=dev),
+        "row_count": torch.empty((B, H, nq), dtype=torch.int32, device=dev),
+        "row_list": torch.empty((B, H, nq, nk), dtype=torch.int32, device=dev),
+    }
+    if with_cols:
+        out["col_count"] = torch.empty((B, H, nk), dtype=torch.int32, device=dev)
+        out["col_list"] = torch.empty((B, H, nk, nq), dtype=torch.int32, device=dev)
+    rc = _LIB.scfa_block_meta(_ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), B, H, Tq, Tk, block,
+                              _ptr(out["q_stats"]), _ptr(out["k_stats"]), _ptr(out["row_count"]),
+                              _ptr(out["row_list"]), _ptr(out.get("col_count")), _ptr(out.get("col_list")),
+                              _stream())
+    _lib.check("scfa_block_meta", rc)
+    return out
+
+
+def _list_args(meta, key_cnt, key_list):
+    if meta is None:
+        return None, None
+    return meta[key_cnt], meta[key_list]
+
+
+def attn_fwd_lists(q, k, v, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0, out=None):
+    """Forward over lists from ``block_meta`` (one kernel).  Positions None = dense causal.
+
+    ``out`` optionally supplies preallocated (o, lse).
+    """
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse = out if out is not None else (torch.empty_like(q),
+                                          torch.empty((B, H, Tq), dtype=torch.float32, device=q.device))
+    rc_, rl_ = _list_args(meta, "row_count", "row_list")
+    rc = _LIB.scfa_attn_fwd_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
+                                  _ptr(rc_), _ptr(rl_), _ptr(o), _ptr(lse), B, H, Tq, Tk, d, block, float(scale),
+                                  _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_attn_fwd_lists", rc)
+    return o, lse
+
+
+def attn_bwd_dq_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0,
+                      out=None):
+    """dQ and D = rowsum(dout * o) over row lists (one kernel).  Returns (dq, delta)."""
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, delta = out if out is not None else (torch.empty_like(q),
+                                             torch.empty((B, H, Tq), dtype=torch.float32, device=q.device))
+    rc_, rl_ = _list_args(meta, "row_count", "row_list")
+    rc = _LIB.scfa_attn_bwd_dq_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_idx),
+                                     _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), _ptr(rc_), _ptr(rl_), _ptr(dq),
+                                     _ptr(delta), B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags),
+                                     _stream())
+    _lib.check("scfa_attn_bwd_dq_lists", rc)
+    return dq, delta
+
+
+def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None,
+                        flags=0, out=None):
+    """dK and dV over column lists (one kernel), reading delta from attn_bwd_dq_lists."""
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dk, dv = out if out is not None else (torch.empty_like(k), torch.empty_like(v))
+    cc_, cl_ = _list_args(meta, "col_count", "col_list")
+    rc = _LIB.scfa_attn_bwd_dkdv_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta), _ptr(q_idx),
+                                       _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), _ptr(cc_), _ptr(cl_), _ptr(dk),
+                                       _ptr(dv), B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags),
+                                       _stream())
+    _lib.check("scfa_attn_bwd_dkdv_lists", rc)
+    return dk, dv

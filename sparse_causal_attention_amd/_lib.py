@@ -1,0 +1,106 @@
+"""ctypes loader for libscfa.so, the HIP library (C ABI declared in include/scfa.h).
+
+There is no fallback: if the library is missing the import of the binding
+fails loudly.  Build it with ``python -m sparse_causal_attention_amd.build``
+(or ``__graft_entry__.build()``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libscfa.so")
+
+# Names declared in include/scfa.h, in declaration order.
+EXPORTED = (
+    "scfa_qk_sparse_fwd",
+    "scfa_qk_sparse_bwd",
+    "scfa_hash_sparse_fwd",
+    "scfa_hash_sparse_bwd",
+    "scfa_lsh_bucket_sort",
+    "scfa_block_meta",
+    "scfa_attn_fwd_lists",
+    "scfa_attn_bwd_dq_lists",
+    "scfa_attn_bwd_dkdv_lists",
+    "scfa_workspace_size",
+    "scfa_last_error",
+)
+
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_UNSUPPORTED = 2
+ERR_WORKSPACE_TOO_SMALL = 3
+ERR_HIP = 4
+
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+
+FLAG_NO_PRUNE = 1 << 0
+FLAG_FORCE_MASK = 1 << 1
+FLAG_IDX_ASCENDING = 1 << 2
+
+OP_QK_FWD = 0
+OP_QK_BWD = 1
+OP_HASH_FWD = 2
+OP_HASH_BWD = 3
+OP_LSH_SORT = 4
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_u = ctypes.c_uint
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_ATTN_TAIL = [_i, _i, _i, _i, _i, _i, _f, _i, _u, _p, _sz, _p]
+_LISTS_TAIL = [_i, _i, _i, _i, _i, _i, _f, _i, _u, _p]
+
+_SIGNATURES = {
+    "scfa_qk_sparse_fwd": [_p, _p, _p, _p, _p, _p, _p] + _ATTN_TAIL,
+    "scfa_qk_sparse_bwd": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p] + _ATTN_TAIL,
+    "scfa_hash_sparse_fwd": [_p, _p, _p, _p, _p, _p, _p, _p, _p] + _ATTN_TAIL,
+    "scfa_hash_sparse_bwd": [_p] * 13 + _ATTN_TAIL,
+    "scfa_lsh_bucket_sort": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    "scfa_block_meta": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p],
+    "scfa_attn_fwd_lists": [_p] * 11 + _LISTS_TAIL,
+    "scfa_attn_bwd_dq_lists": [_p] * 14 + _LISTS_TAIL,
+    "scfa_attn_bwd_dkdv_lists": [_p] * 14 + _LISTS_TAIL,
+    "scfa_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],
+    "scfa_last_error": [],
+}
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libscfa.so once and attach the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} not found: the HIP library is not built "
+            "(run python -m sparse_causal_attention_amd.build)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, argtypes in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = _i
+    lib.scfa_workspace_size.restype = _sz
+    lib.scfa_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+class ScfaError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def check(fn: str, status: int) -> None:
+    if status != OK:
+        raise ScfaError(fn, status, load().scfa_last_error().decode())

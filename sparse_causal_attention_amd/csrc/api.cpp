@@ -1,0 +1,505 @@
+// C ABI of the SCFA library: argument validation, workspace carving and
+// dispatch to the kernel launchers.  Nothing is enqueued unless every
+// argument is valid; the library never allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/scfa.h"
+#include "scfa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SCFA_OK;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+  return fail(SCFA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int nblocks(int T, int block) { return (T + block - 1) / block; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Pointer that must be non-null when `elems` > 0 and aligned to `al` bytes.
+int check_ptr(const void *p, long long elems, size_t al, const char *name) {
+  if (elems <= 0) return SCFA_OK;
+  if (p == nullptr) return fail(SCFA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(p, al)) return fail(SCFA_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", name, al);
+  return SCFA_OK;
+}
+
+struct Shape {
+  int B, H, Tq, Tk, d, block, dtype;
+  float scale;
+};
+
+int check_shape(const Shape &s) {
+  if (s.B < 1 || s.H < 1) return fail(SCFA_ERR_INVALID_ARGUMENT, "B and H must be >= 1 (got %d, %d)", s.B, s.H);
+  if (s.Tq < 0 || s.Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "Tq and Tk must be >= 0 (got %d, %d)", s.Tq, s.Tk);
+  if (s.d != 64 && s.d != 128) return fail(SCFA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", s.d);
+  if (s.block != 64 && s.block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", s.block);
+  if (s.dtype != SCFA_DTYPE_BF16 && s.dtype != SCFA_DTYPE_FP32)
+    return fail(SCFA_ERR_UNSUPPORTED, "dtype=%d unsupported", s.dtype);
+  if (!(std::isfinite(s.scale) && s.scale > 0.f)) return fail(SCFA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  const long long T = s.Tq > s.Tk ? s.Tq : s.Tk;
+  if ((long long)s.B * s.H * T * s.d >= (1ll << 31))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*max(Tq,Tk)*d must be < 2^31");
+  return SCFA_OK;
+}
+
+size_t attn_ws(bool bwd, int B, int H, int Tq, int Tk, int block) {
+  const size_t BH = (size_t)B * H;
+  const size_t nq = nblocks(Tq, block), nk = nblocks(Tk, block);
+  size_t n = round_up(BH * nq * 16) + round_up(BH * nk * 16) + round_up(BH * nq * 4) + round_up(BH * nq * nk * 4);
+  if (bwd) n += round_up(BH * nk * 4) + round_up(BH * nk * nq * 4) + round_up(BH * (size_t)Tq * 4);
+  return n;
+}
+
+struct Carver {
+  char *p;
+  template <typename T>
+  T *take(size_t bytes) {
+    T *r = reinterpret_cast<T *>(p);
+    p += round_up(bytes);
+    return r;
+  }
+};
+
+int check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return SCFA_OK;
+  if (ws == nullptr) return fail(SCFA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, kAlign)) return fail(SCFA_ERR_INVALID_ARGUMENT, "workspace is not %zu-byte aligned", kAlign);
+  if (have < need) return fail(SCFA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", have, need);
+  return SCFA_OK;
+}
+
+enum Kind { kFwd, kBwdAll, kBwdDq, kBwdDkdv };
+enum Api { kApiQK, kApiHash, kApiLists };
+
+// Everything an attention entry point receives.
+struct AttnCall {
+  Kind kind;
+  Api api;
+  const void *q, *k, *v, *o;
+  const float *lse;
+  const void *dout;
+  const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
+  const int32_t *row_cnt, *row_list, *col_cnt, *col_list;  // list entry points only
+  void *out_o;
+  float *out_lse;
+  void *dq, *dk, *dv;
+  float *delta;  // list entry points only
+  Shape s;
+  unsigned flags;
+  void *ws;
+  size_t ws_bytes;
+  void *stream;
+};
+
+// Shared implementation of every attention entry point.
+int attention(const AttnCall &c) {
+  const Shape &s = c.s;
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (c.flags & ~(SCFA_FLAG_NO_PRUNE | SCFA_FLAG_FORCE_MASK))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", c.flags);
+  const long long BH = (long long)s.B * s.H;
+  const long long nQ = BH * s.Tq * s.d, nK = BH * s.Tk * s.d;
+  const long long nQi = BH * s.Tq, nKi = BH * s.Tk;
+  const int nq = nblocks(s.Tq, s.block), nk = nblocks(s.Tk, s.block);
+  if ((rc = check_ptr(c.q, nQ, 16, "q")) || (rc = check_ptr(c.k, nK, 16, "k")) || (rc = check_ptr(c.v, nK, 16, "v")))
+    return rc;
+  // Positions and buckets.  A pointer may be NULL when its tensor is empty
+  // (T == 0): torch hands out NULL for empty tensors.
+  bool dense, hashed;
+  if (c.api == kApiHash) {
+    dense = false;
+    hashed = true;
+  } else {
+    dense = c.q_idx == nullptr && c.k_idx == nullptr;
+    hashed = c.api == kApiLists && (c.q_hash != nullptr || c.k_hash != nullptr);
+    if (hashed && dense && (nQi > 0 || nKi > 0))
+      return fail(SCFA_ERR_INVALID_ARGUMENT, "bucket ids need positions (q_idx, k_idx)");
+  }
+  if (!dense && ((rc = check_ptr(c.q_idx, nQi, 4, "q_idx")) || (rc = check_ptr(c.k_idx, nKi, 4, "k_idx"))))
+    return rc;
+  if (hashed && ((rc = check_ptr(c.q_hash, nQi, 4, "q_hash")) || (rc = check_ptr(c.k_hash, nKi, 4, "k_hash"))))
+    return rc;
+  // tensors of each kind
+  switch (c.kind) {
+    case kFwd:
+      if ((rc = check_ptr(c.out_o, nQ, 16, "o")) || (rc = check_ptr(c.out_lse, nQi, 4, "lse"))) return rc;
+      break;
+    case kBwdAll:
+    case kBwdDq:
+      if ((rc = check_ptr(c.o, nQ, 16, "o")) || (rc = check_ptr(c.lse, nQi, 4, "lse")) ||
+          (rc = check_ptr(c.dout, nQ, 16, "dout")) || (rc = check_ptr(c.dq, nQ, 16, "dq")))
+        return rc;
+      if (c.kind == kBwdAll && ((rc = check_ptr(c.dk, nK, 16, "dk")) || (rc = check_ptr(c.dv, nK, 16, "dv"))))
+        return rc;
+      if (c.kind == kBwdDq && (rc = check_ptr(c.delta, nQi, 4, "delta"))) return rc;
+      break;
+    case kBwdDkdv:
+      if ((rc = check_ptr(c.lse, nQi, 4, "lse")) || (rc = check_ptr(c.dout, nQ, 16, "dout")) ||
+          (rc = check_ptr(c.delta, nQi, 4, "delta")) || (rc = check_ptr(c.dk, nK, 16, "dk")) ||
+          (rc = check_ptr(c.dv, nK, 16, "dv")))
+        return rc;
+      break;
+  }
+  const bool no_prune = (c.flags & SCFA_FLAG_NO_PRUNE) != 0;
+  // lists (list entry points) or workspace (the others)
+  if (c.api == kApiLists) {
+    if (!dense && !no_prune) {
+      if (c.kind != kBwdDkdv && ((rc = check_ptr(c.row_cnt, BH * nq, 4, "row_count")) ||
+                                 (rc = check_ptr(c.row_list, BH * nq * nk, 4, "row_list"))))
+        return rc;
+      if (c.kind == kBwdDkdv && ((rc = check_ptr(c.col_cnt, BH * nk, 4, "col_count")) ||
+                                 (rc = check_ptr(c.col_list, BH * nk * nq, 4, "col_list"))))
+        return rc;
+    }
+  } else {
+    const bool bwd = c.kind != kFwd;
+    size_t need = attn_ws(bwd, s.B, s.H, s.Tq, s.Tk, s.block);
+    if (dense) need = bwd ? round_up((size_t)BH * s.Tq * 4) : 0;
+    if ((rc = check_ws(c.ws, c.ws_bytes, need))) return rc;
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(c.stream);
+  scfa::AttnArgs a{};
+  a.q = c.q;
+  a.k = c.k;
+  a.v = c.v;
+  a.o = c.o;
+  a.dout = c.dout;
+  a.lse = c.lse;
+  a.out_o = c.out_o;
+  a.out_lse = c.out_lse;
+  a.dq = c.dq;
+  a.dk = c.dk;
+  a.dv = c.dv;
+  a.q_idx = c.q_idx;
+  a.k_idx = c.k_idx;
+  a.q_hash = hashed ? c.q_hash : nullptr;
+  a.k_hash = hashed ? c.k_hash : nullptr;
+  a.BH = (int)BH;
+  a.Tq = s.Tq;
+  a.Tk = s.Tk;
+  a.nq = nq;
+  a.nk = nk;
+  a.d = s.d;
+  a.block = s.block;
+  a.scale = s.scale;
+  a.no_prune = no_prune ? 1 : 0;
+  a.force_mask = (c.flags & SCFA_FLAG_FORCE_MASK) ? 1 : 0;
+
+  if (c.api == kApiLists) {
+    a.row_cnt = c.row_cnt;
+    a.row_list = c.row_list;
+    a.col_cnt = c.col_cnt;
+    a.col_list = c.col_list;
+    a.delta = c.delta;
+  } else {
+    Carver cv{static_cast<char *>(c.ws)};
+    const bool bwd = c.kind != kFwd;
+    if (!dense) {
+      scfa::MetaArgs m{};
+      m.q_idx = c.q_idx;
+      m.k_idx = c.k_idx;
+      m.q_hash = a.q_hash;
+      m.k_hash = a.k_hash;
+      m.q_stats = cv.take<int32_t>((size_t)BH * nq * 16);
+      m.k_stats = cv.take<int32_t>((size_t)BH * nk * 16);
+      m.row_cnt = cv.take<int32_t>((size_t)BH * nq * 4);
+      m.row_list = cv.take<int32_t>((size_t)BH * nq * nk * 4);
+      if (bwd) {
+        m.col_cnt = cv.take<int32_t>((size_t)BH * nk * 4);
+        m.col_list = cv.take<int32_t>((size_t)BH * nk * nq * 4);
+      }
+      m.BH = (int)BH;
+      m.Tq = s.Tq;
+      m.Tk = s.Tk;
+      m.nq = nq;
+      m.nk = nk;
+      m.block = s.block;
+      a.row_cnt = m.row_cnt;
+      a.row_list = m.row_list;
+      a.col_cnt = m.col_cnt;
+      a.col_list = m.col_list;
+      if (!no_prune) {
+        hipError_t e = scfa::launch_block_meta(m, bwd, st);
+        if (e != hipSuccess) return hip_fail(e, "block metadata");
+      }
+    }
+    if (bwd) a.delta = cv.take<float>((size_t)BH * s.Tq * 4);
+  }
+
+  const int mode = hashed ? scfa::kHash : (dense ? scfa::kDense : scfa::kQK);
+  const bool bf16 = s.dtype == SCFA_DTYPE_BF16;
+  hipError_t e;
+  if (c.kind == kFwd) {
+    e = bf16 ? scfa::launch_attn_fwd_bf16(a, mode, st) : scfa::launch_attn_fwd_f32(a, mode, st);
+  } else {
+    const int part = c.kind == kBwdAll ? 3 : (c.kind == kBwdDq ? 1 : 2);
+    e = bf16 ? scfa::launch_attn_bwd_bf16(a, mode, part, st) : scfa::launch_attn_bwd_f32(a, mode, part, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, c.kind == kFwd ? "attention forward" : "attention backward");
+  return ok();
+}
+
+size_t lsh_ws(int B, int H, int T, int nb) {
+  const size_t BH = (size_t)B * H;
+  const size_t nbins = (size_t)scfa::sort_bins(nb, true);
+  return round_up(BH * T * 4) + round_up(BH * nbins * scfa::sort_chunks(T) * 4) + 4 * round_up(BH * T * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int scfa_qk_sparse_fwd(const void *q, const void *k, const void *v, const int32_t *q_idx, const int32_t *k_idx,
+                       void *o, float *lse, int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype,
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+  AttnCall c{};
+  c.kind = kFwd;
+  c.api = kApiQK;
+  c.q = q, c.k = k, c.v = v, c.q_idx = q_idx, c.k_idx = k_idx, c.out_o = o, c.out_lse = lse;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.ws = workspace, c.ws_bytes = workspace_bytes, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_qk_sparse_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                       const void *dout, const int32_t *q_idx, const int32_t *k_idx, void *dq, void *dk, void *dv,
+                       int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  AttnCall c{};
+  c.kind = kBwdAll;
+  c.api = kApiQK;
+  c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout, c.q_idx = q_idx, c.k_idx = k_idx;
+  c.dq = dq, c.dk = dk, c.dv = dv;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.ws = workspace, c.ws_bytes = workspace_bytes, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_hash_sparse_fwd(const void *q, const void *k, const void *v, const int32_t *q_idx, const int32_t *k_idx,
+                         const int32_t *q_hash, const int32_t *k_hash, void *o, float *lse, int B, int H, int Tq,
+                         int Tk, int d, int block, float scale, int dtype, unsigned flags, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  AttnCall c{};
+  c.kind = kFwd;
+  c.api = kApiHash;
+  c.q = q, c.k = k, c.v = v, c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.out_o = o, c.out_lse = lse;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.ws = workspace, c.ws_bytes = workspace_bytes, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_hash_sparse_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const void *dout, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                         const int32_t *k_hash, void *dq, void *dk, void *dv, int B, int H, int Tq, int Tk, int d,
+                         int block, float scale, int dtype, unsigned flags, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  AttnCall c{};
+  c.kind = kBwdAll;
+  c.api = kApiHash;
+  c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.dq = dq, c.dk = dk, c.dv = dv;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.ws = workspace, c.ws_bytes = workspace_bytes, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_attn_fwd_lists(const void *q, const void *k, const void *v, const int32_t *q_idx, const int32_t *k_idx,
+                        const int32_t *q_hash, const int32_t *k_hash, const int32_t *row_count,
+                        const int32_t *row_list, void *o, float *lse, int B, int H, int Tq, int Tk, int d, int block,
+                        float scale, int dtype, unsigned flags, void *stream) {
+  AttnCall c{};
+  c.kind = kFwd;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.row_cnt = row_count, c.row_list = row_list, c.out_o = o, c.out_lse = lse;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                           const void *dout, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                           const int32_t *k_hash, const int32_t *row_count, const int32_t *row_list, void *dq,
+                           float *delta, int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype,
+                           unsigned flags, void *stream) {
+  AttnCall c{};
+  c.kind = kBwdDq;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.row_cnt = row_count, c.row_list = row_list, c.dq = dq, c.delta = delta;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v, const float *lse, const void *dout,
+                             const float *delta, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                             const int32_t *k_hash, const int32_t *col_count, const int32_t *col_list, void *dk,
+                             void *dv, int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype,
+                             unsigned flags, void *stream) {
+  AttnCall c{};
+  c.kind = kBwdDkdv;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.lse = lse, c.dout = dout, c.delta = const_cast<float *>(delta);
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int n_buckets, int B, int H, int T, int d,
+                         int dtype, unsigned flags, int32_t *hash_sorted, int32_t *idx_sorted, int32_t *perm,
+                         void *x_sorted, const void *companion, void *companion_sorted, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  if (B < 1 || H < 1 || T < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H must be >= 1 and T >= 0");
+  if (d != 64 && d != 128) return fail(SCFA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
+  if (dtype != SCFA_DTYPE_BF16 && dtype != SCFA_DTYPE_FP32) return fail(SCFA_ERR_UNSUPPORTED, "dtype=%d unsupported", dtype);
+  if (n_buckets < 2 || n_buckets > 1024 || (n_buckets & 1))
+    return fail(SCFA_ERR_UNSUPPORTED, "n_buckets=%d unsupported (even, 2..1024)", n_buckets);
+  if (flags & ~SCFA_FLAG_IDX_ASCENDING) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
+  if ((long long)B * H * T * d >= (1ll << 31)) return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*T*d must be < 2^31");
+  const long long nX = (long long)B * H * T * d, nI = (long long)B * H * T;
+  int rc;
+  if ((rc = check_ptr(x, nX, 16, "x")) || (rc = check_ptr(idx, idx ? nI : 0, 4, "idx")) ||
+      (rc = check_ptr(R, (long long)H * d * (n_buckets / 2), 4, "R")) ||
+      (rc = check_ptr(hash_sorted, nI, 4, "hash_sorted")) || (rc = check_ptr(idx_sorted, nI, 4, "idx_sorted")) ||
+      (rc = check_ptr(perm, nI, 4, "perm")))
+    return rc;
+  if (x_sorted && (rc = check_ptr(x_sorted, nX, 16, "x_sorted"))) return rc;
+  if ((companion == nullptr) != (companion_sorted == nullptr))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "companion and companion_sorted must both be NULL or both set");
+  if (companion && ((rc = check_ptr(companion, nX, 16, "companion")) ||
+                    (rc = check_ptr(companion_sorted, nX, 16, "companion_sorted"))))
+    return rc;
+  const size_t need = T > 0 ? lsh_ws(B, H, T, n_buckets) : 0;
+  if ((rc = check_ws(workspace, workspace_bytes, need))) return rc;
+
+  scfa::LshArgs a{};
+  a.x = x;
+  a.idx = idx;
+  a.R = R;
+  a.nb = n_buckets;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.d = d;
+  a.dtype = dtype;
+  a.idx_ascending = (flags & SCFA_FLAG_IDX_ASCENDING) ? 1 : 0;
+  a.hash_sorted = hash_sorted;
+  a.idx_sorted = idx_sorted;
+  a.perm = perm;
+  a.x_sorted = x_sorted;
+  a.companion = companion;
+  a.companion_sorted = companion_sorted;
+  if (T > 0) {
+    const size_t BH = (size_t)B * H;
+    Carver cv{static_cast<char *>(workspace)};
+    a.hash = cv.take<int32_t>(BH * T * 4);
+    a.hist = cv.take<int32_t>(BH * scfa::sort_bins(n_buckets, true) * scfa::sort_chunks(T) * 4);
+    a.tmp_idx[0] = cv.take<int32_t>(BH * T * 4);
+    a.tmp_idx[1] = cv.take<int32_t>(BH * T * 4);
+    a.tmp_src[0] = cv.take<int32_t>(BH * T * 4);
+    a.tmp_src[1] = cv.take<int32_t>(BH * T * 4);
+  }
+  hipError_t e = scfa::launch_lsh_bucket_sort(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "lsh bucket sort");
+  return ok();
+}
+
+int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B,
+                    int H, int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, int32_t *row_count,
+                    int32_t *row_list, int32_t *col_count, int32_t *col_list, void *stream) {
+  if (B < 1 || H < 1 || Tq < 0 || Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tk >= 0 required");
+  if (block != 64 && block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
+  if ((q_hash == nullptr) != (k_hash == nullptr))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_hash and k_hash must both be NULL or both set");
+  if ((col_count == nullptr) != (col_list == nullptr))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "col_count and col_list must both be NULL or both set");
+  const long long BH = (long long)B * H;
+  const long long nq = nblocks(Tq, block), nk = nblocks(Tk, block);
+  if (BH * nq * nk >= (1ll << 31) || BH * (Tq > Tk ? Tq : Tk) >= (1ll << 31))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "metadata too large");
+  int rc;
+  if ((rc = check_ptr(q_idx, BH * Tq, 4, "q_idx")) || (rc = check_ptr(k_idx, BH * Tk, 4, "k_idx")) ||
+      (rc = check_ptr(q_hash, q_hash ? BH * Tq : 0, 4, "q_hash")) ||
+      (rc = check_ptr(k_hash, k_hash ? BH * Tk : 0, 4, "k_hash")) ||
+      (rc = check_ptr(q_stats, BH * nq * 4, 16, "q_stats")) || (rc = check_ptr(k_stats, BH * nk * 4, 16, "k_stats")) ||
+      (rc = check_ptr(row_count, BH * nq, 4, "row_count")) || (rc = check_ptr(row_list, BH * nq * nk, 4, "row_list")))
+    return rc;
+  if (col_count && ((rc = check_ptr(col_count, BH * nk, 4, "col_count")) ||
+                    (rc = check_ptr(col_list, BH * nk * nq, 4, "col_list"))))
+    return rc;
+  scfa::MetaArgs m{};
+  m.q_idx = q_idx;
+  m.k_idx = k_idx;
+  m.q_hash = q_hash;
+  m.k_hash = k_hash;
+  m.q_stats = q_stats;
+  m.k_stats = k_stats;
+  m.row_cnt = row_count;
+  m.row_list = row_list;
+  m.col_cnt = col_count;
+  m.col_list = col_list;
+  m.BH = (int)BH;
+  m.Tq = Tq;
+  m.Tk = Tk;
+  m.nq = (int)nq;
+  m.nk = (int)nk;
+  m.block = block;
+  hipError_t e = scfa::launch_block_meta(m, col_count != nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block metadata");
+  return ok();
+}
+
+size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int block, int n_buckets) {
+  (void)d;
+  if (B < 1 || H < 1 || Tq < 0) return 0;
+  switch (op) {
+    case SCFA_OP_QK_FWD:
+    case SCFA_OP_HASH_FWD:
+    case SCFA_OP_QK_BWD:
+    case SCFA_OP_HASH_BWD:
+      if (Tk < 0 || (block != 64 && block != 128)) return 0;
+      return attn_ws(op == SCFA_OP_QK_BWD || op == SCFA_OP_HASH_BWD, B, H, Tq, Tk, block);
+    case SCFA_OP_LSH_SORT:
+      if (n_buckets < 2 || n_buckets > 1024 || (n_buckets & 1)) return 0;
+      return Tq > 0 ? lsh_ws(B, H, Tq, n_buckets) : 0;
+    default:
+      return 0;
+  }
+}
+
+const char *scfa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Block metadata and live-tile lists.
+//
+// Tile pruning rules of SCFA (deep-paper.org summary of arXiv 2306.01160,
+// "SCFA solution > 1. QK-Sparse" rule 1 and "2. Hash-Sparse" rules 1-2):
+// a tile (query block i, key block j) is skipped when every query precedes
+// every key, and in Hash-sparse mode when the blocks' buckets cannot match.
+// The bucket test uses the blocks' [min, max] bucket ranges (interval
+// overlap); the element mask inside the tile is exact, so this only decides
+// which tiles are visited.
+//
+// Two launches: block statistics (one wave per block), then one wave per list
+// row that tests 64 partner blocks per step and compacts the live ones in
+// ascending order with a ballot + popcount prefix.
+#include "scfa_device.hpp"
+#include "scfa_internal.hpp"
+
+namespace scfa {
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
+  const int nblk = a.nq + a.nk;
+  const int bh = blockIdx.x / nblk;
+  const int b = blockIdx.x % nblk;
+  const bool isq = b < a.nq;
+  const int blk = isq ? b : b - a.nq;
+  const int T = isq ? a.Tq : a.Tk;
+  const int32_t *idx = (isq ? a.q_idx : a.k_idx) + (size_t)bh * T;
+  const int32_t *hs = isq ? a.q_hash : a.k_hash;
+  const int r0 = blk * a.block;
+  const int r1 = min(r0 + a.block, T);
+  int mn = INT32_MAX, mx = INT32_MIN, hmn = INT32_MAX, hmx = INT32_MIN;
+  for (int r = r0 + (int)threadIdx.x; r < r1; r += 64) {
+    const int v = idx[r];
+    mn = min(mn, v);
+    mx = max(mx, v);
+    if (hs) {
+      const int h = hs[(size_t)bh * T + r];
+      hmn = min(hmn, h);
+      hmx = max(hmx, h);
+    }
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (hs) {
+    hmn = wave_min(hmn);
+    hmx = wave_max(hmx);
+  } else {
+    hmn = hmx = 0;
+  }
+  if (threadIdx.x == 0) {
+    int32_t *out = (isq ? a.q_stats + ((size_t)bh * a.nq + blk) * 4 : a.k_stats + ((size_t)bh * a.nk + blk) * 4);
+    *reinterpret_cast<int4 *>(out) = make_int4(mn, mx, hmn, hmx);
+  }
+}
+
+__global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, int with_cols) {
+  const int nrow = a.nq + (with_cols ? a.nk : 0);
+  const int bh = blockIdx.x / nrow;
+  const int r = blockIdx.x % nrow;
+  const bool is_row = r < a.nq;
+  const int lane = threadIdx.x;
+  const int4 *qst = reinterpret_cast<const int4 *>(a.q_stats) + (size_t)bh * a.nq;
+  const int4 *kst = reinterpret_cast<const int4 *>(a.k_stats) + (size_t)bh * a.nk;
+  int n_other;
+  int32_t *list;
+  int32_t *cnt_out;
+  int4 mine;
+  if (is_row) {
+    n_other = a.nk;
+    mine = qst[r];
+    list = a.row_list + ((size_t)bh * a.nq + r) * a.nk;
+    cnt_out = a.row_cnt + (size_t)bh * a.nq + r;
+  } else {
+    const int j = r - a.nq;
+    n_other = a.nq;
+    mine = kst[j];
+    list = a.col_list + ((size_t)bh * a.nk + j) * a.nq;
+    cnt_out = a.col_cnt + (size_t)bh * a.nk + j;
+  }
+  int count = 0;
+  for (int base = 0; base < n_other; base += 64) {
+    const int o = base + lane;
+    bool live = false, free = false;
+    if (o < n_other) {
+      const int4 qs = is_row ? mine : qst[o];
+      const int4 ks = is_row ? kst[o] : mine;
+      live = qs.y >= ks.x;
+      free = ks.y <= qs.x;
+      if (hash_mode) {
+        live = live && qs.w >= ks.z && qs.z <= ks.w;
+        free = free && qs.z == qs.w && ks.z == ks.w && qs.z == ks.z;
+      }
+    }
+    const unsigned long long m = __ballot(live);
+    if (live) {
+      const int pos = count + __popcll(m & ((1ull << lane) - 1ull));
+      list[pos] = o | (free ? (int)0x80000000u : 0);
+    }
+    count += __popcll(m);
+  }
+  if (lane == 0) *cnt_out = count;
+}
+
+hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s) {
+  const int hash_mode = a.q_hash != nullptr;
+  if (a.nq + a.nk > 0) {
+    hipLaunchKernelGGL(k_block_stats, dim3((unsigned)(a.BH * (a.nq + a.nk))), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int nrow = a.nq + (with_cols ? a.nk : 0);
+  if (nrow > 0) {
+    hipLaunchKernelGGL(k_build_lists, dim3((unsigned)(a.BH * nrow)), dim3(64), 0, s, a, hash_mode,
+                       with_cols ? 1 : 0);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace scfa

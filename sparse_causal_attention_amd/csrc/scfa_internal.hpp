@@ -1,0 +1,73 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel translation
+// units.  Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace scfa {
+
+// Attention modes: dense causal (positions 0..T-1), QK-sparse, Hash-sparse.
+enum Mode { kDense = 0, kQK = 1, kHash = 2 };
+
+struct AttnArgs {
+  // inputs [BH, T, d]
+  const void *q, *k, *v;
+  const void *o, *dout;  // backward only
+  const float *lse;      // backward only [BH, Tq]
+  // outputs
+  void *out_o;
+  float *out_lse;
+  void *dq, *dk, *dv;
+  float *delta;  // backward scratch [BH, Tq]: rowsum(dO * O)
+  // positions / buckets [BH, T] (idx NULL => dense causal)
+  const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
+  // live-tile lists (NULL in dense mode)
+  const int32_t *row_cnt, *row_list;  // [BH, nq], [BH, nq, nk]
+  const int32_t *col_cnt, *col_list;  // [BH, nk], [BH, nk, nq]
+  int BH, Tq, Tk, nq, nk, d, block;
+  float scale;
+  int no_prune, force_mask;
+};
+
+struct MetaArgs {
+  const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
+  int32_t *q_stats, *k_stats;  // [BH, nq, 4], [BH, nk, 4]
+  int32_t *row_cnt, *row_list, *col_cnt, *col_list;
+  int BH, Tq, Tk, nq, nk, block;
+};
+
+struct LshArgs {
+  const void *x;
+  const int32_t *idx;  // nullable
+  const float *R;      // [H, d, nb/2]
+  int nb, B, H, T, d, dtype;
+  int idx_ascending;
+  int32_t *hash_sorted, *idx_sorted, *perm;
+  void *x_sorted;
+  const void *companion;
+  void *companion_sorted;
+  // workspace pieces
+  int32_t *hash;            // [BH, T]
+  int32_t *hist;            // [BH, nbins, nchunks]
+  int32_t *tmp_idx[2];      // [BH, T] ping-pong (radix passes over idx)
+  int32_t *tmp_src[2];
+};
+
+hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s);
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs &a, int mode, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const AttnArgs &a, int mode, hipStream_t s);
+// part: bit 0 = dQ (+ D = rowsum(dO * O)), bit 1 = dK/dV (reads D).
+hipError_t launch_attn_bwd_bf16(const AttnArgs &a, int mode, int part, hipStream_t s);
+hipError_t launch_attn_bwd_f32(const AttnArgs &a, int mode, int part, hipStream_t s);
+
+hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s);
+
+// Sizes shared by the API's workspace carving and the sort launcher.
+constexpr int kSortChunk = 4096;  // tokens per counting-sort work group
+inline int sort_bins(int nb, bool idx_passes) { return idx_passes ? (nb > 256 ? nb : 256) : nb; }
+inline int sort_chunks(int T) { return (T + kSortChunk - 1) / kSortChunk; }
+
+}  // namespace scfa

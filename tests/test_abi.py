@@ -1,0 +1,151 @@
+"""The C ABI library: loads, exports every declared symbol, validates on the host.
+
+No test here launches a kernel: every call below is rejected by host-side
+validation before the library touches the GPU, so these run on a machine
+without one.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_causal_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scfa.h")
+
+# fake, aligned, never-dereferenced device addresses
+P = 0x7F0000000000
+P2 = 0x7F0000100000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(scfa_\w+)\s*\(", text)
+
+
+def test_header_and_binding_agree():
+    names = _declared()
+    assert sorted(names) == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    # also visible to a plain dlopen, independent of the binding
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared():
+        getattr(raw, name)
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, qi=P2, ki=P2, o=P, lse=P2, B=1, H=2, Tq=100, Tk=100, d=64, block=64, scale=0.125,
+             dtype=0, flags=0, ws=P, nws=1 << 30, stream=None)
+    a.update(kw)
+    lib = _lib.load()
+    return lib.scfa_qk_sparse_fwd(a["q"], a["k"], a["v"], a["qi"], a["ki"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["Tq"], a["Tk"], a["d"], a["block"], a["scale"], a["dtype"], a["flags"],
+                                  a["ws"], a["nws"], a["stream"])
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(d=96), _lib.ERR_UNSUPPORTED),
+        (dict(d=32), _lib.ERR_UNSUPPORTED),
+        (dict(block=32), _lib.ERR_UNSUPPORTED),
+        (dict(dtype=7), _lib.ERR_UNSUPPORTED),
+        (dict(B=0), _lib.ERR_INVALID_ARGUMENT),
+        (dict(H=-1), _lib.ERR_INVALID_ARGUMENT),
+        (dict(Tq=-5), _lib.ERR_INVALID_ARGUMENT),
+        (dict(scale=0.0), _lib.ERR_INVALID_ARGUMENT),
+        (dict(scale=float("inf")), _lib.ERR_INVALID_ARGUMENT),
+        (dict(scale=float("nan")), _lib.ERR_INVALID_ARGUMENT),
+        (dict(q=None), _lib.ERR_INVALID_ARGUMENT),
+        (dict(o=None), _lib.ERR_INVALID_ARGUMENT),
+        (dict(lse=None), _lib.ERR_INVALID_ARGUMENT),
+        (dict(q=P + 8), _lib.ERR_INVALID_ARGUMENT),  # not 16-byte aligned
+        (dict(qi=P2 + 2), _lib.ERR_INVALID_ARGUMENT),  # not 4-byte aligned
+        (dict(ki=None), _lib.ERR_INVALID_ARGUMENT),  # only one of q_idx / k_idx
+        (dict(flags=1 << 7), _lib.ERR_INVALID_ARGUMENT),
+        (dict(ws=None), _lib.ERR_INVALID_ARGUMENT),
+        (dict(ws=P + 16), _lib.ERR_INVALID_ARGUMENT),  # workspace alignment
+        (dict(nws=16), _lib.ERR_WORKSPACE_TOO_SMALL),
+        (dict(B=40000, H=40000), _lib.ERR_INVALID_ARGUMENT),  # too large
+    ],
+)
+def test_invalid_arguments_are_rejected_before_launch(kw, status):
+    assert _fwd(**kw) == status
+    msg = _lib.load().scfa_last_error().decode()
+    assert msg
+
+
+def test_hash_entry_points_require_hashes_and_positions():
+    lib = _lib.load()
+    common = (1, 1, 64, 64, 64, 64, 0.125, 0, 0, P, 1 << 30, None)
+    # q_hash NULL
+    assert lib.scfa_hash_sparse_fwd(P, P, P, P2, P2, None, P2, P, P2, *common) == _lib.ERR_INVALID_ARGUMENT
+    # q_idx NULL (positions are mandatory in Hash-sparse mode)
+    assert lib.scfa_hash_sparse_fwd(P, P, P, None, P2, P2, P2, P, P2, *common) == _lib.ERR_INVALID_ARGUMENT
+    # backward: dout NULL
+    assert lib.scfa_hash_sparse_bwd(P, P, P, P, P2, None, P2, P2, P2, P2, P, P, P, *common) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert lib.scfa_qk_sparse_bwd(P, P, P, P, P2, P, P2, P2, P, P, None, *common) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_lsh_sort_validation():
+    lib = _lib.load()
+
+    def call(nb=16, d=64, dtype=0, flags=0, x=P, R=P2, comp=None, comp_s=None, nws=1 << 30):
+        return lib.scfa_lsh_bucket_sort(x, None, R, nb, 1, 2, 1000, d, dtype, flags, P2, P2, P2, P, comp, comp_s,
+                                        P, nws, None)
+
+    assert call(nb=3) == _lib.ERR_UNSUPPORTED
+    assert call(nb=0) == _lib.ERR_UNSUPPORTED
+    assert call(nb=2048) == _lib.ERR_UNSUPPORTED
+    assert call(d=80) == _lib.ERR_UNSUPPORTED
+    assert call(dtype=2) == _lib.ERR_UNSUPPORTED
+    assert call(flags=1) == _lib.ERR_INVALID_ARGUMENT  # NO_PRUNE is not a sort flag
+    assert call(x=None) == _lib.ERR_INVALID_ARGUMENT
+    assert call(R=P2 + 2) == _lib.ERR_INVALID_ARGUMENT
+    assert call(comp=P) == _lib.ERR_INVALID_ARGUMENT  # companion without output
+    assert call(nws=100) == _lib.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_block_meta_validation():
+    lib = _lib.load()
+    assert lib.scfa_block_meta(P2, P2, P2, None, 1, 1, 100, 100, 64, P, P, P2, P2, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert lib.scfa_block_meta(P2, P2, None, None, 1, 1, 100, 100, 48, P, P, P2, P2, None, None, None) == \
+        _lib.ERR_UNSUPPORTED
+    assert lib.scfa_block_meta(P2, P2, None, None, 1, 1, 100, 100, 64, P + 4, P, P2, P2, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT  # stats need 16-byte alignment
+    assert lib.scfa_block_meta(P2, P2, None, None, 1, 1, 100, 100, 64, P, P, P2, P2, P2, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT  # col_count without col_list
+
+
+def test_workspace_sizes():
+    lib = _lib.load()
+    ws = lib.scfa_workspace_size
+    r = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    BH, nq, nk, Tq = 2 * 3, 4, 2, 200
+    fwd = r(BH * nq * 16) + r(BH * nk * 16) + r(BH * nq * 4) + r(BH * nq * nk * 4)
+    bwd = fwd + r(BH * nk * 4) + r(BH * nk * nq * 4) + r(BH * Tq * 4)
+    assert ws(_lib.OP_QK_FWD, 2, 3, 200, 100, 64, 64, 0) == fwd
+    assert ws(_lib.OP_HASH_BWD, 2, 3, 200, 100, 64, 64, 0) == bwd
+    assert ws(_lib.OP_QK_FWD, 0, 3, 200, 100, 64, 64, 0) == 0
+    assert ws(_lib.OP_QK_FWD, 1, 3, 200, 100, 64, 96, 0) == 0
+    assert ws(_lib.OP_LSH_SORT, 1, 1, 5000, 0, 64, 0, 16) > 0
+    assert ws(_lib.OP_LSH_SORT, 1, 1, 5000, 0, 64, 0, 15) == 0
+    assert ws(99, 1, 1, 5, 5, 64, 64, 0) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,173 @@
+"""GPU parity of the attention forward and backward against the fp64 oracle.
+
+Cases span several tiles with ragged tails, Tq != Tk, unsorted rows, empty
+rows (Hash-sparse), empty key sets, d in {64, 128}, block in {64, 128}, bf16
+and fp32, and all three modes (dense causal, QK-sparse, Hash-sparse).
+"""
+
+import numpy as np
+import pytest
+
+from gen import synthetic_case
+from helpers import check_forward, check_grads, dev, note, to_np
+from oracle import attention as A
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _lib():
+    import sparse_causal_attention_amd as scfa
+
+    return scfa
+
+
+def _tdtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def _positions(c, b, h, Tq, Tk):
+    if c.q_idx is None:
+        return np.arange(Tq), np.arange(Tk), None, None
+    qh = None if c.q_hash is None else c.q_hash[b, h]
+    kh = None if c.k_hash is None else c.k_hash[b, h]
+    return c.q_idx[b, h], c.k_idx[b, h], qh, kh
+
+
+def _oracle_fwd(c, scale):
+    B, H, Tq, d = c.q.shape
+    Tk = c.k.shape[2]
+    o = np.zeros((B, H, Tq, d))
+    lse = np.zeros((B, H, Tq))
+    for b in range(B):
+        for h in range(H):
+            qi, ki, qh, kh = _positions(c, b, h, Tq, Tk)
+            o[b, h], lse[b, h] = A.forward(c.q[b, h], c.k[b, h], c.v[b, h], qi, ki, qh, kh, scale)
+    return o, lse
+
+
+def _oracle_bwd(c, scale):
+    B, H, Tq, d = c.q.shape
+    Tk = c.k.shape[2]
+    out = [np.zeros((B, H, Tq, d)), np.zeros((B, H, Tk, d)), np.zeros((B, H, Tk, d))]
+    for b in range(B):
+        for h in range(H):
+            qi, ki, qh, kh = _positions(c, b, h, Tq, Tk)
+            g = A.backward(c.q[b, h], c.k[b, h], c.v[b, h], c.do[b, h], qi, ki, qh, kh, scale)
+            for i in range(3):
+                out[i][b, h] = g[i]
+    return out
+
+
+def _run(c, mode, block, flags=0, bwd=False):
+    scfa = _lib()
+    td = _tdtype(c.dtype)
+    q, k, v = dev(c.q, td), dev(c.k, td), dev(c.v, td)
+    d = c.q.shape[-1]
+    scale = 1.0 / np.sqrt(d)
+    if mode == "hash":
+        idx = [dev(c.q_idx), dev(c.k_idx), dev(c.q_hash), dev(c.k_hash)]
+        o, lse = scfa.hash_sparse_fwd(q, k, v, *idx, block=block, scale=scale, flags=flags)
+    else:
+        idx = [None, None] if mode == "dense" else [dev(c.q_idx), dev(c.k_idx)]
+        o, lse = scfa.qk_sparse_fwd(q, k, v, *idx, block=block, scale=scale, flags=flags)
+    grads = None
+    if bwd:
+        do = dev(c.do, td)
+        if mode == "hash":
+            grads = scfa.hash_sparse_bwd(q, k, v, o, lse, do, *idx, block=block, scale=scale, flags=flags)
+        else:
+            grads = scfa.qk_sparse_bwd(q, k, v, o, lse, do, *idx, block=block, scale=scale, flags=flags)
+    torch.cuda.synchronize()
+    return o, lse, grads, scale
+
+
+# (name, synthetic_case kwargs, mode)
+CASES = [
+    ("dense_T300", dict(Tq=300, Tk=300, mode="dense"), "dense"),
+    ("dense_Tq_lt_Tk", dict(Tq=130, Tk=333, mode="dense"), "dense"),
+    ("qk_shared_ascending", dict(Tq=517, Tk=517, mode="qk", shared=True), "qk"),
+    ("qk_independent_shuffled", dict(Tq=333, Tk=517, mode="qk", layout="shuffled"), "qk"),
+    ("hash_grouped_nb4", dict(Tq=600, Tk=555, mode="hash", nb=4, layout="grouped"), "hash"),
+    ("hash_shuffled_nb3", dict(Tq=257, Tk=321, mode="hash", nb=3, layout="shuffled"), "hash"),
+    ("hash_shared_grouped_nb8", dict(Tq=700, Tk=700, mode="hash", nb=8, layout="grouped", shared=True), "hash"),
+    ("hash_one_bucket", dict(Tq=200, Tk=260, mode="hash", nb=1, layout="grouped"), "hash"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("name,kw,mode", CASES, ids=[c[0] for c in CASES])
+def test_forward_backward_parity(name, kw, mode, d, block, dtype):
+    seed = hash((name, d, block, dtype)) % 100000
+    c = synthetic_case(seed, B=1, H=2, d=d, dtype=dtype, **kw)
+    note(f"[fwd+bwd] {name} d={d} block={block} dtype={dtype} Tq={c.q.shape[2]} Tk={c.k.shape[2]}")
+    o, lse, grads, scale = _run(c, mode, block, bwd=True)
+    o_ref, lse_ref = _oracle_fwd(c, scale)
+    check_forward(to_np(o), to_np(lse), o_ref, lse_ref, dtype, name)
+    ref = _oracle_bwd(c, scale)
+    check_grads([to_np(g) for g in grads], ref, dtype, name)
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_pruning_and_mask_flags_are_bit_identical(mode):
+    c = synthetic_case(7, B=2, H=2, Tq=450, Tk=450, mode=mode, nb=4, layout="grouped", shared=(mode != "hash"))
+    note(f"[flags] {mode}")
+    scfa = _lib()
+    base = _run(c, mode, 64, bwd=True)
+    for flags in (scfa.FLAG_NO_PRUNE, scfa.FLAG_FORCE_MASK, scfa.FLAG_NO_PRUNE | scfa.FLAG_FORCE_MASK):
+        other = _run(c, mode, 64, flags=flags, bwd=True)
+        assert torch.equal(base[0], other[0]), flags
+        assert torch.equal(base[1], other[1]), flags
+        for g0, g1 in zip(base[2], other[2]):
+            assert torch.equal(g0, g1), flags
+
+
+def test_repeated_runs_are_bit_identical():
+    c = synthetic_case(8, B=1, H=3, Tq=640, Tk=640, mode="hash", nb=4, layout="grouped")
+    note("[determinism] hash")
+    a = _run(c, "hash", 64, bwd=True)
+    b = _run(c, "hash", 64, bwd=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_empty_key_set_gives_zero_rows(mode):
+    c = synthetic_case(9, B=1, H=2, Tq=70, Tk=0, mode=mode, nb=2)
+    note(f"[Tk=0] {mode}")
+    o, lse, grads, _ = _run(c, mode, 64, bwd=True)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(grads[0] == 0)
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_empty_query_set(mode):
+    c = synthetic_case(10, B=1, H=2, Tq=0, Tk=90, mode=mode, nb=2)
+    note(f"[Tq=0] {mode}")
+    o, lse, grads, _ = _run(c, mode, 64, bwd=True)
+    assert o.numel() == 0
+    assert torch.all(grads[1] == 0) and torch.all(grads[2] == 0)
+
+
+def test_single_query_row():
+    c = synthetic_case(11, B=1, H=1, Tq=1, Tk=200, mode="qk", T_orig=1000)
+    note("[Tq=1]")
+    o, lse, grads, scale = _run(c, "qk", 64, bwd=True)
+    o_ref, lse_ref = _oracle_fwd(c, scale)
+    check_forward(to_np(o), to_np(lse), o_ref, lse_ref, "bf16", "Tq=1")
+    check_grads([to_np(g) for g in grads], _oracle_bwd(c, scale), "bf16", "Tq=1")
+
+
+def test_value_ones_gives_ones():
+    """V = 1: every non-empty row of O is exactly 1 (rows of P sum to one)."""
+    c = synthetic_case(12, B=1, H=2, Tq=500, Tk=480, mode="hash", nb=4, layout="grouped")
+    c.v[:] = 1.0
+    note("[V=1]")
+    o, lse, _, _ = _run(c, "hash", 64)
+    o = to_np(o)
+    nonempty = ~np.isneginf(to_np(lse))
+    assert np.all(o[nonempty] == 1.0)
+    assert np.all(o[~nonempty] == 0.0)
