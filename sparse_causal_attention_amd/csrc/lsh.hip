@@ -20,11 +20,15 @@
 namespace scfa {
 
 constexpr int kHashThreads = 256;
-constexpr int kColGroup = 32;
 
-template <int D, bool F32>
+// One thread per token.  R's columns are processed in groups of CG (8, 16 or
+// 32, the smallest that covers nb/2 or 32): the group is widened to float64
+// once into LDS and every thread accumulates CG float64 sums over the
+// coordinates in increasing order, eight coordinates (one 16-byte load of x)
+// per step.
+template <int D, int CG, bool F32>
 __global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a) {
-  __shared__ double sR[D * kColGroup];
+  __shared__ __attribute__((aligned(16))) double sR[D * CG];
   const int nblk = (a.T + kHashThreads - 1) / kHashThreads;
   const int bh = blockIdx.x / nblk;
   const int tb = blockIdx.x % nblk;
@@ -33,50 +37,54 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a) {
   const bool valid = t < a.T;
   const int half = a.nb / 2;
   const float *R = a.R + (size_t)h * D * half;
-
-  float x[D];
-  if (F32) {
-    const float *X = static_cast<const float *>(a.x) + ((size_t)bh * a.T + (valid ? t : 0)) * D;
-#pragma unroll
-    for (int k = 0; k < D; k += 4) {
-      const float4 v = valid ? *reinterpret_cast<const float4 *>(X + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-      x[k] = v.x; x[k + 1] = v.y; x[k + 2] = v.z; x[k + 3] = v.w;
-    }
-  } else {
-    const uint16_t *X = static_cast<const uint16_t *>(a.x) + ((size_t)bh * a.T + (valid ? t : 0)) * D;
-#pragma unroll
-    for (int k = 0; k < D; k += 8) {
-      const uint4 v = valid ? ld16(X + k) : make_uint4(0, 0, 0, 0);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[k + 2 * e] = bf16_bits_to_float(wv[e] & 0xffffu);
-        x[k + 2 * e + 1] = bf16_bits_to_float(wv[e] >> 16);
-      }
-    }
-  }
+  const size_t row = (size_t)bh * a.T + (valid ? t : 0);
 
   double best = -INFINITY, worst = INFINITY;
   int besti = 0, worsti = 0;
-  for (int cg = 0; cg < half; cg += kColGroup) {
-    const int ncol = min(kColGroup, half - cg);
+  for (int cg = 0; cg < half; cg += CG) {
+    const int ncol = min(CG, half - cg);
     __syncthreads();
-    for (int i = threadIdx.x; i < D * kColGroup; i += kHashThreads) {
-      const int k = i / kColGroup, cc = i % kColGroup;
+    for (int i = threadIdx.x; i < D * CG; i += kHashThreads) {
+      const int k = i / CG, cc = i % CG;
       sR[i] = cc < ncol ? (double)R[(size_t)k * half + cg + cc] : 0.0;
     }
     __syncthreads();
-    double acc[kColGroup];
+    double acc[CG];
 #pragma unroll
-    for (int cc = 0; cc < kColGroup; ++cc) acc[cc] = 0.0;
+    for (int cc = 0; cc < CG; ++cc) acc[cc] = 0.0;
+#pragma unroll 1
+    for (int k0 = 0; k0 < D; k0 += 8) {
+      float xv[8];
+      if (F32) {
+        const float *X = static_cast<const float *>(a.x) + row * D + k0;
+        const float4 v0 = valid ? *reinterpret_cast<const float4 *>(X) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 v1 = valid ? *reinterpret_cast<const float4 *>(X + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
+        xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
+      } else {
+        const uint16_t *X = static_cast<const uint16_t *>(a.x) + row * D + k0;
+        const uint4 v = valid ? ld16(X) : make_uint4(0, 0, 0, 0);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-      const double xk = (double)x[k];
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = bf16_bits_to_float(wv[e] & 0xffffu);
+          xv[2 * e + 1] = bf16_bits_to_float(wv[e] >> 16);
+        }
+      }
 #pragma unroll
-      for (int cc = 0; cc < kColGroup; ++cc) acc[cc] = fma(xk, sR[k * kColGroup + cc], acc[cc]);
+      for (int kk = 0; kk < 8; ++kk) {
+        const double xk = (double)xv[kk];
+        const double2 *r2 = reinterpret_cast<const double2 *>(sR + (k0 + kk) * CG);
+#pragma unroll
+        for (int c2 = 0; c2 < CG / 2; ++c2) {
+          const double2 r = r2[c2];
+          acc[2 * c2] = fma(xk, r.x, acc[2 * c2]);
+          acc[2 * c2 + 1] = fma(xk, r.y, acc[2 * c2 + 1]);
+        }
+      }
     }
 #pragma unroll
-    for (int cc = 0; cc < kColGroup; ++cc) {
+    for (int cc = 0; cc < CG; ++cc) {
       if (cc < ncol) {
         const double p = acc[cc];
         if (p > best) {
@@ -91,6 +99,20 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a) {
     }
   }
   if (valid) a.hash[(size_t)bh * a.T + t] = best >= -worst ? besti : half + worsti;
+}
+
+template <int D, int CG>
+static void launch_hash_cg(const LshArgs &a, unsigned grid, hipStream_t s) {
+  if (a.dtype == 1) hipLaunchKernelGGL((k_lsh_hash<D, CG, true>), dim3(grid), dim3(kHashThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_lsh_hash<D, CG, false>), dim3(grid), dim3(kHashThreads), 0, s, a);
+}
+
+template <int D>
+static void launch_hash(const LshArgs &a, unsigned grid, hipStream_t s) {
+  const int half = a.nb / 2;
+  if (half <= 8) launch_hash_cg<D, 8>(a, grid, s);
+  else if (half <= 16) launch_hash_cg<D, 16>(a, grid, s);
+  else launch_hash_cg<D, 32>(a, grid, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -240,13 +262,8 @@ hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0 || a.T == 0) return hipSuccess;
   const unsigned hgrid = (unsigned)(BH * ((a.T + kHashThreads - 1) / kHashThreads));
-  if (a.d == 64) {
-    if (a.dtype == 1) hipLaunchKernelGGL((k_lsh_hash<64, true>), dim3(hgrid), dim3(kHashThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_lsh_hash<64, false>), dim3(hgrid), dim3(kHashThreads), 0, s, a);
-  } else {
-    if (a.dtype == 1) hipLaunchKernelGGL((k_lsh_hash<128, true>), dim3(hgrid), dim3(kHashThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_lsh_hash<128, false>), dim3(hgrid), dim3(kHashThreads), 0, s, a);
-  }
+  if (a.d == 64) launch_hash<64>(a, hgrid, s);
+  else launch_hash<128>(a, hgrid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

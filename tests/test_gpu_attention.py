@@ -5,6 +5,8 @@ rows (Hash-sparse), empty key sets, d in {64, 128}, block in {64, 128}, bf16
 and fp32, and all three modes (dense causal, QK-sparse, Hash-sparse).
 """
 
+import zlib
+
 import numpy as np
 import pytest
 
@@ -100,7 +102,7 @@ CASES = [
 @pytest.mark.parametrize("d,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("name,kw,mode", CASES, ids=[c[0] for c in CASES])
 def test_forward_backward_parity(name, kw, mode, d, block, dtype):
-    seed = hash((name, d, block, dtype)) % 100000
+    seed = zlib.crc32(f"{name}/{d}/{block}/{dtype}".encode()) % 100000
     c = synthetic_case(seed, B=1, H=2, d=d, dtype=dtype, **kw)
     note(f"[fwd+bwd] {name} d={d} block={block} dtype={dtype} Tq={c.q.shape[2]} Tk={c.k.shape[2]}")
     o, lse, grads, scale = _run(c, mode, block, bwd=True)

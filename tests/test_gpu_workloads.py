@@ -142,7 +142,7 @@ def test_hash_workloads(wid):
                 if g is not None:
                     dq_ref = A.backward_rows(rows, qs, ks, vs, dO[b, h][pq], iq, ik, hq, hk, w.scale)
                     assert rel_fro(g[0][b, h][rows], dq_ref) <= 5e-2
-                    keys = _rows_sample(rng, w.Tk, 32)
+                    keys = _rows_sample(rng, w.Tk, 16)
                     dk_ref, dv_ref = A.backward_key_rows(keys, qs, ks, vs, dO[b, h][pq], iq, ik, hq, hk, w.scale)
                     assert rel_fro(g[1][b, h][keys], dk_ref) <= 5e-2
                     assert rel_fro(g[2][b, h][keys], dv_ref) <= 5e-2
