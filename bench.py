@@ -185,6 +185,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path has no multi-GPU code); got --gpus {args.gpus}",
@@ -225,21 +226,23 @@ def main():
     step_flops = 14.0 * units * w.d
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    _log("[bench] dense causal reference")
     dtimer = Timer(torch, DENSE_CALLS)
-    for _ in range(max(1, args.warmup)):
-        run_dense(scfa, w, q, k, v, do)
-    torch.cuda.synchronize()
-    nd = max(3, args.steps // 4)
-    t1 = time.perf_counter()
-    for _ in range(nd):
-        run_dense(scfa, w, q, k, v, do)
-    torch.cuda.synchronize()
-    dense_ms = (time.perf_counter() - t1) / nd * 1e3
-    for _ in range(nd):
-        run_dense(scfa, w, q, k, v, do, dtimer)
-    torch.cuda.synchronize()
-    dtimer.collect()
+    dense_ms = float("nan")
+    if not args.no_dense:
+        _log("[bench] dense causal reference")
+        for _ in range(max(1, args.warmup)):
+            run_dense(scfa, w, q, k, v, do)
+        torch.cuda.synchronize()
+        nd = max(3, args.steps // 4)
+        t1 = time.perf_counter()
+        for _ in range(nd):
+            run_dense(scfa, w, q, k, v, do)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t1) / nd * 1e3
+        for _ in range(nd):
+            run_dense(scfa, w, q, k, v, do, dtimer)
+        torch.cuda.synchronize()
+        dtimer.collect()
 
     per_call = {n: round(timer.mean_ms(n), 4) for n in STEP_CALLS}
     attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
@@ -291,11 +294,11 @@ def main():
         "executed_tiles": tiles,
         "dense_causal_tiles": w.B * w.H * (w.T // w.block) * (w.T // w.block + 1) // 2,
         "attention_only_tflops": round(step_flops / (attn_ms * 1e-3) / 1e12, 3),
-        "dense_causal_ms": round(dense_ms, 4),
-        "speedup_vs_dense_causal": round(dense_ms / ms_per_step, 3),
-        "speedup_vs_dense_causal_excl_lsh": round(dense_ms / attn_ms, 3),
+        "dense_causal_ms": None if args.no_dense else round(dense_ms, 4),
+        "speedup_vs_dense_causal": None if args.no_dense else round(dense_ms / ms_per_step, 3),
+        "speedup_vs_dense_causal_excl_lsh": None if args.no_dense else round(dense_ms / attn_ms, 3),
         "per_call_ms": per_call,
-        "dense_per_call_ms": {n: round(dtimer.mean_ms(n), 4) for n in DENSE_CALLS},
+        "dense_per_call_ms": None if args.no_dense else {n: round(dtimer.mean_ms(n), 4) for n in DENSE_CALLS},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

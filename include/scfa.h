@@ -218,8 +218,9 @@ int scfa_attn_fwd_lists(const void *q, const void *k, const void *v,
                         int B, int H, int Tq, int Tk, int d, int block, float scale,
                         int dtype, unsigned flags, void *stream);
 
-/* Backward, first kernel: dq [B,H,Tq,d] and delta [B,H,Tq] float32 =
- * rowsum(dout * o), which the second kernel reads. */
+/* Backward, first kernel: dq [B,H,Tq,d] and the scratch `delta`,
+ * [2,B,H,Tq] float32 = (rowsum(dout * o), lse * log2(e)), which the second
+ * kernel reads. */
 int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v,
                            const void *o, const float *lse, const void *dout,
                            const int32_t *q_idx, const int32_t *k_idx,
@@ -229,8 +230,9 @@ int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v,
                            int B, int H, int Tq, int Tk, int d, int block, float scale,
                            int dtype, unsigned flags, void *stream);
 
-/* Backward, second kernel: dk, dv [B,H,Tk,d] from delta written by
- * scfa_attn_bwd_dq_lists (enqueue that one first on the same stream). */
+/* Backward, second kernel: dk, dv [B,H,Tk,d] from the [2,B,H,Tq] scratch
+ * `delta` written by scfa_attn_bwd_dq_lists (enqueue that one first on the
+ * same stream). */
 int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
                              const float *lse, const void *dout, const float *delta,
                              const int32_t *q_idx, const int32_t *k_idx,

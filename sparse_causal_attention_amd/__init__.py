@@ -248,12 +248,13 @@ def attn_fwd_lists(q, k, v, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, sca
 
 def attn_bwd_dq_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0,
                       out=None):
-    """dQ and D = rowsum(dout * o) over row lists (one kernel).  Returns (dq, delta)."""
+    """dQ over row lists (one kernel).  Returns (dq, delta) with delta [2,B,H,Tq] float32 scratch
+    (rowsum(dout * o), lse * log2 e) for attn_bwd_dkdv_lists."""
     B, H, Tq, Tk, d = _attn_shapes(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, delta = out if out is not None else (torch.empty_like(q),
-                                             torch.empty((B, H, Tq), dtype=torch.float32, device=q.device))
+                                             torch.empty((2, B, H, Tq), dtype=torch.float32, device=q.device))
     rc_, rl_ = _list_args(meta, "row_count", "row_list")
     rc = _LIB.scfa_attn_bwd_dq_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_idx),
                                      _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), _ptr(rc_), _ptr(rl_), _ptr(dq),

@@ -71,7 +71,7 @@ size_t attn_ws(bool bwd, int B, int H, int Tq, int Tk, int block) {
   const size_t BH = (size_t)B * H;
   const size_t nq = nblocks(Tq, block), nk = nblocks(Tk, block);
   size_t n = round_up(BH * nq * 16) + round_up(BH * nk * 16) + round_up(BH * nq * 4) + round_up(BH * nq * nk * 4);
-  if (bwd) n += round_up(BH * nk * 4) + round_up(BH * nk * nq * 4) + round_up(BH * (size_t)Tq * 4);
+  if (bwd) n += round_up(BH * nk * 4) + round_up(BH * nk * nq * 4) + round_up(2 * BH * (size_t)Tq * 4);
   return n;
 }
 
@@ -157,11 +157,11 @@ int attention(const AttnCall &c) {
         return rc;
       if (c.kind == kBwdAll && ((rc = check_ptr(c.dk, nK, 16, "dk")) || (rc = check_ptr(c.dv, nK, 16, "dv"))))
         return rc;
-      if (c.kind == kBwdDq && (rc = check_ptr(c.delta, nQi, 4, "delta"))) return rc;
+      if (c.kind == kBwdDq && (rc = check_ptr(c.delta, 2 * nQi, 4, "delta"))) return rc;
       break;
     case kBwdDkdv:
       if ((rc = check_ptr(c.lse, nQi, 4, "lse")) || (rc = check_ptr(c.dout, nQ, 16, "dout")) ||
-          (rc = check_ptr(c.delta, nQi, 4, "delta")) || (rc = check_ptr(c.dk, nK, 16, "dk")) ||
+          (rc = check_ptr(c.delta, 2 * nQi, 4, "delta")) || (rc = check_ptr(c.dk, nK, 16, "dk")) ||
           (rc = check_ptr(c.dv, nK, 16, "dv")))
         return rc;
       break;
@@ -180,7 +180,7 @@ int attention(const AttnCall &c) {
   } else {
     const bool bwd = c.kind != kFwd;
     size_t need = attn_ws(bwd, s.B, s.H, s.Tq, s.Tk, s.block);
-    if (dense) need = bwd ? round_up((size_t)BH * s.Tq * 4) : 0;
+    if (dense) need = bwd ? round_up(2 * (size_t)BH * s.Tq * 4) : 0;
     if ((rc = check_ws(c.ws, c.ws_bytes, need))) return rc;
   }
 
@@ -250,7 +250,7 @@ int attention(const AttnCall &c) {
         if (e != hipSuccess) return hip_fail(e, "block metadata");
       }
     }
-    if (bwd) a.delta = cv.take<float>((size_t)BH * s.Tq * 4);
+    if (bwd) a.delta = cv.take<float>(2 * (size_t)BH * s.Tq * 4);
   }
 
   const int mode = hashed ? scfa::kHash : (dense ? scfa::kDense : scfa::kQK);

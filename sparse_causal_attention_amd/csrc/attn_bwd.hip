@@ -18,6 +18,7 @@
 //    dV^T += dO^T P, dK^T += Q^T dS.
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
+#include "scfa_pipe.hpp"
 
 namespace scfa {
 
@@ -91,20 +92,63 @@ __device__ __forceinline__ void col_tile(const AttnArgs &a, const List &cl, int 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 dQ (+ D) kernel
+// Chunk iteration over a row list (dQ) or a column list (dK/dV).
+// ---------------------------------------------------------------------------
+struct Chunk {
+  int t, ch, r0, nvalid;
+  bool free;
+};
+
+template <int MODE, int BS, bool ROWS>
+__device__ __forceinline__ bool next_chunk(const AttnArgs &a, const List &ls, int self, int t, int ch, Chunk &out) {
+  constexpr int NCH = BS / kChunk;
+  const int n_other = ROWS ? a.nk : a.nq;
+  const int T_other = ROWS ? a.Tk : a.Tq;
+  for (; t < ls.n; ++t, ch = 0) {
+    int ob;
+    bool free;
+    if (ROWS) row_tile<MODE, BS>(a, ls, t, self, ob, free);
+    else col_tile<MODE, BS>(a, ls, t, self, ob, free);
+    if (ob >= n_other || ch >= NCH) continue;
+    const int r0 = ob * BS + ch * kChunk;
+    if (r0 >= T_other) continue;
+    out.t = t;
+    out.ch = ch;
+    out.r0 = r0;
+    out.nvalid = min(kChunk, T_other - r0);
+    out.free = free;
+    return true;
+  }
+  return false;
+}
+
+template <int D>
+struct KVBufB {
+  MatChunk<D> k, v;
+  int idx[kChunk];
+  int hash[kChunk];
+};
+
+template <int D>
+struct QGBuf {
+  MatChunk<D> q, g;  // Q and dO rows
+  float lse2[kChunk];
+  float del[kChunk];
+  int idx[kChunk];
+  int hash[kChunk];
+};
+
+// ---------------------------------------------------------------------------
+// bf16 dQ (+ D, lse*log2 e) kernel.  Lanes own query columns.
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
 __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
-  constexpr int NT = BS / 32 * 64;
-  constexpr int NCH = BS / kChunk;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * kTPad];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * (D + 8)];
-  __shared__ __attribute__((aligned(16))) int sKidx[kChunk];
-  __shared__ __attribute__((aligned(16))) int sKhash[kChunk];
+  constexpr int NW = BS / 32;
+  __shared__ __attribute__((aligned(16))) KVBufB<D> sb[2];
 
-  const int bh = blockIdx.x / a.nq;
-  const int qb = blockIdx.x % a.nq;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.nq;
+  const int qb = wg % a.nq;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qb * BS + 32 * w + col;
@@ -116,15 +160,30 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
 
+  const List rl = row_list_b<MODE, BS>(a, bh, qb);
+  const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
+  const LaneOffsets<D> lo = lane_offsets<D>();
+  auto issue = [&](KVBufB<D> &b, const Chunk &c) {
+    dma_matrix<D, NW>(b.k, K, c.r0, c.nvalid, dmo);
+    dma_matrix<D, NW>(b.v, V, c.r0, c.nvalid, dmo);
+    if (MODE != kDense && !(c.free && c.nvalid == kChunk)) {
+      if (w == 0) dma_vec(b.idx, a.k_idx + (size_t)bh * a.Tk, c.r0, c.nvalid);
+      if (MODE == kHash && w == NW - 1) dma_vec(b.hash, a.k_hash + (size_t)bh * a.Tk, c.r0, c.nvalid);
+    }
+  };
+  Chunk cur;
+  bool have = next_chunk<MODE, BS, true>(a, rl, qb, 0, 0, cur);
+  if (have) issue(sb[0], cur);
+
   bf16x8 qf[D / 16], dof[D / 16];
   float dsum = 0.f;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const size_t off = (size_t)qrow * D + 16 * kk + 8 * half;
-    const uint4 zq = make_uint4(0, 0, 0, 0);
-    const uint4 uq = qvalid ? ld16(Q + off) : zq;
-    const uint4 ud = qvalid ? ld16(dO + off) : zq;
-    const uint4 uo = qvalid ? ld16(O + off) : zq;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 uq = qvalid ? ld16(Q + off) : z;
+    const uint4 ud = qvalid ? ld16(dO + off) : z;
+    const uint4 uo = qvalid ? ld16(O + off) : z;
     qf[kk] = as_bf16x8(uq);
     dof[kk] = as_bf16x8(ud);
     const uint32_t dw[4] = {ud.x, ud.y, ud.z, ud.w};
@@ -136,8 +195,11 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
     }
   }
   dsum = pair_sum(dsum);
-  if (qvalid && half == 0) a.delta[qoff + qrow] = dsum;
   const float lse2 = qvalid ? a.lse[qoff + qrow] * kLog2e : INFINITY;
+  if (qvalid && half == 0) {
+    a.delta[qoff + qrow] = dsum;
+    a.delta[(size_t)a.BH * a.Tq + qoff + qrow] = lse2;
+  }
   int my_idx = kIdxTailQ, my_hash = 0;
   if (qvalid) {
     my_idx = MODE == kDense ? qrow : a.q_idx[qoff + qrow];
@@ -150,81 +212,51 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[mt][r] = 0.f;
 
-  const List rl = row_list_b<MODE, BS>(a, bh, qb);
-  for (int t = 0; t < rl.n; ++t) {
-    int kb;
-    bool free;
-    row_tile<MODE, BS>(a, rl, t, qb, kb, free);
-    if (kb >= a.nk) continue;  // entries outside the sequence are skipped
-#pragma unroll 1
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int k0 = kb * BS + ch * kChunk;
-      const int kvalid = min(kChunk, a.Tk - k0);
-      if (kvalid <= 0) break;
-      const bool nomask = free && kvalid == kChunk;
-      __syncthreads();
-      stage_rows<D, NT>(sK, K, k0, kvalid);
-      stage_transposed<D, NT>(sKt, K, k0, kvalid);
-      stage_rows<D, NT>(sV, V, k0, kvalid);
-      if (MODE != kDense && !nomask) {
-        for (int r = threadIdx.x; r < kChunk; r += NT) {
-          sKidx[r] = r < kvalid ? a.k_idx[(size_t)bh * a.Tk + k0 + r] : kIdxTailK;
-          if (MODE == kHash) sKhash[r] = r < kvalid ? a.k_hash[(size_t)bh * a.Tk + k0 + r] : 0;
-        }
-      }
-      __syncthreads();
+  int buf = 0;
+  while (have) {
+    Chunk nxt;
+    const bool have_next = next_chunk<MODE, BS, true>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    wait_vmem();
+    __syncthreads();
+    if (have_next) issue(sb[buf ^ 1], nxt);
+    const KVBufB<D> &b = sb[buf];
 
-      f32x16 s[2], dp[2];
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub) {
+      s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, 0), qf[0], kZero16);
+      dp[sub] = mfma32(frag_rows<D>(b.v, lo, sub, 0), dof[0], kZero16);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[sub][r] = 0.f;
-          dp[sub][r] = 0.f;
-        }
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          s[sub] = mfma32(lds_a_rows<D>(sK, 32 * sub + col, kk, half), qf[kk], s[sub]);
-          dp[sub] = mfma32(lds_a_rows<D>(sV, 32 * sub + col, kk, half), dof[kk], dp[sub]);
-        }
+      for (int kk = 1; kk < D / 16; ++kk) {
+        s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, kk), qf[kk], s[sub]);
+        dp[sub] = mfma32(frag_rows<D>(b.v, lo, sub, kk), dof[kk], dp[sub]);
       }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int kr = 32 * sub + 8 * g + 4 * half;
-          int kiv[4] = {0, 0, 0, 0}, khv[4] = {0, 0, 0, 0};
-          if (!nomask) {
-            if (MODE == kDense) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) kiv[e] = kr + e < kvalid ? k0 + kr + e : kIdxTailK;
-            } else {
-              const int4 ki = *reinterpret_cast<const int4 *>(sKidx + kr);
-              kiv[0] = ki.x; kiv[1] = ki.y; kiv[2] = ki.z; kiv[3] = ki.w;
-              if (MODE == kHash) {
-                const int4 kh = *reinterpret_cast<const int4 *>(sKhash + kr);
-                khv[0] = kh.x; khv[1] = kh.y; khv[2] = kh.z; khv[3] = kh.w;
-              }
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const bool ok = nomask || (kiv[e] <= my_idx && (MODE != kHash || khv[e] == my_hash));
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -lse2)) : 0.f;
-            s[sub][r] = p * (dp[sub][r] - dsum);
-          }
-        }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const bf16x8 db = c_regs_to_bf16x8(s[sub], t2);
-#pragma unroll
-          for (int mt = 0; mt < D / 32; ++mt)
-            dqa[mt] = mfma32(lds_a_trans(sKt, 32 * mt + col, 32 * sub + 16 * t2, half), db, dqa[mt]);
-        }
     }
+    // P = exp(scale*S - lse); rows with no admissible key (lse = -inf) only
+    // occur in masked tiles, where the select below discards them.
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -lse2));
+    if (cur.nvalid < kChunk)
+      mask_rows<MODE, true, true>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+    else if (!cur.free)
+      mask_rows<MODE, false, true>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = s[sub][r] * (dp[sub][r] - dsum);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 db = as_bf16x8(c_regs_to_u4(s[sub], t2));
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dqa[mt] = mfma32(frag_trans<D>(b.k, lo, mt, 2 * sub + t2), db, dqa[mt]);
+      }
+    buf ^= 1;
+    cur = nxt;
+    have = have_next;
   }
 
   if (qvalid) {
@@ -242,23 +274,16 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 dK / dV kernel
+// bf16 dK / dV kernel.  Lanes own key columns.
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
 __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dkdv_bf16(AttnArgs a) {
-  constexpr int NT = BS / 32 * 64;
-  constexpr int NCH = BS / kChunk;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * kTPad];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[kChunk * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * kTPad];
-  __shared__ __attribute__((aligned(16))) float sLse[kChunk];
-  __shared__ __attribute__((aligned(16))) float sDel[kChunk];
-  __shared__ __attribute__((aligned(16))) int sQidx[kChunk];
-  __shared__ __attribute__((aligned(16))) int sQhash[kChunk];
+  constexpr int NW = BS / 32;
+  __shared__ __attribute__((aligned(16))) QGBuf<D> sb[2];
 
-  const int bh = blockIdx.x / a.nk;
-  const int kb = blockIdx.x % a.nk;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.nk;
+  const int kb = wg % a.nk;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int krow = kb * BS + 32 * w + col;
@@ -269,6 +294,25 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dkdv_bf16(AttnArgs a) {
   const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + qoff * D;
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + koff * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + koff * D;
+  const float *lse2g = a.delta + (size_t)a.BH * a.Tq + qoff;
+  const float *delg = a.delta + qoff;
+
+  const List cl = col_list_b<MODE, BS>(a, bh, kb);
+  const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
+  const LaneOffsets<D> lo = lane_offsets<D>();
+  auto issue = [&](QGBuf<D> &b, const Chunk &c) {
+    dma_matrix<D, NW>(b.q, Q, c.r0, c.nvalid, dmo);
+    dma_matrix<D, NW>(b.g, dO, c.r0, c.nvalid, dmo);
+    if (w == 0) dma_vec(b.lse2, lse2g, c.r0, c.nvalid);
+    if (w == NW - 1) dma_vec(b.del, delg, c.r0, c.nvalid);
+    if (MODE != kDense && !(c.free && c.nvalid == kChunk)) {
+      if (w == 0) dma_vec(b.idx, a.q_idx + qoff, c.r0, c.nvalid);
+      if (MODE == kHash && w == NW - 1) dma_vec(b.hash, a.q_hash + qoff, c.r0, c.nvalid);
+    }
+  };
+  Chunk cur;
+  bool have = next_chunk<MODE, BS, false>(a, cl, kb, 0, 0, cur);
+  if (have) issue(sb[0], cur);
 
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
@@ -292,90 +336,69 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dkdv_bf16(AttnArgs a) {
       dva[mt][r] = 0.f;
     }
 
-  const List cl = col_list_b<MODE, BS>(a, bh, kb);
-  for (int t = 0; t < cl.n; ++t) {
-    int qb;
-    bool free;
-    col_tile<MODE, BS>(a, cl, t, kb, qb, free);
-    if (qb >= a.nq) continue;
-#pragma unroll 1
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int q0 = qb * BS + ch * kChunk;
-      const int qv = min(kChunk, a.Tq - q0);
-      if (qv <= 0) break;
-      // Query rows past Tq carry lse = +inf (P = 0); key rows past Tk only
-      // pollute their own, never stored, columns.  So a mask-free tile needs
-      // no mask even when either block is partial.
-      const bool nomask = free;
-      __syncthreads();
-      stage_rows<D, NT>(sQ, Q, q0, qv);
-      stage_transposed<D, NT>(sQt, Q, q0, qv);
-      stage_rows<D, NT>(sdO, dO, q0, qv);
-      stage_transposed<D, NT>(sdOt, dO, q0, qv);
-      for (int r = threadIdx.x; r < kChunk; r += NT) {
-        const bool ok = r < qv;
-        sLse[r] = ok ? a.lse[qoff + q0 + r] * kLog2e : INFINITY;
-        sDel[r] = ok ? a.delta[qoff + q0 + r] : 0.f;
-        if (MODE != kDense) sQidx[r] = ok ? a.q_idx[qoff + q0 + r] : kIdxTailQ;
-        else sQidx[r] = ok ? q0 + r : kIdxTailQ;
-        if (MODE == kHash) sQhash[r] = ok ? a.q_hash[qoff + q0 + r] : 0;
-      }
-      __syncthreads();
+  int buf = 0;
+  while (have) {
+    Chunk nxt;
+    const bool have_next = next_chunk<MODE, BS, false>(a, cl, kb, cur.t, cur.ch + 1, nxt);
+    wait_vmem();
+    __syncthreads();
+    if (have_next) issue(sb[buf ^ 1], nxt);
+    const QGBuf<D> &b = sb[buf];
+    // Key rows past Tk only pollute their own (never stored) columns, so a
+    // mask-free tile needs masking only for query rows past Tq.
 
-      f32x16 s[2], dp[2];
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub) {
+      s[sub] = mfma32(frag_rows<D>(b.q, lo, sub, 0), kf[0], kZero16);
+      dp[sub] = mfma32(frag_rows<D>(b.g, lo, sub, 0), vf[0], kZero16);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[sub][r] = 0.f;
-          dp[sub][r] = 0.f;
-        }
+      for (int kk = 1; kk < D / 16; ++kk) {
+        s[sub] = mfma32(frag_rows<D>(b.q, lo, sub, kk), kf[kk], s[sub]);
+        dp[sub] = mfma32(frag_rows<D>(b.g, lo, sub, kk), vf[kk], dp[sub]);
+      }
+    }
+    // P = exp(scale*S - lse) per query row (lse * log2 e staged in LDS).
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          s[sub] = mfma32(lds_a_rows<D>(sQ, 32 * sub + col, kk, half), kf[kk], s[sub]);
-          dp[sub] = mfma32(lds_a_rows<D>(sdO, 32 * sub + col, kk, half), vf[kk], dp[sub]);
-        }
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4 *>(b.lse2 + 32 * sub + 8 * g + 4 * half);
+        s[sub][4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 0], c, -l4.x));
+        s[sub][4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 1], c, -l4.y));
+        s[sub][4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 2], c, -l4.z));
+        s[sub][4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 3], c, -l4.w));
+      }
+    if (cur.nvalid < kChunk)
+      mask_rows<MODE, true, false>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+    else if (!cur.free)
+      mask_rows<MODE, false, false>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+    // dS = P * (dP - D)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4 *>(b.del + 32 * sub + 8 * g + 4 * half);
+        dp[sub][4 * g + 0] = s[sub][4 * g + 0] * (dp[sub][4 * g + 0] - d4.x);
+        dp[sub][4 * g + 1] = s[sub][4 * g + 1] * (dp[sub][4 * g + 1] - d4.y);
+        dp[sub][4 * g + 2] = s[sub][4 * g + 2] * (dp[sub][4 * g + 2] - d4.z);
+        dp[sub][4 * g + 3] = s[sub][4 * g + 3] * (dp[sub][4 * g + 3] - d4.w);
       }
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qr = 32 * sub + 8 * g + 4 * half;
-          const float4 l4 = *reinterpret_cast<const float4 *>(sLse + qr);
-          const float4 d4 = *reinterpret_cast<const float4 *>(sDel + qr);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-          int qiv[4] = {0, 0, 0, 0}, qhv[4] = {0, 0, 0, 0};
-          if (!nomask) {
-            const int4 qi = *reinterpret_cast<const int4 *>(sQidx + qr);
-            qiv[0] = qi.x; qiv[1] = qi.y; qiv[2] = qi.z; qiv[3] = qi.w;
-            if (MODE == kHash) {
-              const int4 qh = *reinterpret_cast<const int4 *>(sQhash + qr);
-              qhv[0] = qh.x; qhv[1] = qh.y; qhv[2] = qh.z; qhv[3] = qh.w;
-            }
-          }
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 pb = as_bf16x8(c_regs_to_u4(s[sub], t2));
+        const bf16x8 db = as_bf16x8(c_regs_to_u4(dp[sub], t2));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const bool ok = nomask || (my_idx <= qiv[e] && (MODE != kHash || qhv[e] == my_hash));
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -lv[e])) : 0.f;
-            s[sub][r] = p;
-            dp[sub][r] = p * (dp[sub][r] - dv4[e]);
-          }
+        for (int mt = 0; mt < D / 32; ++mt) {
+          dva[mt] = mfma32(frag_trans<D>(b.g, lo, mt, 2 * sub + t2), pb, dva[mt]);
+          dka[mt] = mfma32(frag_trans<D>(b.q, lo, mt, 2 * sub + t2), db, dka[mt]);
         }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const bf16x8 pb = c_regs_to_bf16x8(s[sub], t2);
-          const bf16x8 db = c_regs_to_bf16x8(dp[sub], t2);
-#pragma unroll
-          for (int mt = 0; mt < D / 32; ++mt) {
-            dva[mt] = mfma32(lds_a_trans(sdOt, 32 * mt + col, 32 * sub + 16 * t2, half), pb, dva[mt]);
-            dka[mt] = mfma32(lds_a_trans(sQt, 32 * mt + col, 32 * sub + 16 * t2, half), db, dka[mt]);
-          }
-        }
-    }
+      }
+    buf ^= 1;
+    cur = nxt;
+    have = have_next;
   }
 
   if (kvalid_row) {

@@ -18,6 +18,7 @@
 // fp32 kernel: one thread per query, plain fp32 FMAs over 32-key LDS chunks.
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
+#include "scfa_pipe.hpp"
 
 namespace scfa {
 
@@ -60,18 +61,65 @@ __device__ __forceinline__ void tile_at(const AttnArgs &a, const RowList &rl, in
   if (a.force_mask) free = false;
 }
 
+// Position of one 64-key chunk in a row list.
+struct ChunkPos {
+  int t, ch, k0, kvalid;
+  bool free;
+};
+
+// First usable chunk at or after entry t, chunk ch (entries naming a block
+// outside the sequence and chunks past Tk are skipped).  Scalar code.
+template <int MODE, int BS>
+__device__ __forceinline__ bool find_chunk(const AttnArgs &a, const RowList &rl, int qb, int t, int ch, ChunkPos &out) {
+  constexpr int NCH = BS / kChunk;
+  for (; t < rl.n; ++t, ch = 0) {
+    int kb;
+    bool free;
+    tile_at<MODE, BS>(a, rl, t, qb, kb, free);
+    if (kb >= a.nk || ch >= NCH) continue;
+    const int k0 = kb * BS + ch * kChunk;
+    if (k0 >= a.Tk) continue;
+    out.t = t;
+    out.ch = ch;
+    out.k0 = k0;
+    out.kvalid = min(kChunk, a.Tk - k0);
+    out.free = free;
+    return true;
+  }
+  return false;
+}
+
+template <int D>
+struct KVBuf {
+  MatChunk<D> k, v;
+  int idx[kChunk];
+  int hash[kChunk];
+};
+
+template <int MODE, int D, int NW>
+__device__ __forceinline__ void issue_kv(KVBuf<D> &b, const AttnArgs &a, const uint16_t *K, const uint16_t *V,
+                                         int bh, const ChunkPos &c, const DmaOffsets<D, NW> &dof) {
+  dma_matrix<D, NW>(b.k, K, c.k0, c.kvalid, dof);
+  dma_matrix<D, NW>(b.v, V, c.k0, c.kvalid, dof);
+  if (MODE != kDense && !(c.free && c.kvalid == kChunk)) {
+    const int w = threadIdx.x >> 6;
+    if (w == 0) dma_vec(b.idx, a.k_idx + (size_t)bh * a.Tk, c.k0, c.kvalid);
+    if (MODE == kHash && w == NW - 1) dma_vec(b.hash, a.k_hash + (size_t)bh * a.Tk, c.k0, c.kvalid);
+  }
+}
+
+// Lazy-rescale threshold of the online softmax, in log2 units: the reference
+// max is only raised when a score exceeds it by more than this, so P <= 2^8.
+constexpr float kRescaleLog2 = 8.f;
+
 template <int MODE, int D, int BS>
 __global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
-  constexpr int NT = NW * 64;
-  constexpr int NCH = BS / kChunk;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * kTPad];
-  __shared__ __attribute__((aligned(16))) int sKidx[kChunk];
-  __shared__ __attribute__((aligned(16))) int sKhash[kChunk];
+  __shared__ __attribute__((aligned(16))) KVBuf<D> sb[2];
 
-  const int bh = blockIdx.x / a.nq;
-  const int qb = blockIdx.x % a.nq;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.nq;
+  const int qb = wg % a.nq;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qb * BS + 32 * w + col;
@@ -79,6 +127,13 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
   const uint16_t *Q = static_cast<const uint16_t *>(a.q) + (size_t)bh * a.Tq * D;
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
+
+  const RowList rl = row_list<MODE, BS>(a, bh, qb);
+  const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
+  ChunkPos cur;
+  bool have = find_chunk<MODE, BS>(a, rl, qb, 0, 0, cur);
+  if (have) issue_kv<MODE, D, NW>(sb[0], a, K, V, bh, cur, dof);
+  const LaneOffsets<D> lo = lane_offsets<D>();
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -90,107 +145,77 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
     if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
   }
 
-  const RowList rl = row_list<MODE, BS>(a, bh, qb);
   const float c = a.scale * kLog2e;
-  float m = -INFINITY, l = 0.f;
+  float mref = -INFINITY, l = 0.f;
   f32x16 acc[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
-  for (int t = 0; t < rl.n; ++t) {
-    int kb;
-    bool free;
-    tile_at<MODE, BS>(a, rl, t, qb, kb, free);
-    if (kb >= a.nk) continue;  // entries outside the sequence are skipped
-#pragma unroll 1
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int k0 = kb * BS + ch * kChunk;
-      const int kvalid = min(kChunk, a.Tk - k0);
-      if (kvalid <= 0) break;
-      const bool nomask = free && kvalid == kChunk;
-      __syncthreads();
-      stage_rows<D, NT>(sK, K, k0, kvalid);
-      stage_transposed<D, NT>(sVt, V, k0, kvalid);
-      if (MODE != kDense && !nomask) {
-        for (int r = threadIdx.x; r < kChunk; r += NT) {
-          sKidx[r] = r < kvalid ? a.k_idx[(size_t)bh * a.Tk + k0 + r] : kIdxTailK;
-          if (MODE == kHash) sKhash[r] = r < kvalid ? a.k_hash[(size_t)bh * a.Tk + k0 + r] : 0;
-        }
-      }
-      __syncthreads();
+  int buf = 0;
+  while (have) {
+    ChunkPos nxt;
+    const bool have_next = find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    wait_vmem();
+    __syncthreads();
+    if (have_next) issue_kv<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, dof);
+    const KVBuf<D> &b = sb[buf];
 
-      f32x16 s[2];
+    f32x16 s[2];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub) {
+      s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, 0), qf[0], kZero16);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) s[sub] = mfma32(lds_a_rows<D>(sK, 32 * sub + col, kk, half), qf[kk], s[sub]);
-      }
-      if (!nomask) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int kr = 32 * sub + 8 * g + 4 * half;
-            int4 ki, kh = make_int4(0, 0, 0, 0);
-            if (MODE == kDense) {
-              ki.x = kr + 0 < kvalid ? k0 + kr + 0 : kIdxTailK;
-              ki.y = kr + 1 < kvalid ? k0 + kr + 1 : kIdxTailK;
-              ki.z = kr + 2 < kvalid ? k0 + kr + 2 : kIdxTailK;
-              ki.w = kr + 3 < kvalid ? k0 + kr + 3 : kIdxTailK;
-            } else {
-              ki = *reinterpret_cast<const int4 *>(sKidx + kr);
-              if (MODE == kHash) kh = *reinterpret_cast<const int4 *>(sKhash + kr);
-            }
-            const int kiv[4] = {ki.x, ki.y, ki.z, ki.w};
-            const int khv[4] = {kh.x, kh.y, kh.z, kh.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool ok = kiv[e] <= my_idx && (MODE != kHash || khv[e] == my_hash);
-              if (!ok) s[sub][4 * g + e] = -INFINITY;
-            }
-          }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
-      const float mc = m_use * c;
-      float rs = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -mc));
-          s[sub][r] = p;
-          rs += p;
-        }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
-
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const bf16x8 pb = c_regs_to_bf16x8(s[sub], t2);
-#pragma unroll
-          for (int mt = 0; mt < D / 32; ++mt)
-            acc[mt] = mfma32(lds_a_trans(sVt, 32 * mt + col, 32 * sub + 16 * t2, half), pb, acc[mt]);
-        }
+      for (int kk = 1; kk < D / 16; ++kk) s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, kk), qf[kk], s[sub]);
     }
+    if (cur.kvalid < kChunk)
+      mask_rows<MODE, true, true>(s, b.idx, b.hash, cur.k0, cur.kvalid, my_idx, my_hash, half, -INFINITY);
+    else if (!cur.free)
+      mask_rows<MODE, false, true>(s, b.idx, b.hash, cur.k0, cur.kvalid, my_idx, my_hash, half, -INFINITY);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+    mx = pair_max(mx);
+    // Only real query rows vote: rows past Tq are unmasked on mask-free tiles
+    // and must not change the rescale schedule of the others.
+    const bool need = qvalid & (mx * c > mref * c + kRescaleLog2);
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float m_new = fmaxf(mref, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mref - m_new) * c);
+      // A lane whose reference is still -inf has seen no admissible key: its
+      // accumulator is zero, so the multiply is skipped while that holds for all.
+      if (__builtin_amdgcn_ballot_w64(mref != -INFINITY) != 0ull) {
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
+      }
+      l *= alpha;
+      mref = m_new;
+    }
+    const float mc = mref == -INFINITY ? 0.f : mref * c;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -mc));
+
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const uint4 pk = c_regs_to_u4(s[sub], t2);
+        l = add_bf16x8(pk, l);
+        const bf16x8 pb = as_bf16x8(pk);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma32(frag_trans<D>(b.v, lo, mt, 2 * sub + t2), pb, acc[mt]);
+      }
+    buf ^= 1;
+    cur = nxt;
+    have = have_next;
   }
 
   const float lt = pair_sum(l);
@@ -206,7 +231,7 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
                                      pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv));
         *reinterpret_cast<uint2 *>(O + d0) = val;
       }
-    if (half == 0) a.out_lse[(size_t)bh * a.Tq + qrow] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+    if (half == 0) a.out_lse[(size_t)bh * a.Tq + qrow] = lt > 0.f ? mref * a.scale + logf(lt) : -INFINITY;
   }
 }
 

@@ -1,0 +1,229 @@
+// Chunk pipeline shared by the bf16 attention kernels (gfx950).
+//
+// A "chunk" is 64 consecutive rows of two [T, D] bf16 matrices (K and V in
+// the forward and dQ kernels, Q and dO in the dK/dV kernel) plus up to four
+// 64-entry int/float vectors (positions, buckets, lse, D).  Chunks are copied
+// global -> LDS with global_load_lds_dwordx4 (lane l's 16 bytes land at
+// dst + 16*l whatever the source address), double-buffered, so no VGPRs or
+// ds_write instructions are spent on staging.
+//
+// LDS layout of a matrix: row-major, 16-byte pieces XOR-swizzled inside each
+// row: logical piece c of row r sits at physical piece c ^ (r & 7).  The
+// swizzle is applied through the DMA source addresses.  Rows past the end of
+// the sequence are filled with copies of the last real row (finite values);
+// the kernels mask them explicitly.
+//
+// Fragment reads for v_mfma_f32_32x32x16_bf16 (lane l, col = l % 32,
+// half = l / 32):
+//  * frag_rows: A operand whose rows are chunk rows (row r = 32*sub + col,
+//    k = 8 consecutive columns 16*kk + 8*half ..): one ds_read_b128.
+//  * frag_trans: A operand whose rows are matrix COLUMNS (column
+//    32*mt + col) and whose k items are 8 chunk rows: rows 16t + 4*half + 0..3
+//    (items 0..3) and 16t + 8 + 4*half + 0..3 (items 4..7), built from two
+//    ds_read_b64_tr_b16.  That row order is exactly the order in which a C
+//    tile's registers 8t'..8t'+7 (rows 8*(r/4) + 4*half + r%4) hold their
+//    rows, so a C tile converted to bf16 is the matching B operand.
+//    ds_read_b64_tr_b16 within each group of 16 lanes returns to lane 4a+b
+//    element b of the 8-byte pieces read by lanes a, a+4, a+8, a+12.
+#pragma once
+
+#include "scfa_device.hpp"
+
+namespace scfa {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ lds_void *to_lds(const void *p) {
+  return (lds_void *)(p);  // generic -> LDS address space (the pointer is an LDS pointer)
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// global->LDS copies) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Hardware dispatches work group i to XCD i % 8.  Give each XCD a contiguous
+// range of logical ids so the blocks of one head share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int q = n / 8, r = n % 8;
+  const int xcd = i % 8, slot = i / 8;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+template <int D>
+struct MatChunk {
+  uint16_t v[kChunk * D];
+};
+
+// Per-lane source offsets (elements, relative to row0) of this wave's DMA
+// pieces of a full chunk; a chunk copy is then one 64-bit add per piece.
+template <int D, int NW>
+struct DmaOffsets {
+  static constexpr int CPR = D / 8;
+  static constexpr int NINST = kChunk * CPR / 64;  // 16-byte-piece instructions per chunk
+  static constexpr int PER_WAVE = (NINST + NW - 1) / NW;
+  int off[PER_WAVE];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ DmaOffsets<D, NW> dma_offsets() {
+  using O = DmaOffsets<D, NW>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  O o;
+#pragma unroll
+  for (int k = 0; k < O::PER_WAVE; ++k) {
+    const int i = k * NW + w;
+    const int s = i * 64 + lane;
+    const int r = s / O::CPR, p = s % O::CPR;
+    o.off[k] = r * D + ((p ^ (r & 7)) << 3);
+  }
+  return o;
+}
+
+// Copy rows row0 .. row0+63 of g ([T, D], this head) into an LDS chunk.
+// Rows at or past row0 + nvalid repeat row row0 + nvalid - 1 (nvalid >= 1).
+// Work is split over the NW waves of the group: 16-byte pieces, 64 per
+// instruction.
+template <int D, int NW>
+__device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, int row0, int nvalid,
+                                           const DmaOffsets<D, NW> &o) {
+  using O = DmaOffsets<D, NW>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint16_t *base = g + (size_t)row0 * D;
+#pragma unroll
+  for (int k = 0; k < O::PER_WAVE; ++k) {
+    const int i = k * NW + w;
+    if (O::NINST % NW == 0 || i < O::NINST) {
+      const uint16_t *src;
+      if (nvalid == kChunk) {
+        src = base + o.off[k];
+      } else {
+        const int s = i * 64 + lane;
+        const int r = s / O::CPR, p = s % O::CPR;
+        const int rr = r < nvalid ? r : nvalid - 1;
+        src = base + rr * D + ((p ^ (r & 7)) << 3);
+      }
+#if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only (the host pass never emits this code)
+      __builtin_amdgcn_global_load_lds(src, to_lds(dst.v + i * 512), 16, 0, 0);
+#endif
+    }
+  }
+}
+
+// Copy 64 consecutive 4-byte values (clamped like dma_matrix) with one wave.
+__device__ __forceinline__ void dma_vec(void *dst, const void *g, int row0, int nvalid) {
+  const int lane = threadIdx.x & 63;
+  const int rr = lane < nvalid ? lane : nvalid - 1;
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(static_cast<const uint32_t *>(g) + row0 + rr, to_lds(dst), 4, 0, 0);
+#endif
+}
+
+// Per-lane element offsets of the fragment reads inside a MatChunk<D>, computed
+// once per kernel so every read in the main loop is base + lane offset +
+// compile-time constant (an LDS instruction immediate).
+//  rows[kk]: frag_rows(row = col, kk); add 32*sub*D for sub-tile sub.
+//  trans[mt]: first read of frag_trans(mt, t = 0); add 16*t*D for k-step t and
+//             8*D for the second read (rows r and r + 8 share r & 7).
+template <int D>
+struct LaneOffsets {
+  int rows[D / 16];
+  int trans[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets() {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  LaneOffsets<D> o;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) o.rows[kk] = col * D + (((2 * kk + half) ^ (col & 7)) << 3);
+  const int j = lane & 15, a = j & 3, mm = j >> 2, g = lane >> 4, h = g >> 1;
+  const int x = 4 * h + mm;  // == r & 7 for both rows a lane reads
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+    const int c = 4 * mt + 2 * (g & 1) + (a >> 1);
+    o.trans[mt] = x * D + ((c ^ x) << 3) + 4 * (a & 1);
+  }
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows(const MatChunk<D> &m, const LaneOffsets<D> &o, int sub, int kk) {
+  return as_bf16x8(*reinterpret_cast<const uint4 *>(m.v + o.rows[kk] + 32 * sub * D));
+}
+
+// A operand over matrix columns 32*mt + (l % 32) and chunk rows of k-step t.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_trans(const MatChunk<D> &m, const LaneOffsets<D> &o, int mt, int t) {
+  const uint16_t *p0 = m.v + o.trans[mt] + 16 * t * D;
+#if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only
+  const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0));
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0 + 8 * D));
+#else
+  const i16x4 x0 = {}, x1 = {};
+#endif
+  const uint2 lo = __builtin_bit_cast(uint2, x0), hi = __builtin_bit_cast(uint2, x1);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Sum of eight bf16 values packed in a uint4, accumulated into acc (fp32)
+// with v_dot2 against (1, 1).
+__device__ __forceinline__ float add_bf16x8(uint4 u, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.z), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.w), one, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ uint4 c_regs_to_u4(const f32x16 &c, int t) {
+  uint4 u;
+  u.x = pack_bf16x2(c[8 * t + 0], c[8 * t + 1]);
+  u.y = pack_bf16x2(c[8 * t + 2], c[8 * t + 3]);
+  u.z = pack_bf16x2(c[8 * t + 4], c[8 * t + 5]);
+  u.w = pack_bf16x2(c[8 * t + 6], c[8 * t + 7]);
+  return u;
+}
+
+// Element mask over a pair of C tiles whose rows are chunk rows r0 + 32*sub +
+// 8g + 4*half + e.  LANE_IS_QUERY: the lane's column is a query (my_idx is a
+// query position, rows are keys): admissible iff row_idx <= my_idx.
+// Otherwise the lane's column is a key and rows are queries: admissible iff
+// my_idx <= row_idx.  Hash mode also needs equal bucket ids; with TAIL, rows at
+// or past nvalid (copies of a real row) are inadmissible.  Inadmissible entries
+// are replaced by `fill`.  Branch-free (compare + select).
+template <int MODE, bool TAIL, bool LANE_IS_QUERY>
+__device__ __forceinline__ void mask_rows(f32x16 (&s)[2], const int *sidx, const int *shash, int r0, int nvalid,
+                                          int my_idx, int my_hash, int half, float fill) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rr = 32 * sub + 8 * g + 4 * half;
+      int iv[4], hv[4] = {0, 0, 0, 0};
+      if (MODE == kDense) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) iv[e] = r0 + rr + e;
+      } else {
+        const int4 ki = *reinterpret_cast<const int4 *>(sidx + rr);
+        iv[0] = ki.x, iv[1] = ki.y, iv[2] = ki.z, iv[3] = ki.w;
+        if (MODE == kHash) {
+          const int4 kh = *reinterpret_cast<const int4 *>(shash + rr);
+          hv[0] = kh.x, hv[1] = kh.y, hv[2] = kh.z, hv[3] = kh.w;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool ok = LANE_IS_QUERY ? iv[e] <= my_idx : my_idx <= iv[e];
+        if (MODE == kHash) ok = ok & (hv[e] == my_hash);
+        if (TAIL) ok = ok & (rr + e < nvalid);
+        s[sub][4 * g + e] = ok ? s[sub][4 * g + e] : fill;
+      }
+    }
+}
+
+}  // namespace scfa

@@ -134,7 +134,7 @@ def test_workspace_sizes():
     r = lambda n: (n + 255) // 256 * 256  # noqa: E731
     BH, nq, nk, Tq = 2 * 3, 4, 2, 200
     fwd = r(BH * nq * 16) + r(BH * nk * 16) + r(BH * nq * 4) + r(BH * nq * nk * 4)
-    bwd = fwd + r(BH * nk * 4) + r(BH * nk * nq * 4) + r(BH * Tq * 4)
+    bwd = fwd + r(BH * nk * 4) + r(BH * nk * nq * 4) + r(2 * BH * Tq * 4)
     assert ws(_lib.OP_QK_FWD, 2, 3, 200, 100, 64, 64, 0) == fwd
     assert ws(_lib.OP_HASH_BWD, 2, 3, 200, 100, 64, 64, 0) == bwd
     assert ws(_lib.OP_QK_FWD, 0, 3, 200, 100, 64, 64, 0) == 0
