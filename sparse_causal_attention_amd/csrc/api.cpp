@@ -266,10 +266,11 @@ int attention(const AttnCall &c) {
   return ok();
 }
 
-size_t lsh_ws(int B, int H, int T, int nb) {
+size_t lsh_ws(int B, int H, int T, int d, int nb) {
   const size_t BH = (size_t)B * H;
   const size_t nbins = (size_t)scfa::sort_bins(nb, true);
-  return round_up(BH * T * 4) + round_up(BH * nbins * scfa::sort_chunks(T) * 4) + 4 * round_up(BH * T * 4);
+  return round_up(BH * T * 4) + round_up(BH * nbins * scfa::sort_chunks(T) * 4) + 4 * round_up(BH * T * 4) +
+         round_up((size_t)H * d * scfa::lsh_r64_cols(nb) * 8);
 }
 
 }  // namespace
@@ -402,7 +403,7 @@ int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int 
   if (companion && ((rc = check_ptr(companion, nX, 16, "companion")) ||
                     (rc = check_ptr(companion_sorted, nX, 16, "companion_sorted"))))
     return rc;
-  const size_t need = T > 0 ? lsh_ws(B, H, T, n_buckets) : 0;
+  const size_t need = T > 0 ? lsh_ws(B, H, T, d, n_buckets) : 0;
   if ((rc = check_ws(workspace, workspace_bytes, need))) return rc;
 
   scfa::LshArgs a{};
@@ -431,6 +432,7 @@ int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int 
     a.tmp_idx[1] = cv.take<int32_t>(BH * T * 4);
     a.tmp_src[0] = cv.take<int32_t>(BH * T * 4);
     a.tmp_src[1] = cv.take<int32_t>(BH * T * 4);
+    a.R64 = cv.take<double>((size_t)H * d * scfa::lsh_r64_cols(n_buckets) * 8);
   }
   hipError_t e = scfa::launch_lsh_bucket_sort(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "lsh bucket sort");
@@ -493,8 +495,8 @@ size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int bloc
       if (Tk < 0 || (block != 64 && block != 128)) return 0;
       return attn_ws(op == SCFA_OP_QK_BWD || op == SCFA_OP_HASH_BWD, B, H, Tq, Tk, block);
     case SCFA_OP_LSH_SORT:
-      if (n_buckets < 2 || n_buckets > 1024 || (n_buckets & 1)) return 0;
-      return Tq > 0 ? lsh_ws(B, H, Tq, n_buckets) : 0;
+      if (n_buckets < 2 || n_buckets > 1024 || (n_buckets & 1) || (d != 64 && d != 128)) return 0;
+      return Tq > 0 ? lsh_ws(B, H, Tq, d, n_buckets) : 0;
     default:
       return 0;
   }

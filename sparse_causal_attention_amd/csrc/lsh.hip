@@ -9,80 +9,174 @@
 // product bf16*fp32 or fp32*fp32 is exact in float64, so fma and mul+add agree
 // and the ids are bit-reproducible.
 //
-// Sort: least-significant-digit counting sort per (b, h) segment.  Each pass
-// is histogram -> exclusive scan over (digit, chunk) -> stable scatter, with
-// ranks inside a wave from ballot-based digit matching.  When positions are
-// already ascending (the usual case) a single pass keyed by bucket suffices;
-// otherwise four byte passes over the position come first.
+// Sort: least-significant-digit counting sort per (b, h) segment over chunks
+// of 256 tokens (one work group).  Each pass is histogram -> exclusive scan
+// over (digit, chunk) -> stable scatter, with ranks inside a wave from
+// ballot-based digit matching.  When positions are already ascending (the
+// usual case) a single pass keyed by bucket suffices: the hash kernel then
+// also writes the bucket histogram of its chunk, and the scatter copies the
+// token rows (x and a companion tensor) to their sorted slots, so the whole
+// call is three launches.  Otherwise four byte passes over the position come
+// first.
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
 
 namespace scfa {
 
-constexpr int kHashThreads = 256;
+constexpr int kHashThreads = kSortChunk;
 
-// One thread per token.  R's columns are processed in groups of CG (8, 16 or
-// 32, the smallest that covers nb/2 or 32): the group is widened to float64
-// once into LDS and every thread accumulates CG float64 sums over the
-// coordinates in increasing order, eight coordinates (one 16-byte load of x)
-// per step.
+// R ([H, d, half] float32) widened to float64 once per call and regrouped by
+// column group: R64[h][g][k][c] = R[h][k][g*CG + c] for g*CG + c < half, else
+// 0 ([H, cols/CG, d, CG] doubles in the workspace), so a group's values for
+// consecutive coordinates are CG apart.
+__global__ __launch_bounds__(256) void k_r_to_f64(const float *R, double *R64, int half, int cg_size, int d, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = i % cg_size;
+  const int k = (i / cg_size) % d;
+  const int hg = i / (cg_size * d);
+  const int ngroups = (half + cg_size - 1) / cg_size;
+  const int h = hg / ngroups, g = hg % ngroups;
+  const int col = g * cg_size + c;
+  R64[i] = col < half ? (double)R[((size_t)h * d + k) * half + col] : 0.0;
+}
+
+typedef __attribute__((address_space(4))) const double const_double;
+
+// One thread per token, one 256-token sort chunk per work group.  R (float64)
+// is read through the scalar unit: its addresses are uniform across the work
+// group, so every product takes its R operand from scalar registers.  The x
+// rows of the chunk pass through LDS in 64-byte column slabs (coalesced
+// global loads, double-buffered, one barrier per slab; an 80-byte row pitch
+// keeps each thread's 16-byte row reads conflict-free), because a thread
+// reading its own row straight from memory touches one cache line per lane
+// per load.  The CG column sums (8, 16 or 32 at a time) accumulate in float64
+// over the coordinates in increasing order.  With `hist` set, the group also
+// writes its chunk's bucket histogram.
+constexpr int kSlabBytes = 64;
+constexpr int kSlabPitch = 80;
+
+// Coordinate k (0 .. 4*KP-1) of a slab row held as four 16-byte pieces.
+template <bool F32, int KP>
+__device__ __forceinline__ float slab_coord(const uint4 (&u)[4], int k) {
+  const uint4 p = u[k / KP];
+  const int e = k % KP;
+  if (F32) {
+    const uint32_t w = e == 0 ? p.x : e == 1 ? p.y : e == 2 ? p.z : p.w;
+    return __uint_as_float(w);
+  }
+  const int wi = e >> 1;
+  const uint32_t w = wi == 0 ? p.x : wi == 1 ? p.y : wi == 2 ? p.z : p.w;
+  return bf16_bits_to_float((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// R values of step st of a slab (see k_lsh_hash), from Rs = the column
+// group's values for the slab's first coordinate: CG >= 16: coordinate
+// st / (CG/16), columns 16*(st % (CG/16)) .. +15; CG == 8: coordinates 2*st
+// and 2*st + 1, columns 0 .. 7.  All offsets are compile-time constants.
+template <int CG>
+__device__ __forceinline__ void load_r_step(double (&r)[16], const_double *Rs, int st) {
+  const_double *p = Rs + (CG >= 16 ? (st / (CG / 16)) * CG + (st % (CG / 16)) * 16 : 16 * st);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = p[i];
+}
+
 template <int D, int CG, bool F32>
-__global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a) {
-  __shared__ __attribute__((aligned(16))) double sR[D * CG];
-  const int nblk = (a.T + kHashThreads - 1) / kHashThreads;
-  const int bh = blockIdx.x / nblk;
-  const int tb = blockIdx.x % nblk;
+__global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a, const double *R64, int32_t *hist, int nchunks) {
+  constexpr int ES = F32 ? 4 : 2;          // bytes per coordinate
+  constexpr int RB = D * ES;               // bytes per row
+  constexpr int NS = RB / kSlabBytes;      // slabs per row
+  constexpr int KP = 16 / ES;              // coordinates per 16-byte piece
+  constexpr int PPS = kSlabBytes / 16;     // pieces per slab
+  constexpr int NSS = PPS * KP * CG / 16;  // 16-value R steps per slab
+  static_assert(kHashThreads == 256 && PPS == 4, "staging assumes 256 rows x 4 pieces");
+  __shared__ __align__(16) unsigned char xs[2][kHashThreads * kSlabPitch];
+
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / nchunks;
+  const int tb = blockIdx.x % nchunks;
   const int h = bh % a.H;
-  const int t = tb * kHashThreads + threadIdx.x;
+  const int t0 = tb * kHashThreads;
+  const int t = t0 + tid;
   const bool valid = t < a.T;
   const int half = a.nb / 2;
-  const float *R = a.R + (size_t)h * D * half;
-  const size_t row = (size_t)bh * a.T + (valid ? t : 0);
+  const int ngroups = (half + CG - 1) / CG;
+  const_double *Rh = (const_double *)(R64 + (size_t)h * ngroups * D * CG);
+  const char *xb = static_cast<const char *>(a.x) + (size_t)bh * a.T * RB;
+
+  // staging: this thread copies piece (tid & 3) of rows (tid >> 2) + 64j,
+  // j = 0..3; rows past the end repeat the last row (never compared)
+  const int sr = tid >> 2, sp = (tid & 3) * 16;
+  const char *src0 = xb + (size_t)min(t0 + sr, a.T - 1) * RB + sp;
+  const char *src1 = xb + (size_t)min(t0 + sr + 64, a.T - 1) * RB + sp;
+  const char *src2 = xb + (size_t)min(t0 + sr + 128, a.T - 1) * RB + sp;
+  const char *src3 = xb + (size_t)min(t0 + sr + 192, a.T - 1) * RB + sp;
+  const int dst0 = sr * kSlabPitch + sp;  // rows +64j: + 64 * j * kSlabPitch
+  uint4 st0 = *reinterpret_cast<const uint4 *>(src0);
+  uint4 st1 = *reinterpret_cast<const uint4 *>(src1);
+  uint4 st2 = *reinterpret_cast<const uint4 *>(src2);
+  uint4 st3 = *reinterpret_cast<const uint4 *>(src3);
 
   double best = -INFINITY, worst = INFINITY;
   int besti = 0, worsti = 0;
+  int buf = 0;
   for (int cg = 0; cg < half; cg += CG) {
-    const int ncol = min(CG, half - cg);
-    __syncthreads();
-    for (int i = threadIdx.x; i < D * CG; i += kHashThreads) {
-      const int k = i / CG, cc = i % CG;
-      sR[i] = cc < ncol ? (double)R[(size_t)k * half + cg + cc] : 0.0;
-    }
-    __syncthreads();
     double acc[CG];
 #pragma unroll
     for (int cc = 0; cc < CG; ++cc) acc[cc] = 0.0;
 #pragma unroll 1
-    for (int k0 = 0; k0 < D; k0 += 8) {
-      float xv[8];
-      if (F32) {
-        const float *X = static_cast<const float *>(a.x) + row * D + k0;
-        const float4 v0 = valid ? *reinterpret_cast<const float4 *>(X) : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 v1 = valid ? *reinterpret_cast<const float4 *>(X + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
-        xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
-      } else {
-        const uint16_t *X = static_cast<const uint16_t *>(a.x) + row * D + k0;
-        const uint4 v = valid ? ld16(X) : make_uint4(0, 0, 0, 0);
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    for (int sl = 0; sl < NS; ++sl) {
+      unsigned char *xbuf = xs[buf];
+      *reinterpret_cast<uint4 *>(xbuf + dst0) = st0;
+      *reinterpret_cast<uint4 *>(xbuf + dst0 + 64 * kSlabPitch) = st1;
+      *reinterpret_cast<uint4 *>(xbuf + dst0 + 128 * kSlabPitch) = st2;
+      *reinterpret_cast<uint4 *>(xbuf + dst0 + 192 * kSlabPitch) = st3;
+      // next slab (wrapping to slab 0 for the next column group; one
+      // redundant in-range load at the very end)
+      const int nso = (sl + 1 < NS ? sl + 1 : 0) * kSlabBytes;
+      st0 = *reinterpret_cast<const uint4 *>(src0 + nso);
+      st1 = *reinterpret_cast<const uint4 *>(src1 + nso);
+      st2 = *reinterpret_cast<const uint4 *>(src2 + nso);
+      st3 = *reinterpret_cast<const uint4 *>(src3 + nso);
+      __syncthreads();
+      // this thread's row of the slab: PPS pieces of KP coordinates
+      uint4 u[PPS];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xv[2 * e] = bf16_bits_to_float(wv[e] & 0xffffu);
-          xv[2 * e + 1] = bf16_bits_to_float(wv[e] >> 16);
+      for (int pc = 0; pc < PPS; ++pc) u[pc] = *reinterpret_cast<const uint4 *>(xbuf + tid * kSlabPitch + pc * 16);
+      // column group cg, first coordinate of the slab
+      const_double *Rs = Rh + ((size_t)(cg / CG) * D + sl * PPS * KP) * CG;
+      // The slab's products run in steps of 16 R values (one s_load_dwordx16
+      // pair): one coordinate x 16 columns (CG 16), half a coordinate (CG 32)
+      // or two coordinates x 8 columns (CG 8).  The next step's R values are
+      // requested before the current step's FMAs so their latency overlaps.
+      double rn[16];
+      load_r_step<CG>(rn, Rs, 0);
+#pragma unroll
+      for (int st = 0; st < NSS; ++st) {
+        double rc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rc[i] = rn[i];
+        if (st + 1 < NSS) load_r_step<CG>(rn, Rs, st + 1);
+        if (CG >= 16) {
+          const int k = st / (CG / 16), c0 = (st % (CG / 16)) * 16;
+          const double xk = (double)slab_coord<F32, KP>(u, k);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[c0 + i] = fma(xk, rc[i], acc[c0 + i]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const double xk = (double)slab_coord<F32, KP>(u, 2 * st + j);
+#pragma unroll
+            for (int i = 0; i < CG; ++i) acc[i] = fma(xk, rc[8 * j + i], acc[i]);
+          }
         }
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_sched_barrier(0);  // bounds the R values live in scalar registers
+#endif
       }
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const double xk = (double)xv[kk];
-        const double2 *r2 = reinterpret_cast<const double2 *>(sR + (k0 + kk) * CG);
-#pragma unroll
-        for (int c2 = 0; c2 < CG / 2; ++c2) {
-          const double2 r = r2[c2];
-          acc[2 * c2] = fma(xk, r.x, acc[2 * c2]);
-          acc[2 * c2 + 1] = fma(xk, r.y, acc[2 * c2 + 1]);
-        }
-      }
+      buf ^= 1;
     }
+    const int ncol = min(CG, half - cg);
 #pragma unroll
     for (int cc = 0; cc < CG; ++cc) {
       if (cc < ncol) {
@@ -98,21 +192,37 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a) {
       }
     }
   }
-  if (valid) a.hash[(size_t)bh * a.T + t] = best >= -worst ? besti : half + worsti;
+  const int bucket = best >= -worst ? besti : half + worsti;
+  if (valid) a.hash[(size_t)bh * a.T + t] = bucket;
+  if (hist) {
+    // the staging buffers are free once every thread has read its last slab
+    int *sh = reinterpret_cast<int *>(&xs[0][0]);
+    __syncthreads();
+    for (int i = tid; i < a.nb; i += kHashThreads) sh[i] = 0;
+    __syncthreads();
+    if (valid) atomicAdd(&sh[bucket], 1);
+    __syncthreads();
+    for (int i = tid; i < a.nb; i += kHashThreads) hist[((size_t)bh * a.nb + i) * nchunks + tb] = sh[i];
+  }
 }
 
 template <int D, int CG>
-static void launch_hash_cg(const LshArgs &a, unsigned grid, hipStream_t s) {
-  if (a.dtype == 1) hipLaunchKernelGGL((k_lsh_hash<D, CG, true>), dim3(grid), dim3(kHashThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_lsh_hash<D, CG, false>), dim3(grid), dim3(kHashThreads), 0, s, a);
+static void launch_hash_cg(const LshArgs &a, const double *R64, int32_t *hist, int nchunks, unsigned grid,
+                           hipStream_t s) {
+  if (a.dtype == 1)
+    hipLaunchKernelGGL((k_lsh_hash<D, CG, true>), dim3(grid), dim3(kHashThreads), 0, s, a, R64, hist, nchunks);
+  else
+    hipLaunchKernelGGL((k_lsh_hash<D, CG, false>), dim3(grid), dim3(kHashThreads), 0, s, a, R64, hist, nchunks);
 }
 
 template <int D>
-static void launch_hash(const LshArgs &a, unsigned grid, hipStream_t s) {
+static void launch_hash(const LshArgs &a, const double *R64, int32_t *hist, int nchunks, unsigned grid,
+                        hipStream_t s) {
   const int half = a.nb / 2;
-  if (half <= 8) launch_hash_cg<D, 8>(a, grid, s);
-  else if (half <= 16) launch_hash_cg<D, 16>(a, grid, s);
-  else launch_hash_cg<D, 32>(a, grid, s);
+  const int g = lsh_col_group(a.nb);
+  if (g == 8) launch_hash_cg<D, 8>(a, R64, hist, nchunks, grid, s);
+  else if (g == 16) launch_hash_cg<D, 16>(a, R64, hist, nchunks, grid, s);
+  else launch_hash_cg<D, 32>(a, R64, hist, nchunks, grid, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -127,27 +237,36 @@ struct SortPass {
   int T, nbins, nbits, nchunks, shift, bucket_pass;
 };
 
+// Rows moved by the final pass: x[src] -> xs[slot], cmp[src] -> cs[slot].
+struct RowCopy {
+  const uint4 *x;
+  uint4 *xs;
+  const uint4 *cmp;
+  uint4 *cs;
+  int pieces;  // 16-byte pieces per row: 8, 16 or 32
+};
+
 __device__ __forceinline__ void item_at(const SortPass &p, size_t base, int pos, int &idx, int &src, int &digit) {
   idx = p.in_idx ? p.in_idx[base + pos] : pos;
   src = p.in_src ? p.in_src[base + pos] : pos;
   digit = p.bucket_pass ? p.hash[base + src] : ((unsigned)idx >> p.shift) & 255u;
 }
 
-__global__ __launch_bounds__(256) void k_sort_hist(SortPass p) {
+__global__ __launch_bounds__(kSortChunk) void k_sort_hist(SortPass p) {
   extern __shared__ int sh[];
   const int bh = blockIdx.x / p.nchunks;
   const int chunk = blockIdx.x % p.nchunks;
   const size_t base = (size_t)bh * p.T;
-  for (int i = threadIdx.x; i < p.nbins; i += 256) sh[i] = 0;
+  for (int i = threadIdx.x; i < p.nbins; i += kSortChunk) sh[i] = 0;
   __syncthreads();
-  const int c1 = min(p.T, (chunk + 1) * kSortChunk);
-  for (int pos = chunk * kSortChunk + threadIdx.x; pos < c1; pos += 256) {
+  const int pos = chunk * kSortChunk + threadIdx.x;
+  if (pos < p.T) {
     int idx, src, digit;
     item_at(p, base, pos, idx, src, digit);
     atomicAdd(&sh[digit], 1);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < p.nbins; i += 256)
+  for (int i = threadIdx.x; i < p.nbins; i += kSortChunk)
     p.hist[((size_t)bh * p.nbins + i) * p.nchunks + chunk] = sh[i];
 }
 
@@ -176,105 +295,94 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortPass p) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_sort_scatter(SortPass p) {
+// Stable scatter of one 256-token chunk; wave w owns tokens 64w .. 64w+63.
+__global__ __launch_bounds__(kSortChunk) void k_sort_scatter(SortPass p, RowCopy rc) {
   extern __shared__ int cnt[];  // [4][nbins]
   const int bh = blockIdx.x / p.nchunks;
   const int chunk = blockIdx.x % p.nchunks;
   const size_t base = (size_t)bh * p.T;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c0 = chunk * kSortChunk, c1 = min(p.T, c0 + kSortChunk);
-  constexpr int kPerWave = kSortChunk / 4;
-  const int w0 = c0 + w * kPerWave, w1 = min(c1, w0 + kPerWave);
+  const int pos = chunk * kSortChunk + threadIdx.x;
+  const bool valid = pos < p.T;
+  int idx = 0, src = 0, digit = 0;
+  if (valid) item_at(p, base, pos, idx, src, digit);
 
-  for (int i = threadIdx.x; i < 4 * p.nbins; i += 256) cnt[i] = 0;
-  __syncthreads();
-  for (int pos = w0 + lane; pos < w1; pos += 64) {
-    int idx, src, digit;
-    item_at(p, base, pos, idx, src, digit);
-    atomicAdd(&cnt[w * p.nbins + digit], 1);
+  for (int i = threadIdx.x; i < 4 * p.nbins; i += kSortChunk) cnt[i] = 0;
+  unsigned long long peers = __ballot(valid);
+  for (int b = 0; b < p.nbits; ++b) {
+    const bool bit = (digit >> b) & 1;
+    const unsigned long long m = __ballot(bit);
+    peers &= bit ? m : ~m;
   }
+  const int rank = __popcll(peers & ((1ull << lane) - 1ull));
   __syncthreads();
-  for (int dgt = threadIdx.x; dgt < p.nbins; dgt += 256) {
-    int run = p.hist[((size_t)bh * p.nbins + dgt) * p.nchunks + chunk];
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const int tmp = cnt[ww * p.nbins + dgt];
-      cnt[ww * p.nbins + dgt] = run;
-      run += tmp;
-    }
+  if (valid && rank == 0) cnt[w * p.nbins + digit] = __popcll(peers);
+  __syncthreads();
+  int slot = 0;
+  if (valid) {
+    slot = p.hist[((size_t)bh * p.nbins + digit) * p.nchunks + chunk] + rank;
+    for (int ww = 0; ww < w; ++ww) slot += cnt[ww * p.nbins + digit];
+    p.out_idx[base + slot] = idx;
+    p.out_src[base + slot] = src;
+    if (p.bucket_pass) p.out_hash[base + slot] = digit;
   }
-  __syncthreads();
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int r0 = w0; r0 < w1; r0 += 64) {
-    const int pos = r0 + lane;
-    const bool valid = pos < w1;
-    int idx = 0, src = 0, digit = 0;
-    if (valid) item_at(p, base, pos, idx, src, digit);
-    unsigned long long peers = __ballot(valid);
-    for (int b = 0; b < p.nbits; ++b) {
-      const bool bit = (digit >> b) & 1;
-      const unsigned long long m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
-    const int rank = __popcll(peers & lt);
-    const bool leader = valid && rank == 0;
-    int slot = 0;
-    if (valid) slot = cnt[w * p.nbins + digit];
-    if (leader) cnt[w * p.nbins + digit] = slot + __popcll(peers);
-    if (valid) {
-      const size_t o = base + slot + rank;
-      p.out_idx[o] = idx;
-      p.out_src[o] = src;
-      if (p.bucket_pass) p.out_hash[o] = digit;
+  if (rc.xs || rc.cs) {
+    // cooperative row copy: `per_it` tokens per iteration, `pieces` lanes each
+    const int per_it = 64 / rc.pieces;
+    for (int it = 0; it < rc.pieces; ++it) {
+      const int tok = it * per_it + lane / rc.pieces;
+      const int piece = lane % rc.pieces;
+      const int s_src = __shfl(src, tok, 64);
+      const int s_slot = __shfl(slot, tok, 64);
+      const int s_valid = __shfl((int)valid, tok, 64);
+      if (s_valid) {
+        if (rc.xs) rc.xs[(base + s_slot) * rc.pieces + piece] = rc.x[(base + s_src) * rc.pieces + piece];
+        if (rc.cs) rc.cs[(base + s_slot) * rc.pieces + piece] = rc.cmp[(base + s_src) * rc.pieces + piece];
+      }
     }
   }
 }
 
-// x_sorted[s] = x[perm[s]] (and the companion tensor), 16-byte pieces.
-__global__ __launch_bounds__(256) void k_gather_rows(const int32_t *perm, const uint4 *x, uint4 *xs, const uint4 *cmp,
-                                                     uint4 *cs, int T, int cpr, int rows_per_block) {
-  const int nblk = (T + rows_per_block - 1) / rows_per_block;
-  const int bh = blockIdx.x / nblk;
-  const int r0 = (blockIdx.x % nblk) * rows_per_block;
-  const size_t base = (size_t)bh * T;
-  for (int i = threadIdx.x; i < rows_per_block * cpr; i += 256) {
-    const int r = r0 + i / cpr, c = i % cpr;
-    if (r >= T) break;
-    const int src = perm[base + r];
-    if (xs) xs[(base + r) * cpr + c] = x[(base + src) * cpr + c];
-    if (cs) cs[(base + r) * cpr + c] = cmp[(base + src) * cpr + c];
-  }
-}
-
-static hipError_t run_pass(const SortPass &p, int BH, hipStream_t s) {
+static hipError_t run_pass(const SortPass &p, const RowCopy &rc, int BH, bool with_hist, hipStream_t s) {
   const unsigned grid = (unsigned)(BH * p.nchunks);
-  hipLaunchKernelGGL(k_sort_hist, dim3(grid), dim3(256), p.nbins * sizeof(int), s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (with_hist) {
+    hipLaunchKernelGGL(k_sort_hist, dim3(grid), dim3(kSortChunk), p.nbins * sizeof(int), s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)BH), dim3(1024), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sort_scatter, dim3(grid), dim3(256), 4 * p.nbins * sizeof(int), s, p);
+  hipLaunchKernelGGL(k_sort_scatter, dim3(grid), dim3(kSortChunk), 4 * p.nbins * sizeof(int), s, p, rc);
   return hipGetLastError();
 }
 
 hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0 || a.T == 0) return hipSuccess;
-  const unsigned hgrid = (unsigned)(BH * ((a.T + kHashThreads - 1) / kHashThreads));
-  if (a.d == 64) launch_hash<64>(a, hgrid, s);
-  else launch_hash<128>(a, hgrid, s);
+  const int nchunks = sort_chunks(a.T);
+  const bool idx_passes = a.idx != nullptr && !a.idx_ascending;
+  const unsigned hgrid = (unsigned)(BH * nchunks);
+  int32_t *fused_hist = idx_passes ? nullptr : a.hist;
+  const int nr = a.H * a.d * lsh_r64_cols(a.nb);
+  hipLaunchKernelGGL(k_r_to_f64, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, a.R, a.R64, a.nb / 2,
+                     lsh_col_group(a.nb), a.d, nr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.d == 64) launch_hash<64>(a, a.R64, fused_hist, nchunks, hgrid, s);
+  else launch_hash<128>(a, a.R64, fused_hist, nchunks, hgrid, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
 
-  const bool idx_passes = a.idx != nullptr && !a.idx_ascending;
   SortPass p{};
   p.hash = a.hash;
   p.hist = a.hist;
   p.T = a.T;
-  p.nchunks = sort_chunks(a.T);
+  p.nchunks = nchunks;
   p.in_idx = a.idx;
   p.in_src = nullptr;
+  const RowCopy none{nullptr, nullptr, nullptr, nullptr, 8};
   int buf = 0;
   if (idx_passes) {
     for (int shift = 0; shift < 32; shift += 8) {
@@ -285,7 +393,7 @@ hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
       p.out_idx = a.tmp_idx[buf];
       p.out_src = a.tmp_src[buf];
       p.out_hash = nullptr;
-      e = run_pass(p, BH, s);
+      e = run_pass(p, none, BH, true, s);
       if (e != hipSuccess) return e;
       p.in_idx = a.tmp_idx[buf];
       p.in_src = a.tmp_src[buf];
@@ -300,20 +408,10 @@ hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
   p.out_idx = a.idx_sorted;
   p.out_src = a.perm;
   p.out_hash = a.hash_sorted;
-  e = run_pass(p, BH, s);
-  if (e != hipSuccess) return e;
-
-  if (a.x_sorted || a.companion_sorted) {
-    const int esz = a.dtype == 1 ? 4 : 2;
-    const int cpr = a.d * esz / 16;
-    const int rows_per_block = 2048 / cpr;
-    const unsigned grid = (unsigned)(BH * ((a.T + rows_per_block - 1) / rows_per_block));
-    hipLaunchKernelGGL(k_gather_rows, dim3(grid), dim3(256), 0, s, a.perm, static_cast<const uint4 *>(a.x),
-                       static_cast<uint4 *>(a.x_sorted), static_cast<const uint4 *>(a.companion),
-                       static_cast<uint4 *>(a.companion_sorted), a.T, cpr, rows_per_block);
-    e = hipGetLastError();
-  }
-  return e;
+  RowCopy rc{static_cast<const uint4 *>(a.x), static_cast<uint4 *>(a.x_sorted),
+             static_cast<const uint4 *>(a.companion), static_cast<uint4 *>(a.companion_sorted),
+             a.d * (a.dtype == 1 ? 4 : 2) / 16};
+  return run_pass(p, rc, BH, idx_passes, s);
 }
 
 }  // namespace scfa

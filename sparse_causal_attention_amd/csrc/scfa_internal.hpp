@@ -53,6 +53,7 @@ struct LshArgs {
   int32_t *hist;            // [BH, nbins, nchunks]
   int32_t *tmp_idx[2];      // [BH, T] ping-pong (radix passes over idx)
   int32_t *tmp_src[2];
+  double *R64;              // [H, lsh_r64_cols(nb) / lsh_col_group(nb), d, lsh_col_group(nb)] float64 R
 };
 
 hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s);
@@ -66,8 +67,15 @@ hipError_t launch_attn_bwd_f32(const AttnArgs &a, int mode, int part, hipStream_
 hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s);
 
 // Sizes shared by the API's workspace carving and the sort launcher.
-constexpr int kSortChunk = 4096;  // tokens per counting-sort work group
+constexpr int kSortChunk = 256;  // tokens per counting-sort work group (one per thread)
 inline int sort_bins(int nb, bool idx_passes) { return idx_passes ? (nb > 256 ? nb : 256) : nb; }
 inline int sort_chunks(int T) { return (T + kSortChunk - 1) / kSortChunk; }
+// LSH projection: columns per register group, and the float64 copy of R's
+// row length (nb/2 padded with zeros to a whole number of groups).
+inline int lsh_col_group(int nb) { return nb / 2 <= 8 ? 8 : nb / 2 <= 16 ? 16 : 32; }
+inline int lsh_r64_cols(int nb) {
+  const int g = lsh_col_group(nb);
+  return (nb / 2 + g - 1) / g * g;
+}
 
 }  // namespace scfa
