@@ -15,11 +15,20 @@ at the original shape and the speedup over it, per-kernel HIP-event times, the
 roofline of the dominant kernel, and the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-dense] [--copy-calibration MIB]
+
+HBM traffic of the dominant kernel ("roofline.traffic") comes from rocprofv3
+FETCH_SIZE / WRITE_SIZE counter runs summarised under profiles/, scaled by
+what the same counters read for a plain device copy of known size
+(--copy-calibration makes this process run one, before the warmup).  The
+summary records a digest of the kernel's sources and build flags; once they
+change, traffic is reported as null until the counters are taken again.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +42,35 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
 PEAK_FP64_TFLOPS = 78.6  # MI355X fp64 vector (published)
 WORKLOAD_ID = 4
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_bwd_dkdv_hash_train_T16384_traffic.txt")
+# files that determine the code of the attention kernels
+KERNEL_SOURCES = ["attn_bwd.hip", "attn_fwd.hip", "scfa_pipe.hpp", "scfa_device.hpp", "scfa_internal.hpp",
+                  "../build.py"]
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "sparse_causal_attention_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.normpath(os.path.join(base, name)), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _log(msg):
@@ -186,6 +224,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of MIB MiB (fp32) before the warmup, for counter scaling")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path has no multi-GPU code); got --gpus {args.gpus}",
@@ -202,24 +242,31 @@ def main():
     q, k, v, do, R = make_inputs(w, torch)
     torch.cuda.synchronize()
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        _log(f"[bench] calibration copy: {args.copy_calibration} MiB read + {args.copy_calibration} MiB written")
+        del src, dst
+
     _log("[bench] warmup")
     for _ in range(args.warmup):
         run_step(scfa, w, q, k, v, do, R)
     torch.cuda.synchronize()
 
+    # HIP events between the calls, on the stream the kernels run on, inside the timed region
     _log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        meta, _ = run_step(scfa, w, q, k, v, do, R)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-
-    # per-call HIP-event times (separate pass so the events do not sit in the wall-clock region)
     timer = Timer(torch, STEP_CALLS)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for _ in range(args.steps):
         meta, _ = run_step(scfa, w, q, k, v, do, R, timer)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
     timer.collect()
 
     units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
@@ -258,8 +305,9 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic() if dominant == "bwd_dkdv" else None,
         "avg_launch_ms": per_call[dominant],
+        "algorithmic_flops_per_launch": kernel_flops[dominant],
     }
 
     cpu = None

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
 // bf16 dK / dV kernel.  Lanes own key columns.
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
-__global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dkdv_bf16(AttnArgs a) {
+__global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_bwd_dkdv_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) QGBuf<D> sb[2];
 
