@@ -16,6 +16,12 @@ roofline of the dominant kernel, and the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-dense] [--copy-calibration MIB]
+       python bench.py --sweep-nb 2,4,8,16,32,64,128 [--steps K] [--warmup W]
+
+--sweep-nb runs the same step at the same shape for each bucket count and
+prints one JSON line per count (executed tiles, step time, effective TFLOP/s,
+speedup over the dense-causal path with and without the LSH + sort), then the
+dense-causal reference line; it is a measurement mode, not the benchmark line.
 
 HBM traffic of the dominant kernel ("roofline.traffic") comes from rocprofv3
 FETCH_SIZE / WRITE_SIZE counter runs summarised under profiles/, scaled by
@@ -217,6 +223,48 @@ def cpu_baseline(w, tile_units_per_head):
     }
 
 
+def _time_steps(torch, fn, steps, warmup, timer=None):
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = None
+    for _ in range(steps):
+        out = fn(timer)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3, out
+
+
+def sweep_buckets(scfa, torch, w, q, k, v, do, nbs, args):
+    """Same shape and inputs, LSH rotations drawn per bucket count (seeded by the workload)."""
+    import dataclasses
+
+    import numpy as np
+
+    from gen import lsh_rotation
+
+    dense_ms, _ = _time_steps(torch, lambda t: run_dense(scfa, w, q, k, v, do, t), max(3, args.steps // 2),
+                              max(1, args.warmup))
+    for nb in nbs:
+        wn = dataclasses.replace(w, n_buckets=nb, name=f"{w.name.rsplit('_nb', 1)[0]}_nb{nb}")
+        R = torch.from_numpy(np.stack([lsh_rotation(wn, h) for h in range(w.H)])).to("cuda:0")
+        timer = Timer(torch, STEP_CALLS)
+        ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t), args.steps,
+                                    args.warmup, timer)
+        timer.collect()
+        units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
+        per_call = {n: round(timer.mean_ms(n), 4) for n in STEP_CALLS}
+        attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
+        nq = (w.T + w.block - 1) // w.block
+        print(json.dumps({
+            "sweep": "n_buckets", "workload": wn.name, "n_buckets": nb, "executed_tiles": tiles,
+            "mean_live_kblocks_per_qblock": round(tiles / (w.B * w.H * nq), 2),
+            "ms_per_step": round(ms, 4), "tflops": round(14.0 * units * w.d / (ms * 1e-3) / 1e12, 2),
+            "dense_causal_ms": round(dense_ms, 4), "speedup_vs_dense_causal": round(dense_ms / ms, 3),
+            "speedup_vs_dense_causal_excl_lsh": round(dense_ms / attn_ms, 3), "per_call_ms": per_call,
+        }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +272,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
+    ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
+                    help="comma-separated bucket counts: one JSON line per count instead of the benchmark line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB (fp32) before the warmup, for counter scaling")
     args = ap.parse_args()
@@ -241,6 +291,9 @@ def main():
     _log(f"[bench] workload {w.name}: generating inputs")
     q, k, v, do, R = make_inputs(w, torch)
     torch.cuda.synchronize()
+    if args.sweep_nb:
+        sweep_buckets(scfa, torch, w, q, k, v, do, [int(x) for x in args.sweep_nb.split(",")], args)
+        return
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4

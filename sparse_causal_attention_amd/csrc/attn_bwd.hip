@@ -142,7 +142,7 @@ struct QGBuf {
 // bf16 dQ (+ D, lse*log2 e) kernel.  Lanes own query columns.
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
-__global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
+__global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_bwd_dq_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) KVBufB<D> sb[2];
 
@@ -221,17 +221,35 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
     if (have_next) issue(sb[buf ^ 1], nxt);
     const KVBufB<D> &b = sb[buf];
 
+    // Fragments first, then four independent accumulator chains (S^T and
+    // dP^T of both 32-key halves) interleaved with the k-step outermost.
+    bf16x8 kfr[2][D / 16], vfr[2][D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        kfr[sub][kk] = frag_rows<D>(b.k, lo, sub, kk);
+        vfr[sub][kk] = frag_rows<D>(b.v, lo, sub, kk);
+      }
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, 0), qf[0], kZero16);
-      dp[sub] = mfma32(frag_rows<D>(b.v, lo, sub, 0), dof[0], kZero16);
-#pragma unroll
-      for (int kk = 1; kk < D / 16; ++kk) {
-        s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, kk), qf[kk], s[sub]);
-        dp[sub] = mfma32(frag_rows<D>(b.v, lo, sub, kk), dof[kk], dp[sub]);
-      }
+      s[sub] = mfma32(kfr[sub][0], qf[0], kZero16);
+      dp[sub] = mfma32(vfr[sub][0], dof[0], kZero16);
     }
+#pragma unroll
+    for (int kk = 1; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = mfma32(kfr[sub][kk], qf[kk], s[sub]);
+        dp[sub] = mfma32(vfr[sub][kk], dof[kk], dp[sub]);
+      }
+    // K^T fragments of the dQ product, requested before the exponent work
+    bf16x8 ktr[4][D / 32];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) ktr[t][mt] = frag_trans<D>(b.k, lo, mt, t);
     // P = exp(scale*S - lse); rows with no admissible key (lse = -inf) only
     // occur in masked tiles, where the select below discards them.
 #pragma unroll
@@ -252,7 +270,7 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_bwd_dq_bf16(AttnArgs a) {
       for (int t2 = 0; t2 < 2; ++t2) {
         const bf16x8 db = as_bf16x8(c_regs_to_u4(s[sub], t2));
 #pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) dqa[mt] = mfma32(frag_trans<D>(b.k, lo, mt, 2 * sub + t2), db, dqa[mt]);
+        for (int mt = 0; mt < D / 32; ++mt) dqa[mt] = mfma32(ktr[2 * sub + t2][mt], db, dqa[mt]);
       }
     buf ^= 1;
     cur = nxt;
@@ -346,56 +364,67 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     const QGBuf<D> &b = sb[buf];
     // Key rows past Tk only pollute their own (never stored) columns, so a
     // mask-free tile needs masking only for query rows past Tq.
-
-    f32x16 s[2], dp[2];
+    // The chunk is processed as two halves of 32 query rows; each half is
+    // S, dP (4 independent chains) -> P, dS -> dV^T, dK^T, so the second
+    // half's products can overlap the first half's exponent and mask work.
+    const bool tail = cur.nvalid < kChunk, masked = tail || !cur.free;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = mfma32(frag_rows<D>(b.q, lo, sub, 0), kf[0], kZero16);
-      dp[sub] = mfma32(frag_rows<D>(b.g, lo, sub, 0), vf[0], kZero16);
+      bf16x8 qfr[D / 16], gfr[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        qfr[kk] = frag_rows<D>(b.q, lo, sub, kk);
+        gfr[kk] = frag_rows<D>(b.g, lo, sub, kk);
+      }
+      f32x16 s1[1], dp1[1];
+      s1[0] = mfma32(qfr[0], kf[0], kZero16);
+      dp1[0] = mfma32(gfr[0], vf[0], kZero16);
 #pragma unroll
       for (int kk = 1; kk < D / 16; ++kk) {
-        s[sub] = mfma32(frag_rows<D>(b.q, lo, sub, kk), kf[kk], s[sub]);
-        dp[sub] = mfma32(frag_rows<D>(b.g, lo, sub, kk), vf[kk], dp[sub]);
+        s1[0] = mfma32(qfr[kk], kf[kk], s1[0]);
+        dp1[0] = mfma32(gfr[kk], vf[kk], dp1[0]);
       }
-    }
-    // P = exp(scale*S - lse) per query row (lse * log2 e staged in LDS).
+      bf16x8 gtr[2][D / 32], qtr[2][D / 32];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+          gtr[t2][mt] = frag_trans<D>(b.g, lo, mt, 2 * sub + t2);
+          qtr[t2][mt] = frag_trans<D>(b.q, lo, mt, 2 * sub + t2);
+        }
+      // P = exp(scale*S - lse) per query row (lse * log2 e staged in LDS).
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 l4 = *reinterpret_cast<const float4 *>(b.lse2 + 32 * sub + 8 * g + 4 * half);
-        s[sub][4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 0], c, -l4.x));
-        s[sub][4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 1], c, -l4.y));
-        s[sub][4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 2], c, -l4.z));
-        s[sub][4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(s[sub][4 * g + 3], c, -l4.w));
+        s1[0][4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(s1[0][4 * g + 0], c, -l4.x));
+        s1[0][4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(s1[0][4 * g + 1], c, -l4.y));
+        s1[0][4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(s1[0][4 * g + 2], c, -l4.z));
+        s1[0][4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(s1[0][4 * g + 3], c, -l4.w));
       }
-    if (cur.nvalid < kChunk)
-      mask_rows<MODE, true, false>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
-    else if (!cur.free)
-      mask_rows<MODE, false, false>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
-    // dS = P * (dP - D)
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+      if (tail)
+        mask_half<MODE, true>(s1[0], b.idx, b.hash, 32 * sub, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+      else if (masked)
+        mask_half<MODE, false>(s1[0], b.idx, b.hash, 32 * sub, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+      // dS = P * (dP - D)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 d4 = *reinterpret_cast<const float4 *>(b.del + 32 * sub + 8 * g + 4 * half);
-        dp[sub][4 * g + 0] = s[sub][4 * g + 0] * (dp[sub][4 * g + 0] - d4.x);
-        dp[sub][4 * g + 1] = s[sub][4 * g + 1] * (dp[sub][4 * g + 1] - d4.y);
-        dp[sub][4 * g + 2] = s[sub][4 * g + 2] * (dp[sub][4 * g + 2] - d4.z);
-        dp[sub][4 * g + 3] = s[sub][4 * g + 3] * (dp[sub][4 * g + 3] - d4.w);
+        dp1[0][4 * g + 0] = s1[0][4 * g + 0] * (dp1[0][4 * g + 0] - d4.x);
+        dp1[0][4 * g + 1] = s1[0][4 * g + 1] * (dp1[0][4 * g + 1] - d4.y);
+        dp1[0][4 * g + 2] = s1[0][4 * g + 2] * (dp1[0][4 * g + 2] - d4.z);
+        dp1[0][4 * g + 3] = s1[0][4 * g + 3] * (dp1[0][4 * g + 3] - d4.w);
       }
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8 pb = as_bf16x8(c_regs_to_u4(s[sub], t2));
-        const bf16x8 db = as_bf16x8(c_regs_to_u4(dp[sub], t2));
+        const bf16x8 pb = as_bf16x8(c_regs_to_u4(s1[0], t2));
+        const bf16x8 db = as_bf16x8(c_regs_to_u4(dp1[0], t2));
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-          dva[mt] = mfma32(frag_trans<D>(b.g, lo, mt, 2 * sub + t2), pb, dva[mt]);
-          dka[mt] = mfma32(frag_trans<D>(b.q, lo, mt, 2 * sub + t2), db, dka[mt]);
+          dva[mt] = mfma32(gtr[t2][mt], pb, dva[mt]);
+          dka[mt] = mfma32(qtr[t2][mt], db, dka[mt]);
         }
       }
+    }
     buf ^= 1;
     cur = nxt;
     have = have_next;

@@ -162,13 +162,27 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
     if (have_next) issue_kv<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, dof);
     const KVBuf<D> &b = sb[buf];
 
+    // All K fragments of the chunk are requested first, then the two
+    // independent S^T accumulator chains run interleaved (k-step outer).
+    bf16x8 kfr[2][D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) kfr[sub][kk] = frag_rows<D>(b.k, lo, sub, kk);
     f32x16 s[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, 0), qf[0], kZero16);
+    for (int sub = 0; sub < 2; ++sub) s[sub] = mfma32(kfr[sub][0], qf[0], kZero16);
 #pragma unroll
-      for (int kk = 1; kk < D / 16; ++kk) s[sub] = mfma32(frag_rows<D>(b.k, lo, sub, kk), qf[kk], s[sub]);
-    }
+    for (int kk = 1; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) s[sub] = mfma32(kfr[sub][kk], qf[kk], s[sub]);
+    // V^T fragments do not depend on the softmax: request them now so their
+    // latency overlaps the mask / max / exp work below.
+    bf16x8 vfr[4][D / 32];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) vfr[t][mt] = frag_trans<D>(b.v, lo, mt, t);
     if (cur.kvalid < kChunk)
       mask_rows<MODE, true, true>(s, b.idx, b.hash, cur.k0, cur.kvalid, my_idx, my_hash, half, -INFINITY);
     else if (!cur.free)
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
         l = add_bf16x8(pk, l);
         const bf16x8 pb = as_bf16x8(pk);
 #pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma32(frag_trans<D>(b.v, lo, mt, 2 * sub + t2), pb, acc[mt]);
+        for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma32(vfr[2 * sub + t2][mt], pb, acc[mt]);
       }
     buf ^= 1;
     cur = nxt;
