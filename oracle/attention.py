@@ -223,3 +223,45 @@ def backward_key_rows(
         dv += p[:, key_rows].T @ do[rr]
         dk += scale * (ds[:, key_rows].T @ q[rr])
     return dk, dv
+
+
+def zero_query_forward(
+    q_idx: np.ndarray,
+    k_idx: np.ndarray,
+    v: np.ndarray,
+    q_hash: Optional[np.ndarray] = None,
+    k_hash: Optional[np.ndarray] = None,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """O and lse of every query row when Q = 0, without a Tq x Tk matrix.
+
+    With Q = 0 every admissible score is 0, so softmax is uniform over the
+    admissible keys of row i: lse_i = ln N_i and O_i is the mean of their V
+    rows (N_i = 0: O_i = 0, lse_i = -inf, as in ``forward``).  N_i and the V
+    sums come from the keys of row i's bucket ordered by position, with
+    prefix sums, so the cost is O((Tq + Tk) log Tk) and every row of a
+    million-token head can be checked.
+    """
+    q_idx = np.asarray(q_idx, dtype=np.int64)
+    k_idx = np.asarray(k_idx, dtype=np.int64)
+    v = np.asarray(v, dtype=np.float64)
+    if q_hash is None:
+        q_hash = np.zeros_like(q_idx)
+        k_hash = np.zeros_like(k_idx)
+    q_hash = np.asarray(q_hash, dtype=np.int64)
+    k_hash = np.asarray(k_hash, dtype=np.int64)
+    o = np.zeros((q_idx.size, v.shape[1]))
+    lse = np.full(q_idx.size, -np.inf)
+    for h in np.unique(q_hash):
+        qs = np.nonzero(q_hash == h)[0]
+        ks = np.nonzero(k_hash == h)[0]
+        if ks.size == 0:
+            continue
+        order = ks[np.argsort(k_idx[ks], kind="stable")]
+        pos = k_idx[order]
+        prefix = np.vstack([np.zeros((1, v.shape[1])), np.cumsum(v[order], axis=0)])
+        n = np.searchsorted(pos, q_idx[qs], side="right")  # admissible keys: position <= query's
+        some = n > 0
+        rows = qs[some]
+        o[rows] = prefix[n[some]] / n[some][:, None]
+        lse[rows] = np.log(n[some])
+    return o, lse

@@ -82,6 +82,7 @@ def test_workload3_qk_train_bf16():
             check_forward(o[b, h][rows], lse[b, h][rows], o_ref, lse_ref, "bf16", f"{w.name} rows b{b}h{h}")
             dq_ref = A.backward_rows(rows, Q[b, h], K[b, h], V[b, h], dO[b, h], qp[b, h], kp[b, h], scale=w.scale)
             assert rel_fro(dq[b, h][rows], dq_ref) <= 5e-2
+    _zero_query_all_rows(w, {(b, h): (qp[b, h], kp[b, h], None, None) for b in range(w.B) for h in range(w.H)})
 
 
 def _hash_pipeline(w, Q, K, V, dO, qp, kp):
@@ -114,6 +115,54 @@ def _check_sort(R, srt, X, pos, b, h, which):
     return p_ref, h_ref, i_ref
 
 
+def _zero_query_all_rows(w, heads):
+    """Closed form at full size: Q = 0 makes P uniform over the admissible keys.
+
+    ``heads`` maps (b, h) to the oracle's (q_idx, k_idx, q_hash, k_hash); the
+    bucket ids are None in QK-sparse mode.
+    K is 0 as well (scores are 0 whatever K is) and V holds binary features
+    of each key's position and bucket, exact in bf16, so O_i is the mean of
+    the admissible keys' features: every row of every head is compared with
+    the oracle's O(T log T) evaluation, within bf16 rounding of a value in
+    [0, 1] (2^-9) for O and float32 log for lse.
+    """
+    scfa = _scfa()
+    B, H, Tq, Tk, d = w.B, w.H, w.Tq, w.Tk, w.d
+    bits = np.arange(d)
+
+    hashed = w.mode != "qk"
+
+    def feats(ki, kh):
+        kh = ki * 7 if kh is None else kh
+        f = np.where(bits < d // 2, (ki[:, None] >> (bits % 20)) & 1, (kh[:, None] >> (bits % 8)) & 1)
+        return f.astype(np.float32)
+
+    stack = lambda i: np.stack([np.stack([heads[(b, h)][i] for h in range(H)]) for b in range(B)])  # noqa: E731
+    iq, ik = (dev(stack(i).astype(np.int32)) for i in range(2))
+    hq, hk = (dev(stack(i).astype(np.int32)) for i in (2, 3)) if hashed else (None, None)
+    v = torch.empty((B, H, Tk, d), dtype=torch.bfloat16, device="cuda:0")
+    for (b, h), (_, ki, _, kh) in heads.items():
+        v[b, h] = torch.from_numpy(feats(ki, kh)).to(torch.bfloat16)
+    zq = torch.zeros((B, H, Tq, d), dtype=torch.bfloat16, device="cuda:0")
+    zk = torch.zeros((B, H, Tk, d), dtype=torch.bfloat16, device="cuda:0")
+    note(f"[workload] {w.name}: Q = 0 closed form on all {B * H * Tq} rows")
+    if hashed:
+        o, lse = scfa.hash_sparse_fwd(zq, zk, v, iq, ik, hq, hk, block=w.block, scale=w.scale)
+    else:
+        o, lse = scfa.qk_sparse_fwd(zq, zk, v, iq, ik, block=w.block, scale=w.scale)
+    torch.cuda.synchronize()
+    del zq, zk, v
+    for (b, h), (qi, ki, qh, kh) in heads.items():
+        o_ref, lse_ref = A.zero_query_forward(qi, ki, feats(ki, kh).astype(np.float64), qh, kh)
+        og = o[b, h].float().cpu().numpy()
+        lg = lse[b, h].cpu().numpy()
+        empty = np.isneginf(lse_ref)
+        assert np.array_equal(np.isneginf(lg), empty), f"b{b}h{h}: empty rows differ"
+        assert np.all(og[empty] == 0)
+        np.testing.assert_allclose(og, o_ref, rtol=0, atol=2.0 ** -9 + 1e-6, err_msg=f"O b{b}h{h}")
+        np.testing.assert_allclose(lg[~empty], lse_ref[~empty], rtol=0, atol=1e-5, err_msg=f"lse b{b}h{h}")
+
+
 @pytest.mark.parametrize("wid", [2, 4])
 def test_hash_workloads(wid):
     w = WORKLOADS[wid]
@@ -124,10 +173,12 @@ def test_hash_workloads(wid):
     g = [to_np(t) for t in grads] if grads is not None else None
     rng = np.random.default_rng(wid)
     full_heads = {(0, 0), (w.B - 1, w.H - 1)} if wid == 4 else {(0, h) for h in range(w.H)}
+    sorted_heads = {}
     for b in range(w.B):
         for h in range(w.H):
             pq, hq, iq = _check_sort(R, srt, Q, qp, b, h, "q")
             pk, hk, ik = _check_sort(R, srt, K, kp, b, h, "k")
+            sorted_heads[(b, h)] = (iq, ik, hq, hk)
             qs, ks, vs = Q[b, h][pq], K[b, h][pk], V[b, h][pk]
             if (b, h) in full_heads:
                 o_ref, lse_ref = A.forward(qs, ks, vs, iq, ik, hq, hk, w.scale)
@@ -146,6 +197,8 @@ def test_hash_workloads(wid):
                     dk_ref, dv_ref = A.backward_key_rows(keys, qs, ks, vs, dO[b, h][pq], iq, ik, hq, hk, w.scale)
                     assert rel_fro(g[1][b, h][keys], dk_ref) <= 5e-2
                     assert rel_fro(g[2][b, h][keys], dv_ref) <= 5e-2
+    del o, lse, g, srt
+    _zero_query_all_rows(w, sorted_heads)
 
 
 def test_workload5_million_token_hash_drop():
@@ -155,9 +208,13 @@ def test_workload5_million_token_hash_drop():
     R, srt, o, lse, _ = _hash_pipeline(w, Q, K, V, None, qp, kp)
     o, lse = to_np(o), to_np(lse)
     rng = np.random.default_rng(5)
+    sorted_heads = {}
     for h in range(w.H):
         pq, hq, iq = _check_sort(R, srt, Q, qp, 0, h, "q")
         pk, hk, ik = _check_sort(R, srt, K, kp, 0, h, "k")
+        sorted_heads[(0, h)] = (iq, ik, hq, hk)
         rows = _rows_sample(rng, w.Tq, 64)
         o_ref, lse_ref = A.forward_rows(rows, Q[0, h][pq], K[0, h][pk], V[0, h][pk], iq, ik, hq, hk, w.scale)
         check_forward(o[0, h][rows], lse[0, h][rows], o_ref, lse_ref, "bf16", f"{w.name} rows h{h}")
+    del Q, K, V, o, lse, srt
+    _zero_query_all_rows(w, sorted_heads)

@@ -125,6 +125,37 @@ def test_zero_queries_closed_form():
         np.testing.assert_allclose(o[i], v[adm].mean(axis=0), atol=1e-14)
 
 
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_zero_query_closed_form_all_rows(shuffle):
+    """The O(T log T) Q = 0 evaluator equals the dense oracle and a brute-force loop."""
+    rng = np.random.default_rng(11)
+    Tq, Tk = 150, 170
+    qi = np.sort(rng.choice(400, Tq, replace=False))
+    ki = np.sort(rng.choice(400, Tk, replace=False))
+    qh = rng.integers(0, 5, Tq)
+    kh = rng.integers(0, 5, Tk)
+    if shuffle:
+        pq, pk = rng.permutation(Tq), rng.permutation(Tk)
+        qi, qh, ki, kh = qi[pq], qh[pq], ki[pk], kh[pk]
+    v = rng.integers(0, 2, (Tk, 4)).astype(np.float64)
+    o, lse = A.zero_query_forward(qi, ki, v, qh, kh)
+    o_ref, lse_ref = A.forward(np.zeros((Tq, 8)), rng.standard_normal((Tk, 8)), v, qi, ki, qh, kh)
+    np.testing.assert_allclose(o, o_ref, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-13)
+    for i in range(0, Tq, 7):
+        adm = [j for j in range(Tk) if ki[j] <= qi[i] and kh[j] == qh[i]]
+        if not adm:
+            assert np.isneginf(lse[i]) and np.all(o[i] == 0)
+        else:
+            assert lse[i] == pytest.approx(np.log(len(adm)), abs=1e-13)
+            np.testing.assert_allclose(o[i], v[adm].mean(axis=0), atol=1e-14)
+    # QK mode (no buckets)
+    o2, lse2 = A.zero_query_forward(qi, ki, v)
+    o2_ref, lse2_ref = A.forward(np.zeros((Tq, 8)), rng.standard_normal((Tk, 8)), v, qi, ki)
+    np.testing.assert_allclose(o2, o2_ref, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse2_ref, atol=1e-13)
+
+
 def test_rows_of_p_sum_to_one():
     rng = np.random.default_rng(9)
     Tq, Tk, d = 90, 120, 8
