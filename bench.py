@@ -17,6 +17,11 @@ roofline of the dominant kernel, and the CPU oracle on a bounded sample.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-dense] [--copy-calibration MIB]
        python bench.py --sweep-nb 2,4,8,16,32,64,128 [--steps K] [--warmup W]
+       python bench.py --measure-rows [--steps K] [--warmup W]
+
+--measure-rows times the row gather / scatter calls around the path at the
+same shape (un-sorting O, dQ, dK, dV of the step; compacting Q, K, V to a
+70% kept set) and prints one JSON line with their HBM throughput.
 
 --sweep-nb runs the same step at the same shape for each bucket count and
 prints one JSON line per count (executed tiles, step time, effective TFLOP/s,
@@ -235,6 +240,40 @@ def _time_steps(torch, fn, steps, warmup, timer=None):
     return (time.perf_counter() - t0) / steps * 1e3, out
 
 
+def measure_rows(scfa, torch, w, q, k, v, do, R, args):
+    """HBM throughput of gather_rows / scatter_rows at the step's shape."""
+    import numpy as np
+
+    qh, qi, qperm, qs, dos = scfa.lsh_bucket_sort(q, R, w.n_buckets, companion=do)
+    rows_out = [qs, dos, qs, dos]  # four [B,H,T,d] tensors, as O, dQ, dK, dV
+    perm = qperm
+    n_keep = int(round(0.7 * w.T))
+    rng = np.random.default_rng(0)
+    keep = torch.from_numpy(np.stack([np.stack([np.sort(rng.choice(w.T, n_keep, replace=False)).astype(np.int32)
+                                                for _ in range(w.H)]) for _ in range(w.B)])).to(q.device)
+    row_bytes = w.d * 2
+
+    def unsort(_):
+        for x in rows_out:
+            scfa.scatter_rows(x, perm, w.T, zero_fill=False)
+
+    def compact(_):
+        for x in (q, k, v):
+            scfa.gather_rows(x, keep)
+
+    ms_u, _ = _time_steps(torch, unsort, args.steps, args.warmup)
+    ms_c, _ = _time_steps(torch, compact, args.steps, args.warmup)
+    bytes_u = 4 * (w.B * w.H * w.T) * (2 * row_bytes + 4)  # read row + index, write row
+    bytes_c = 3 * (w.B * w.H * n_keep) * (2 * row_bytes + 4)
+    print(json.dumps({
+        "measure": "row gather / scatter", "workload": w.name,
+        "unsort_4_tensors_ms": round(ms_u, 4), "unsort_GBps": round(bytes_u / (ms_u * 1e-3) / 1e9, 1),
+        "compact_3_tensors_ms": round(ms_c, 4), "compact_GBps": round(bytes_c / (ms_c * 1e-3) / 1e9, 1),
+        "peak_GBps": PEAK_HBM_GBS, "kept_fraction": 0.7,
+        "bytes_per_row": "row read + row written + 4-byte index",
+    }), flush=True)
+
+
 def sweep_buckets(scfa, torch, w, q, k, v, do, nbs, args):
     """Same shape and inputs, LSH rotations drawn per bucket count (seeded by the workload)."""
     import dataclasses
@@ -274,6 +313,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
     ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
                     help="comma-separated bucket counts: one JSON line per count instead of the benchmark line")
+    ap.add_argument("--measure-rows", action="store_true",
+                    help="time the row gather / scatter calls instead of the step (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB (fp32) before the warmup, for counter scaling")
     args = ap.parse_args()
@@ -293,6 +334,9 @@ def main():
     torch.cuda.synchronize()
     if args.sweep_nb:
         sweep_buckets(scfa, torch, w, q, k, v, do, [int(x) for x in args.sweep_nb.split(",")], args)
+        return
+    if args.measure_rows:
+        measure_rows(scfa, torch, w, q, k, v, do, R, args)
         return
 
     if args.copy_calibration > 0:

@@ -81,6 +81,8 @@ extern "C" {
                                              bit-identical to the pruned run (test aid) */
 #define SCFA_FLAG_FORCE_MASK (1u << 1)    /* apply the element mask on mask-free tiles too;
                                              bit-identical results (test aid) */
+#define SCFA_FLAG_ZERO_FILL (1u << 3)     /* scfa_scatter_rows: zero every destination row
+                                             first, so rows no index names read 0 */
 #define SCFA_FLAG_IDX_ASCENDING (1u << 2) /* scfa_lsh_bucket_sort: the caller guarantees idx is
                                              strictly ascending within each (b, h), which lets the
                                              sort run one pass instead of five */
@@ -241,6 +243,32 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
                              void *dk, void *dv,
                              int B, int H, int Tq, int Tk, int d, int block, float scale,
                              int dtype, unsigned flags, void *stream);
+
+/*
+ * Row gather and scatter: the steps either side of the attention path.
+ * Dropping tokens compacts Q/K/V to the kept rows, and Hash-sparse attention
+ * reorders tokens by bucket; every row keeps its original position ("why
+ * dynamic sparsity breaks it"; "1. QK-Sparse": compact tensors plus q_idx /
+ * k_idx).  These two calls build the compact or reordered inputs and put
+ * outputs and gradients back at their original rows.
+ *   scfa_gather_rows:  dst[b,h,i,:] = src[b,h,index[b,h,i],:]  for i < T_dst
+ *     src [B,H,T_src,d], index [B,H,T_dst] int32, dst [B,H,T_dst,d].  An index
+ *     outside [0, T_src) yields a zero row.  Compaction: index = kept
+ *     positions (q_idx / k_idx); reordering: index = the sort's perm.
+ *   scfa_scatter_rows: dst[b,h,index[b,h,i],:] = src[b,h,i,:] for i < T_src
+ *     src [B,H,T_src,d], index [B,H,T_src] int32, dst [B,H,T_dst,d].  Rows
+ *     whose index is outside [0, T_dst) are dropped; when two rows name the
+ *     same destination, which one lands is unspecified.  flags:
+ *     SCFA_FLAG_ZERO_FILL zeroes dst first (un-compaction: dropped rows 0).
+ *     Un-sorting: index = perm, T_dst = T_src; un-compaction: index = q_idx.
+ *   dtype as above (bf16 or fp32); d >= 1 with d * sizeof(dtype) a multiple
+ *   of 16 bytes; src/dst 16-byte aligned, index 4-byte aligned; src and dst
+ *   must not overlap.  Device pointers owned by the caller; no workspace.
+ */
+int scfa_gather_rows(const void *src, const int32_t *index, void *dst,
+                     int B, int H, int T_src, int T_dst, int d, int dtype, void *stream);
+int scfa_scatter_rows(const void *src, const int32_t *index, void *dst,
+                      int B, int H, int T_src, int T_dst, int d, int dtype, unsigned flags, void *stream);
 
 /*
  * Bytes of workspace an operation needs (0 for invalid arguments).  For the

@@ -14,6 +14,8 @@ from the exact values the GPU sees (bf16 inputs widened without rounding):
 * ``blocks``: per-block min/max of positions and bucket ids, the tile liveness
   and mask-free predicates, and the per-row / per-column live-tile lists,
   all by brute force over every block pair.
+* ``rows``: gathering rows into compact / reordered tensors and scattering
+  results back to their original rows.
 * ``lsh``: the random-rotation LSH bucket (first maximum of ``[xR, -xR]``)
   with float64 accumulation in increasing coordinate order, and the stable
   ordering of tokens by (bucket, original position).
@@ -29,4 +31,4 @@ integer-exact cases, closed forms and invariants.  Nothing here is
 "parity unpinned".
 """
 
-from . import attention, blocks, lsh  # noqa: F401
+from . import attention, blocks, lsh, rows  # noqa: F401

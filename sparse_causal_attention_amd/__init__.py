@@ -42,6 +42,8 @@ __all__ = [
     "attn_bwd_dq_lists",
     "attn_bwd_dkdv_lists",
     "workspace_size",
+    "gather_rows",
+    "scatter_rows",
     "ScfaError",
     "FLAG_NO_PRUNE",
     "FLAG_FORCE_MASK",
@@ -278,3 +280,36 @@ def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash,
                                        _stream())
     _lib.check("scfa_attn_bwd_dkdv_lists", rc)
     return dk, dv
+
+
+def gather_rows(src, index):
+    """dst[b, h, i] = src[b, h, index[b, h, i]] (zero rows for out-of-range indices).
+
+    Compaction of kept tokens (index = their positions) or reordering (index =
+    a sort permutation).  src [B,H,T_src,d]; index [B,H,T_dst] int32.
+    """
+    B, H, Ts, d = src.shape
+    _need(src, "src")
+    Td = index.shape[2]
+    _need(index, "index", torch.int32, (B, H, Td))
+    dst = torch.empty((B, H, Td, d), dtype=src.dtype, device=src.device)
+    rc = _LIB.scfa_gather_rows(_ptr(src), _ptr(index), _ptr(dst), B, H, Ts, Td, d, _dtype_code(src), _stream())
+    _lib.check("scfa_gather_rows", rc)
+    return dst
+
+
+def scatter_rows(src, index, T_dst, *, zero_fill=True, out=None):
+    """dst[b, h, index[b, h, i]] = src[b, h, i]; rows no index names are 0 with ``zero_fill``.
+
+    Un-sorting (index = the sort permutation, T_dst = T_src) or un-compaction
+    (index = kept positions, T_dst = original length).  src [B,H,T_src,d].
+    """
+    B, H, Ts, d = src.shape
+    _need(src, "src")
+    _need(index, "index", torch.int32, (B, H, Ts))
+    dst = out if out is not None else torch.empty((B, H, T_dst, d), dtype=src.dtype, device=src.device)
+    flags = _lib.FLAG_ZERO_FILL if zero_fill else 0
+    rc = _LIB.scfa_scatter_rows(_ptr(src), _ptr(index), _ptr(dst), B, H, Ts, T_dst, d, _dtype_code(src), flags,
+                                _stream())
+    _lib.check("scfa_scatter_rows", rc)
+    return dst

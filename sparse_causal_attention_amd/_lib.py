@@ -24,6 +24,8 @@ EXPORTED = (
     "scfa_attn_fwd_lists",
     "scfa_attn_bwd_dq_lists",
     "scfa_attn_bwd_dkdv_lists",
+    "scfa_gather_rows",
+    "scfa_scatter_rows",
     "scfa_workspace_size",
     "scfa_last_error",
 )
@@ -40,6 +42,7 @@ DTYPE_FP32 = 1
 FLAG_NO_PRUNE = 1 << 0
 FLAG_FORCE_MASK = 1 << 1
 FLAG_IDX_ASCENDING = 1 << 2
+FLAG_ZERO_FILL = 1 << 3
 
 OP_QK_FWD = 0
 OP_QK_BWD = 1
@@ -66,6 +69,8 @@ _SIGNATURES = {
     "scfa_attn_fwd_lists": [_p] * 11 + _LISTS_TAIL,
     "scfa_attn_bwd_dq_lists": [_p] * 14 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_lists": [_p] * 14 + _LISTS_TAIL,
+    "scfa_gather_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p],
+    "scfa_scatter_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p],
     "scfa_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],
     "scfa_last_error": [],
 }

@@ -273,6 +273,32 @@ size_t lsh_ws(int B, int H, int T, int d, int nb) {
          round_up((size_t)H * d * scfa::lsh_r64_cols(nb) * 8);
 }
 
+int rows_call(bool gather, const void *src, const int32_t *index, void *dst, int B, int H, int Ts, int Td, int d,
+              int dtype, unsigned flags, void *stream) {
+  if (B < 1 || H < 1 || Ts < 0 || Td < 0 || d < 1)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H, d >= 1 and T_src, T_dst >= 0 required");
+  if (dtype != SCFA_DTYPE_BF16 && dtype != SCFA_DTYPE_FP32) return fail(SCFA_ERR_UNSUPPORTED, "dtype=%d unsupported", dtype);
+  const int esize = dtype == SCFA_DTYPE_BF16 ? 2 : 4;
+  if ((d * esize) % 16 != 0) return fail(SCFA_ERR_UNSUPPORTED, "row of %d bytes is not a multiple of 16", d * esize);
+  if (flags & ~(gather ? 0u : SCFA_FLAG_ZERO_FILL)) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
+  const long long BH = (long long)B * H;
+  const long long T = Ts > Td ? Ts : Td;
+  if (BH * T >= (1ll << 31) || BH * T * d >= (1ll << 40)) return fail(SCFA_ERR_INVALID_ARGUMENT, "tensors too large");
+  int rc;
+  const long long n_index = BH * (gather ? Td : Ts);
+  if ((rc = check_ptr(src, BH * Ts * d, 16, "src")) || (rc = check_ptr(dst, BH * Td * d, 16, "dst")) ||
+      (rc = check_ptr(index, n_index, 4, "index")))
+    return rc;
+  const char *s0 = static_cast<const char *>(src), *d0 = static_cast<const char *>(dst);
+  if (BH * Ts * d > 0 && BH * Td * d > 0 && s0 < d0 + BH * Td * d * esize && d0 < s0 + BH * Ts * d * esize)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "src and dst overlap");
+  scfa::RowArgs r{src, index, dst, (int)BH, Ts, Td, d * esize / 16};
+  const hipError_t e = gather ? scfa::launch_gather_rows(r, static_cast<hipStream_t>(stream))
+                              : scfa::launch_scatter_rows(r, (flags & SCFA_FLAG_ZERO_FILL) != 0,
+                                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, gather ? "gather rows" : "scatter rows");
+  return ok();
+}
 }  // namespace
 
 extern "C" {
@@ -482,6 +508,16 @@ int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q
   hipError_t e = scfa::launch_block_meta(m, col_count != nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block metadata");
   return ok();
+}
+
+int scfa_gather_rows(const void *src, const int32_t *index, void *dst, int B, int H, int T_src, int T_dst, int d,
+                     int dtype, void *stream) {
+  return rows_call(true, src, index, dst, B, H, T_src, T_dst, d, dtype, 0, stream);
+}
+
+int scfa_scatter_rows(const void *src, const int32_t *index, void *dst, int B, int H, int T_src, int T_dst, int d,
+                      int dtype, unsigned flags, void *stream) {
+  return rows_call(false, src, index, dst, B, H, T_src, T_dst, d, dtype, flags, stream);
 }
 
 size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int block, int n_buckets) {

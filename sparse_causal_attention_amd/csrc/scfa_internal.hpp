@@ -31,6 +31,15 @@ struct AttnArgs {
   int no_prune, force_mask;
 };
 
+// Row gather / scatter: [BH, Ts, row] <-> [BH, Td, row], rows of ppr 16-byte
+// pieces, index [BH, Td] (gather) or [BH, Ts] (scatter).
+struct RowArgs {
+  const void *src;
+  const int32_t *index;
+  void *dst;
+  int BH, Ts, Td, ppr;
+};
+
 struct MetaArgs {
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
   int32_t *q_stats, *k_stats;  // [BH, nq, 4], [BH, nk, 4]
@@ -58,6 +67,8 @@ struct LshArgs {
 
 hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s);
 
+hipError_t launch_gather_rows(const RowArgs &r, hipStream_t s);
+hipError_t launch_scatter_rows(const RowArgs &r, bool zero_fill, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const AttnArgs &a, int mode, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs &a, int mode, hipStream_t s);
 // part: bit 0 = dQ (+ D = rowsum(dO * O)), bit 1 = dK/dV (reads D).

@@ -149,3 +149,30 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_row_gather_scatter_validation():
+    lib = _lib.load()
+
+    def g(**kw):
+        a = dict(src=P, index=P2, dst=P + (1 << 24), B=1, H=2, Ts=100, Td=80, d=64, dtype=0)
+        a.update(kw)
+        return lib.scfa_gather_rows(a["src"], a["index"], a["dst"], a["B"], a["H"], a["Ts"], a["Td"], a["d"],
+                                    a["dtype"], None)
+
+    def s(flags=0, **kw):
+        a = dict(src=P, index=P2, dst=P + (1 << 24), B=1, H=2, Ts=100, Td=80, d=64, dtype=0)
+        a.update(kw)
+        return lib.scfa_scatter_rows(a["src"], a["index"], a["dst"], a["B"], a["H"], a["Ts"], a["Td"], a["d"],
+                                     a["dtype"], flags, None)
+
+    assert g(dtype=3) == _lib.ERR_UNSUPPORTED
+    assert g(d=4) == _lib.ERR_UNSUPPORTED  # 8-byte rows
+    assert g(B=0) == _lib.ERR_INVALID_ARGUMENT
+    assert g(src=None) == _lib.ERR_INVALID_ARGUMENT
+    assert g(index=P2 + 2) == _lib.ERR_INVALID_ARGUMENT
+    assert g(dst=P + 8) == _lib.ERR_INVALID_ARGUMENT
+    assert g(dst=P + 1024) == _lib.ERR_INVALID_ARGUMENT  # overlaps src
+    assert s(flags=1) == _lib.ERR_INVALID_ARGUMENT  # not a scatter flag
+    assert s(flags=_lib.FLAG_ZERO_FILL, dst=None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.scfa_last_error().decode()
