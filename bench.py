@@ -18,6 +18,18 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-dense] [--copy-calibration MIB]
        python bench.py --sweep-nb 2,4,8,16,32,64,128 [--steps K] [--warmup W]
        python bench.py --measure-rows [--steps K] [--warmup W]
+       python bench.py --sweep-drop 0,0.1,...,0.9 | --sweep-T 1024,...,1048576 [--steps K]
+
+--sweep-drop: QK-sparse training step (B=4, H=12, T=8192, d=64) at each drop
+rate: compaction (gather), forward + backward on the kept tokens,
+un-compaction (scatter), against the naive way of dropping tokens, which
+masks them inside dense causal attention at the full length and so costs
+the dense-causal step whatever the rate.
+--sweep-T: Hash-sparse (B=1, H=8, d=64, 32 buckets) at each length: LSH +
+sort of Q and K, forward + backward; up to 32k tokens also the dense-causal
+step and the naive hash attention (every tile computed, then masked:
+NO_PRUNE + FORCE_MASK on the same sorted inputs); beyond, forward only.
+Both print one JSON line per point (synthetic inputs drawn on the GPU).
 
 --measure-rows times the row gather / scatter calls around the path at the
 same shape (un-sorting O, dQ, dK, dV of the step; compacting Q, K, V to a
@@ -240,6 +252,86 @@ def _time_steps(torch, fn, steps, warmup, timer=None):
     return (time.perf_counter() - t0) / steps * 1e3, out
 
 
+def _gpu_normal(torch, shape, seed):
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+
+
+def _dense_step(scfa, q, k, v, do):
+    o, lse = scfa.qk_sparse_fwd(q, k, v)
+    scfa.qk_sparse_bwd(q, k, v, o, lse, do)
+
+
+def sweep_drop(scfa, torch, rates, args):
+    B, H, T, d = 4, 12, 8192, 64
+    q, k, v, do = (_gpu_normal(torch, (B, H, T, d), 100 + i) for i in range(4))
+    dense_ms, _ = _time_steps(torch, lambda _: _dense_step(scfa, q, k, v, do), max(3, args.steps // 2),
+                              max(1, args.warmup))
+    for rate in rates:
+        n_keep = max(1, int(round((1.0 - rate) * T)))
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(7)
+        keep = torch.stack([torch.stack([torch.sort(torch.randperm(T, generator=g, device="cuda:0")[:n_keep])[0]
+                                         for _ in range(H)]) for _ in range(B)]).to(torch.int32).contiguous()
+
+        def step(_):
+            qc, kc, vc, gc = (scfa.gather_rows(x, keep) for x in (q, k, v, do))
+            o, lse = scfa.qk_sparse_fwd(qc, kc, vc, keep, keep)
+            grads = scfa.qk_sparse_bwd(qc, kc, vc, o, lse, gc, keep, keep)
+            for x in (o, *grads):
+                scfa.scatter_rows(x, keep, T)
+
+        ms, _ = _time_steps(torch, step, args.steps, args.warmup)
+        print(json.dumps({"sweep": "qk_drop_rate", "B": B, "H": H, "T": T, "d": d, "drop_rate": rate,
+                          "kept": n_keep, "scfa_step_ms": round(ms, 4),
+                          "naive_token_drop_ms": round(dense_ms, 4), "speedup_vs_naive": round(dense_ms / ms, 3),
+                          "scfa_step": "gather Q,K,V,dO + QK-sparse fwd + bwd + scatter O,dQ,dK,dV",
+                          "naive": "dense causal fwd + bwd at full length (masking does not reduce its work)"}),
+              flush=True)
+
+
+def sweep_length(scfa, torch, lengths, args):
+    B, H, d, nb = 1, 8, 64, 32
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(3)
+    R = torch.randn((H, d, nb // 2), generator=g, device="cuda:0", dtype=torch.float32)
+    naive_flags = scfa.FLAG_NO_PRUNE | scfa.FLAG_FORCE_MASK
+    for T in lengths:
+        q, k, v, do = (_gpu_normal(torch, (B, H, T, d), 200 + i) for i in range(4))
+        train = T <= 32768
+        state = {}
+
+        def scfa_step(_):
+            qh, qi, _, qs, dos = scfa.lsh_bucket_sort(q, R, nb, companion=do)
+            kh, ki, _, ks, vs = scfa.lsh_bucket_sort(k, R, nb, companion=v)
+            o, lse = scfa.hash_sparse_fwd(qs, ks, vs, qi, ki, qh, kh)
+            if train:
+                scfa.hash_sparse_bwd(qs, ks, vs, o, lse, dos, qi, ki, qh, kh)
+            state["sorted"] = (qs, ks, vs, dos, qi, ki, qh, kh, o, lse)
+
+        steps = args.steps if T <= 262144 else max(2, args.steps // 4)
+        ms, _ = _time_steps(torch, scfa_step, steps, min(args.warmup, 2))
+        line = {"sweep": "hash_length", "B": B, "H": H, "T": T, "d": d, "n_buckets": nb,
+                "pass": "fwd+bwd" if train else "fwd", "scfa_ms": round(ms, 4)}
+        if train:
+            qs, ks, vs, dos, qi, ki, qh, kh, o, lse = state["sorted"]
+
+            def naive(_):
+                o2, l2 = scfa.hash_sparse_fwd(qs, ks, vs, qi, ki, qh, kh, flags=naive_flags)
+                scfa.hash_sparse_bwd(qs, ks, vs, o2, l2, dos, qi, ki, qh, kh, flags=naive_flags)
+
+            nd = max(2, args.steps // 4)
+            naive_ms, _ = _time_steps(torch, naive, nd, 1)
+            dense_ms, _ = _time_steps(torch, lambda _: _dense_step(scfa, q, k, v, do), nd, 1)
+            line.update({"naive_hash_ms": round(naive_ms, 4), "dense_causal_ms": round(dense_ms, 4),
+                         "speedup_vs_dense_causal": round(dense_ms / ms, 3),
+                         "speedup_vs_naive_hash": round(naive_ms / ms, 3)})
+        print(json.dumps(line), flush=True)
+        del q, k, v, do, state
+        torch.cuda.empty_cache()
+
+
 def measure_rows(scfa, torch, w, q, k, v, do, R, args):
     """HBM throughput of gather_rows / scatter_rows at the step's shape."""
     import numpy as np
@@ -313,6 +405,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
     ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
                     help="comma-separated bucket counts: one JSON line per count instead of the benchmark line")
+    ap.add_argument("--sweep-drop", type=str, default="", metavar="LIST", help="comma-separated drop rates")
+    ap.add_argument("--sweep-T", type=str, default="", metavar="LIST", help="comma-separated sequence lengths")
     ap.add_argument("--measure-rows", action="store_true",
                     help="time the row gather / scatter calls instead of the step (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -327,6 +421,13 @@ def main():
 
     import sparse_causal_attention_amd as scfa
     from gen import WORKLOADS
+
+    if args.sweep_drop:
+        sweep_drop(scfa, torch, [float(x) for x in args.sweep_drop.split(",")], args)
+        return
+    if args.sweep_T:
+        sweep_length(scfa, torch, [int(x) for x in args.sweep_T.split(",")], args)
+        return
 
     w = WORKLOADS[WORKLOAD_ID]
     _log(f"[bench] workload {w.name}: generating inputs")
