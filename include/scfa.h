@@ -39,6 +39,13 @@
  * Values.  Original positions satisfy 0 <= idx < 2147483647.  Bucket ids are
  *   any int32 (attention only compares them).  Inputs need not be sorted by
  *   position or bucket: sorting only changes speed, never the result.
+ * Ragged lengths.  Heads whose kept counts differ share the [B,H,T,...]
+ *   layout padded to the longest head: a padding query row carries position
+ *   -1 (it admits no key: output 0, lse -inf, zero gradients) and a padding
+ *   key row position 2147483647 (no query admits it; its dK, dV are 0).
+ *   Blocks made only of padding are pruned like any other dead tile, so the
+ *   work follows each head's own length.  Padding rows' values are ignored
+ *   (keep them finite).
  * Types.  dtype SCFA_DTYPE_BF16: tensors are bfloat16, products accumulate in
  *   float32 on the matrix cores, softmax is float32, P is rounded to bf16
  *   before the P.V product, outputs are rounded once.  SCFA_DTYPE_FP32: every

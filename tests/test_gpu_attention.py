@@ -10,7 +10,7 @@ import zlib
 import numpy as np
 import pytest
 
-from gen import synthetic_case
+from gen import bf16_round, synthetic_case
 from helpers import check_forward, check_grads, dev, note, to_np
 from oracle import attention as A
 
@@ -173,3 +173,49 @@ def test_value_ones_gives_ones():
     nonempty = ~np.isneginf(to_np(lse))
     assert np.all(o[nonempty] == 1.0)
     assert np.all(o[~nonempty] == 0.0)
+
+
+@pytest.mark.parametrize("mode", ["qk", "hash"])
+def test_ragged_head_lengths_by_padding(mode):
+    """Heads with different kept counts in one padded batch: padding queries at
+    position -1, padding keys at 2^31 - 1; every head equals the oracle at its
+    own length, and padding rows give 0 (lse -inf) and zero gradients."""
+    rng = np.random.default_rng(31 if mode == "qk" else 32)
+    B, H, T, d = 2, 3, 640, 64
+    nq = rng.integers(60, T + 1, (B, H))
+    nk = rng.integers(60, T + 1, (B, H))
+    nq[0, 0], nk[0, 1] = T, 1
+    Q, K, V, G = (bf16_round(rng.standard_normal((B, H, T, d)).astype(np.float32)) for _ in range(4))
+    qi = np.full((B, H, T), -1, np.int32)
+    ki = np.full((B, H, T), 2**31 - 1, np.int32)
+    qh = rng.integers(0, 5, (B, H, T)).astype(np.int32)
+    kh = rng.integers(0, 5, (B, H, T)).astype(np.int32)
+    for b in range(B):
+        for h in range(H):
+            qi[b, h, :nq[b, h]] = np.sort(rng.choice(2 * T, nq[b, h], replace=False))
+            ki[b, h, :nk[b, h]] = np.sort(rng.choice(2 * T, nk[b, h], replace=False))
+    scfa = _lib()
+    note(f"[ragged] {mode}")
+    q, k, v, g = (dev(x, torch.bfloat16) for x in (Q, K, V, G))
+    idx = (dev(qi), dev(ki))
+    if mode == "qk":
+        o, lse = scfa.qk_sparse_fwd(q, k, v, *idx)
+        grads = scfa.qk_sparse_bwd(q, k, v, o, lse, g, *idx)
+    else:
+        hs = (dev(qh), dev(kh))
+        o, lse = scfa.hash_sparse_fwd(q, k, v, *idx, *hs)
+        grads = scfa.hash_sparse_bwd(q, k, v, o, lse, g, *idx, *hs)
+    torch.cuda.synchronize()
+    o, lse = to_np(o), to_np(lse)
+    dq, dk, dv = (to_np(x) for x in grads)
+    for b in range(B):
+        for h in range(H):
+            a, c = nq[b, h], nk[b, h]
+            hq = qh[b, h, :a] if mode == "hash" else None
+            hk = kh[b, h, :c] if mode == "hash" else None
+            o_ref, lse_ref = A.forward(Q[b, h, :a], K[b, h, :c], V[b, h, :c], qi[b, h, :a], ki[b, h, :c], hq, hk)
+            check_forward(o[b, h, :a], lse[b, h, :a], o_ref, lse_ref, "bf16", f"ragged {mode} b{b}h{h}")
+            ref = A.backward(Q[b, h, :a], K[b, h, :c], V[b, h, :c], G[b, h, :a], qi[b, h, :a], ki[b, h, :c], hq, hk)
+            check_grads([dq[b, h, :a], dk[b, h, :c], dv[b, h, :c]], ref, "bf16", f"ragged {mode} b{b}h{h}")
+            assert np.all(o[b, h, a:] == 0) and np.all(np.isneginf(lse[b, h, a:]))
+            assert np.all(dq[b, h, a:] == 0) and np.all(dk[b, h, c:] == 0) and np.all(dv[b, h, c:] == 0)
