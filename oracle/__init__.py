@@ -14,6 +14,8 @@ from the exact values the GPU sees (bf16 inputs widened without rounding):
 * ``blocks``: per-block min/max of positions and bucket ids, the tile liveness
   and mask-free predicates, and the per-row / per-column live-tile lists,
   all by brute force over every block pair.
+* ``coverage``: the share of bucket collisions (admissible pairs) a chunked
+  within-bucket approximation visits, against SCFA's exact mask.
 * ``rows``: gathering rows into compact / reordered tensors and scattering
   results back to their original rows.
 * ``lsh``: the random-rotation LSH bucket (first maximum of ``[xR, -xR]``)
@@ -31,4 +33,4 @@ integer-exact cases, closed forms and invariants.  Nothing here is
 "parity unpinned".
 """
 
-from . import attention, blocks, lsh, rows  # noqa: F401
+from . import attention, blocks, coverage, lsh, rows  # noqa: F401
