@@ -66,9 +66,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E (published)
 PEAK_FP64_TFLOPS = 78.6  # MI355X fp64 vector (published)
 WORKLOAD_ID = 4
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_bwd_dkdv_hash_train_T16384_traffic.txt")
-# files that determine the code of the attention kernels
-KERNEL_SOURCES = ["attn_bwd.hip", "attn_fwd.hip", "scfa_pipe.hpp", "scfa_device.hpp", "scfa_internal.hpp",
-                  "../build.py"]
+# files that determine the code of the attention kernels and the tile lists they walk
+KERNEL_SOURCES = ["attn_bwd.hip", "attn_fwd.hip", "meta.hip", "scfa_pipe.hpp", "scfa_device.hpp",
+                  "scfa_internal.hpp", "../build.py"]
 
 
 def kernel_source_digest():
@@ -80,15 +80,16 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None."""
+def measured_traffic(tile_rule):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
+    (None too when the summary was taken with the other tile rule)."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_digest") != kernel_source_digest():
+    if kv.get("source_digest") != kernel_source_digest() or kv.get("tile_rule") != tile_rule:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -159,7 +160,7 @@ class Timer:
         return sum(s) / len(s) if s else float("nan")
 
 
-def run_step(scfa, w, q, k, v, do, R, timer=None):
+def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True):
     nb, blk, sc = w.n_buckets, w.block, w.scale
     if timer:
         timer.begin()
@@ -169,7 +170,7 @@ def run_step(scfa, w, q, k, v, do, R, timer=None):
     kh, ki, _, ks, vs = scfa.lsh_bucket_sort(k, R, nb, companion=v)
     if timer:
         timer.mark()
-    meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=True)
+    meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=True, exact=exact)
     if timer:
         timer.mark()
     o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc)
@@ -380,7 +381,8 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, nbs, args):
         wn = dataclasses.replace(w, n_buckets=nb, name=f"{w.name.rsplit('_nb', 1)[0]}_nb{nb}")
         R = torch.from_numpy(np.stack([lsh_rotation(wn, h) for h in range(w.H)])).to("cuda:0")
         timer = Timer(torch, STEP_CALLS)
-        ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t), args.steps,
+        ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists),
+                                    args.steps,
                                     args.warmup, timer)
         timer.collect()
         units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
@@ -403,6 +405,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
+    ap.add_argument("--range-lists", action="store_true",
+                    help="build the tile lists with the bucket-range rule only (keep tiles that hold no valid pair)")
     ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
                     help="comma-separated bucket counts: one JSON line per count instead of the benchmark line")
     ap.add_argument("--sweep-drop", type=str, default="", metavar="LIST", help="comma-separated drop rates")
@@ -452,7 +456,7 @@ def main():
 
     _log("[bench] warmup")
     for _ in range(args.warmup):
-        run_step(scfa, w, q, k, v, do, R)
+        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists)
     torch.cuda.synchronize()
 
     # HIP events between the calls, on the stream the kernels run on, inside the timed region
@@ -461,7 +465,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        meta, _ = run_step(scfa, w, q, k, v, do, R, timer)
+        meta, _ = run_step(scfa, w, q, k, v, do, R, timer, exact=not args.range_lists)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -470,6 +474,11 @@ def main():
     units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
     step_flops = 14.0 * units * w.d
     value = step_flops / (ms_per_step * 1e-3) / 1e12
+    # tiles the bucket-range rule alone would visit (context; not timed)
+    qh, qi, _, _, _ = scfa.lsh_bucket_sort(q, R, w.n_buckets)
+    kh, ki, _, _, _ = scfa.lsh_bucket_sort(k, R, w.n_buckets)
+    _, range_tiles = tile_work(scfa.block_meta(qi, ki, qh, kh, block=w.block, with_cols=False), w.Tq, w.Tk,
+                               w.block, torch)
 
     dtimer = Timer(torch, DENSE_CALLS)
     dense_ms = float("nan")
@@ -503,7 +512,7 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": measured_traffic() if dominant == "bwd_dkdv" else None,
+        "traffic": measured_traffic("range" if args.range_lists else "exact") if dominant == "bwd_dkdv" else None,
         "avg_launch_ms": per_call[dominant],
         "algorithmic_flops_per_launch": kernel_flops[dominant],
     }
@@ -535,9 +544,11 @@ def main():
             "block": w.block,
             "n_buckets": w.n_buckets,
             "step": "lsh+sort(Q,dO) + lsh+sort(K,V) + block lists + fwd + bwd",
+            "tile_rule": "range" if args.range_lists else "exact",
         },
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "executed_tiles": tiles,
+        "range_rule_tiles": range_tiles,
         "dense_causal_tiles": w.B * w.H * (w.T // w.block) * (w.T // w.block + 1) // 2,
         "attention_only_tflops": round(step_flops / (attn_ms * 1e-3) / 1e12, 3),
         "dense_causal_ms": None if args.no_dense else round(dense_ms, 4),

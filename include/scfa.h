@@ -23,7 +23,10 @@
  * Tiles of `block` query rows x `block` key rows are skipped when every query
  * precedes every key ("1. QK-Sparse" rule 1) or, in Hash-sparse mode, when the
  * two blocks' bucket ranges do not overlap ("2. Hash-Sparse" rules 1-2); the
- * skipped tiles hold no valid pair, so the result is exact.
+ * skipped tiles hold no valid pair, so the result is exact.  The Hash-sparse
+ * entry points below also skip the tiles that pass the range test yet hold
+ * no valid pair (the exact test of scfa_block_meta_exact); that changes no
+ * output bit.
  *
  * Conventions shared by all entry points
  * --------------------------------------
@@ -205,6 +208,33 @@ int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx,
                     int32_t *q_stats, int32_t *k_stats,
                     int32_t *row_count, int32_t *row_list,
                     int32_t *col_count, int32_t *col_list, void *stream);
+
+/*
+ * scfa_block_meta with exact tile liveness in Hash-sparse mode.  The page's
+ * block rule ("2. Hash-Sparse" rules 1-2) keeps a tile when the blocks'
+ * bucket ranges overlap, which also keeps tiles where every bucket the blocks
+ * share has all its keys after all its queries; such a tile holds no valid
+ * pair.  Here a tile is live iff it passes the range test and some bucket h
+ * present in both blocks has min k_idx over the key rows of bucket h <= max
+ * q_idx over the query rows of bucket h, which is exactly "the tile holds a
+ * valid pair".  A block with more than 3 distinct buckets keeps the range
+ * test's answer for its tiles.  Mask-free flags, list layout and all other
+ * arguments are as in scfa_block_meta; attention over these lists gives
+ * bit-identical results (a skipped tile would only add exact zeros).
+ *   q_segs [B,H,nq,16], k_segs [B,H,nk,16] int32, 16-byte aligned, written:
+ *   per block, [0] = number of distinct buckets if <= 3, else -1; [1..3] = 0;
+ *   then 3 records (bucket, min idx, max idx, 0) in ascending bucket order
+ *   (unused records 0; all records 0 when [0] is -1).  In QK-sparse mode (hashes NULL) the range test is
+ *   already exact: segs may be NULL, are not written, and the lists equal
+ *   scfa_block_meta's.
+ */
+int scfa_block_meta_exact(const int32_t *q_idx, const int32_t *k_idx,
+                          const int32_t *q_hash, const int32_t *k_hash,
+                          int B, int H, int Tq, int Tk, int block,
+                          int32_t *q_stats, int32_t *k_stats,
+                          int32_t *q_segs, int32_t *k_segs,
+                          int32_t *row_count, int32_t *row_list,
+                          int32_t *col_count, int32_t *col_list, void *stream);
 
 /*
  * Attention over precomputed block lists: the single-kernel building blocks of

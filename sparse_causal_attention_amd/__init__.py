@@ -197,8 +197,13 @@ def lsh_bucket_sort(x, R, n_buckets, idx=None, companion=None, *, idx_ascending=
     return hs, ids, perm, xs, cs
 
 
-def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=True):
-    """Block statistics and live-tile lists (see include/scfa.h, scfa_block_meta)."""
+def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=True, exact=False):
+    """Block statistics and live-tile lists (see include/scfa.h, scfa_block_meta).
+
+    ``exact=True`` calls scfa_block_meta_exact: in Hash-sparse mode the lists
+    also drop tiles that pass the bucket-range test yet hold no valid pair, and
+    the per-block bucket segments are returned as "q_segs" / "k_segs".
+    """
     B, H, Tq = q_idx.shape
     Tk = k_idx.shape[2]
     _need(q_idx, "q_idx", torch.int32)
@@ -216,11 +221,19 @@ def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=Tr
     if with_cols:
         out["col_count"] = torch.empty((B, H, nk), dtype=torch.int32, device=dev)
         out["col_list"] = torch.empty((B, H, nk, nq), dtype=torch.int32, device=dev)
-    rc = _LIB.scfa_block_meta(_ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), B, H, Tq, Tk, block,
-                              _ptr(out["q_stats"]), _ptr(out["k_stats"]), _ptr(out["row_count"]),
-                              _ptr(out["row_list"]), _ptr(out.get("col_count")), _ptr(out.get("col_list")),
-                              _stream())
-    _lib.check("scfa_block_meta", rc)
+    lists = (_ptr(out["row_count"]), _ptr(out["row_list"]), _ptr(out.get("col_count")), _ptr(out.get("col_list")))
+    if exact:
+        if q_hash is not None:
+            out["q_segs"] = torch.empty((B, H, nq, 16), dtype=torch.int32, device=dev)
+            out["k_segs"] = torch.empty((B, H, nk, 16), dtype=torch.int32, device=dev)
+        rc = _LIB.scfa_block_meta_exact(_ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), B, H, Tq, Tk, block,
+                                        _ptr(out["q_stats"]), _ptr(out["k_stats"]), _ptr(out.get("q_segs")),
+                                        _ptr(out.get("k_segs")), *lists, _stream())
+        _lib.check("scfa_block_meta_exact", rc)
+    else:
+        rc = _LIB.scfa_block_meta(_ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), B, H, Tq, Tk, block,
+                                  _ptr(out["q_stats"]), _ptr(out["k_stats"]), *lists, _stream())
+        _lib.check("scfa_block_meta", rc)
     return out
 
 

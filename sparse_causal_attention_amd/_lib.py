@@ -21,6 +21,7 @@ EXPORTED = (
     "scfa_hash_sparse_bwd",
     "scfa_lsh_bucket_sort",
     "scfa_block_meta",
+    "scfa_block_meta_exact",
     "scfa_attn_fwd_lists",
     "scfa_attn_bwd_dq_lists",
     "scfa_attn_bwd_dkdv_lists",
@@ -66,6 +67,7 @@ _SIGNATURES = {
     "scfa_hash_sparse_bwd": [_p] * 13 + _ATTN_TAIL,
     "scfa_lsh_bucket_sort": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_block_meta": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p],
+    "scfa_block_meta_exact": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p],
     "scfa_attn_fwd_lists": [_p] * 11 + _LISTS_TAIL,
     "scfa_attn_bwd_dq_lists": [_p] * 14 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_lists": [_p] * 14 + _LISTS_TAIL,

@@ -70,7 +70,8 @@ int check_shape(const Shape &s) {
 size_t attn_ws(bool bwd, int B, int H, int Tq, int Tk, int block) {
   const size_t BH = (size_t)B * H;
   const size_t nq = nblocks(Tq, block), nk = nblocks(Tk, block);
-  size_t n = round_up(BH * nq * 16) + round_up(BH * nk * 16) + round_up(BH * nq * 4) + round_up(BH * nq * nk * 4);
+  size_t n = round_up(BH * nq * 16) + round_up(BH * nk * 16) + round_up(BH * nq * 4) + round_up(BH * nq * nk * 4) +
+             round_up(BH * nq * scfa::kSegInts * 4) + round_up(BH * nk * scfa::kSegInts * 4);
   if (bwd) n += round_up(BH * nk * 4) + round_up(BH * nk * nq * 4) + round_up(2 * BH * (size_t)Tq * 4);
   return n;
 }
@@ -231,6 +232,9 @@ int attention(const AttnCall &c) {
       m.k_stats = cv.take<int32_t>((size_t)BH * nk * 16);
       m.row_cnt = cv.take<int32_t>((size_t)BH * nq * 4);
       m.row_list = cv.take<int32_t>((size_t)BH * nq * nk * 4);
+      int32_t *qsg = cv.take<int32_t>((size_t)BH * nq * scfa::kSegInts * 4);
+      int32_t *ksg = cv.take<int32_t>((size_t)BH * nk * scfa::kSegInts * 4);
+      if (hashed) m.q_segs = qsg, m.k_segs = ksg;  // exact tile test
       if (bwd) {
         m.col_cnt = cv.take<int32_t>((size_t)BH * nk * 4);
         m.col_list = cv.take<int32_t>((size_t)BH * nk * nq * 4);
@@ -271,6 +275,58 @@ size_t lsh_ws(int B, int H, int T, int d, int nb) {
   const size_t nbins = (size_t)scfa::sort_bins(nb, true);
   return round_up(BH * T * 4) + round_up(BH * nbins * scfa::sort_chunks(T) * 4) + 4 * round_up(BH * T * 4) +
          round_up((size_t)H * d * scfa::lsh_r64_cols(nb) * 8);
+}
+
+int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B, int H,
+              int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, int32_t *q_segs, int32_t *k_segs,
+              bool exact, int32_t *row_count, int32_t *row_list, int32_t *col_count, int32_t *col_list,
+              void *stream) {
+  if (B < 1 || H < 1 || Tq < 0 || Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tk >= 0 required");
+  if (block != 64 && block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
+  if ((q_hash == nullptr) != (k_hash == nullptr))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_hash and k_hash must both be NULL or both set");
+  if ((col_count == nullptr) != (col_list == nullptr))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "col_count and col_list must both be NULL or both set");
+  const long long BH = (long long)B * H;
+  const long long nq = nblocks(Tq, block), nk = nblocks(Tk, block);
+  if (BH * nq * nk >= (1ll << 31) || BH * (Tq > Tk ? Tq : Tk) >= (1ll << 31))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "metadata too large");
+  int rc;
+  if ((rc = check_ptr(q_idx, BH * Tq, 4, "q_idx")) || (rc = check_ptr(k_idx, BH * Tk, 4, "k_idx")) ||
+      (rc = check_ptr(q_hash, q_hash ? BH * Tq : 0, 4, "q_hash")) ||
+      (rc = check_ptr(k_hash, k_hash ? BH * Tk : 0, 4, "k_hash")) ||
+      (rc = check_ptr(q_stats, BH * nq * 4, 16, "q_stats")) || (rc = check_ptr(k_stats, BH * nk * 4, 16, "k_stats")) ||
+      (rc = check_ptr(row_count, BH * nq, 4, "row_count")) || (rc = check_ptr(row_list, BH * nq * nk, 4, "row_list")))
+    return rc;
+  if (col_count && ((rc = check_ptr(col_count, BH * nk, 4, "col_count")) ||
+                    (rc = check_ptr(col_list, BH * nk * nq, 4, "col_list"))))
+    return rc;
+  const bool use_segs = exact && q_hash != nullptr;  // QK-sparse: the range test is already exact
+  if (use_segs && ((rc = check_ptr(q_segs, BH * nq * scfa::kSegInts, 16, "q_segs")) ||
+                   (rc = check_ptr(k_segs, BH * nk * scfa::kSegInts, 16, "k_segs"))))
+    return rc;
+  scfa::MetaArgs m{};
+  m.q_idx = q_idx;
+  m.k_idx = k_idx;
+  m.q_hash = q_hash;
+  m.k_hash = k_hash;
+  m.q_stats = q_stats;
+  m.k_stats = k_stats;
+  m.q_segs = use_segs ? q_segs : nullptr;
+  m.k_segs = use_segs ? k_segs : nullptr;
+  m.row_cnt = row_count;
+  m.row_list = row_list;
+  m.col_cnt = col_count;
+  m.col_list = col_list;
+  m.BH = (int)BH;
+  m.Tq = Tq;
+  m.Tk = Tk;
+  m.nq = (int)nq;
+  m.nk = (int)nk;
+  m.block = block;
+  hipError_t e = scfa::launch_block_meta(m, col_count != nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block metadata");
+  return ok();
 }
 
 int rows_call(bool gather, const void *src, const int32_t *index, void *dst, int B, int H, int Ts, int Td, int d,
@@ -468,46 +524,16 @@ int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int 
 int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B,
                     int H, int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, int32_t *row_count,
                     int32_t *row_list, int32_t *col_count, int32_t *col_list, void *stream) {
-  if (B < 1 || H < 1 || Tq < 0 || Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tk >= 0 required");
-  if (block != 64 && block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
-  if ((q_hash == nullptr) != (k_hash == nullptr))
-    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_hash and k_hash must both be NULL or both set");
-  if ((col_count == nullptr) != (col_list == nullptr))
-    return fail(SCFA_ERR_INVALID_ARGUMENT, "col_count and col_list must both be NULL or both set");
-  const long long BH = (long long)B * H;
-  const long long nq = nblocks(Tq, block), nk = nblocks(Tk, block);
-  if (BH * nq * nk >= (1ll << 31) || BH * (Tq > Tk ? Tq : Tk) >= (1ll << 31))
-    return fail(SCFA_ERR_INVALID_ARGUMENT, "metadata too large");
-  int rc;
-  if ((rc = check_ptr(q_idx, BH * Tq, 4, "q_idx")) || (rc = check_ptr(k_idx, BH * Tk, 4, "k_idx")) ||
-      (rc = check_ptr(q_hash, q_hash ? BH * Tq : 0, 4, "q_hash")) ||
-      (rc = check_ptr(k_hash, k_hash ? BH * Tk : 0, 4, "k_hash")) ||
-      (rc = check_ptr(q_stats, BH * nq * 4, 16, "q_stats")) || (rc = check_ptr(k_stats, BH * nk * 4, 16, "k_stats")) ||
-      (rc = check_ptr(row_count, BH * nq, 4, "row_count")) || (rc = check_ptr(row_list, BH * nq * nk, 4, "row_list")))
-    return rc;
-  if (col_count && ((rc = check_ptr(col_count, BH * nk, 4, "col_count")) ||
-                    (rc = check_ptr(col_list, BH * nk * nq, 4, "col_list"))))
-    return rc;
-  scfa::MetaArgs m{};
-  m.q_idx = q_idx;
-  m.k_idx = k_idx;
-  m.q_hash = q_hash;
-  m.k_hash = k_hash;
-  m.q_stats = q_stats;
-  m.k_stats = k_stats;
-  m.row_cnt = row_count;
-  m.row_list = row_list;
-  m.col_cnt = col_count;
-  m.col_list = col_list;
-  m.BH = (int)BH;
-  m.Tq = Tq;
-  m.Tk = Tk;
-  m.nq = (int)nq;
-  m.nk = (int)nk;
-  m.block = block;
-  hipError_t e = scfa::launch_block_meta(m, col_count != nullptr, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "block metadata");
-  return ok();
+  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, Tq, Tk, block, q_stats, k_stats, nullptr, nullptr, false,
+                   row_count, row_list, col_count, col_list, stream);
+}
+
+int scfa_block_meta_exact(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash,
+                          int B, int H, int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats,
+                          int32_t *q_segs, int32_t *k_segs, int32_t *row_count, int32_t *row_list,
+                          int32_t *col_count, int32_t *col_list, void *stream) {
+  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, Tq, Tk, block, q_stats, k_stats, q_segs, k_segs, true,
+                   row_count, row_list, col_count, col_list, stream);
 }
 
 int scfa_gather_rows(const void *src, const int32_t *index, void *dst, int B, int H, int T_src, int T_dst, int d,

@@ -295,7 +295,48 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortPass p) {
   }
 }
 
+// Cooperative copy of a wave's 64 rows (row src of lane l -> row dst of lane
+// l, skipped where dst < 0) for one or two matrices with P 16-byte pieces per
+// row: each instruction moves 64 / P rows, P lanes per row.  Eight
+// instructions' loads are issued before their stores so that their latencies
+// overlap (the compiler may not move a load above a store to a buffer that
+// might alias it).
+template <int P, bool TWO>
+__device__ __forceinline__ void copy_rows(const uint4 *x0_, uint4 *y0_, const uint4 *x1_, uint4 *y1_, size_t base,
+                                          int src, int dst, int lane) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 *x0 = reinterpret_cast<const u32x4 *>(x0_), *x1 = reinterpret_cast<const u32x4 *>(x1_);
+  u32x4 *y0 = reinterpret_cast<u32x4 *>(y0_), *y1 = reinterpret_cast<u32x4 *>(y1_);
+  constexpr int PER_IT = 64 / P;
+  constexpr int NB = 8;
+  const int piece = lane % P;
+#pragma unroll
+  for (int it0 = 0; it0 < P; it0 += NB) {
+    int ss[NB], sl[NB];
+    u32x4 v0[NB], v1[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int tok = (it0 + j) * PER_IT + lane / P;
+      ss[j] = __shfl(src, tok, 64);
+      sl[j] = __shfl(dst, tok, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      v0[j] = x0[(base + ss[j]) * P + piece];
+      if (TWO) v1[j] = x1[(base + ss[j]) * P + piece];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (sl[j] >= 0) {
+        y0[(base + sl[j]) * P + piece] = v0[j];
+        if (TWO) y1[(base + sl[j]) * P + piece] = v1[j];
+      }
+  }
+}
+
 // Stable scatter of one 256-token chunk; wave w owns tokens 64w .. 64w+63.
+// P = rc.pieces (16-byte pieces per row).
+template <int P>
 __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(SortPass p, RowCopy rc) {
   extern __shared__ int cnt[];  // [4][nbins]
   const int bh = blockIdx.x / p.nchunks;
@@ -326,21 +367,10 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(SortPass p, RowCopy
     p.out_src[base + slot] = src;
     if (p.bucket_pass) p.out_hash[base + slot] = digit;
   }
-  if (rc.xs || rc.cs) {
-    // cooperative row copy: `per_it` tokens per iteration, `pieces` lanes each
-    const int per_it = 64 / rc.pieces;
-    for (int it = 0; it < rc.pieces; ++it) {
-      const int tok = it * per_it + lane / rc.pieces;
-      const int piece = lane % rc.pieces;
-      const int s_src = __shfl(src, tok, 64);
-      const int s_slot = __shfl(slot, tok, 64);
-      const int s_valid = __shfl((int)valid, tok, 64);
-      if (s_valid) {
-        if (rc.xs) rc.xs[(base + s_slot) * rc.pieces + piece] = rc.x[(base + s_src) * rc.pieces + piece];
-        if (rc.cs) rc.cs[(base + s_slot) * rc.pieces + piece] = rc.cmp[(base + s_src) * rc.pieces + piece];
-      }
-    }
-  }
+  const int dst_slot = valid ? slot : -1;  // src is 0 (a real row) on padding lanes
+  if (rc.xs && rc.cs) copy_rows<P, true>(rc.x, rc.xs, rc.cmp, rc.cs, base, src, dst_slot, lane);
+  else if (rc.xs) copy_rows<P, false>(rc.x, rc.xs, nullptr, nullptr, base, src, dst_slot, lane);
+  else if (rc.cs) copy_rows<P, false>(rc.cmp, rc.cs, nullptr, nullptr, base, src, dst_slot, lane);
 }
 
 static hipError_t run_pass(const SortPass &p, const RowCopy &rc, int BH, bool with_hist, hipStream_t s) {
@@ -354,7 +384,10 @@ static hipError_t run_pass(const SortPass &p, const RowCopy &rc, int BH, bool wi
   hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)BH), dim3(1024), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sort_scatter, dim3(grid), dim3(kSortChunk), 4 * p.nbins * sizeof(int), s, p, rc);
+  const size_t lds = 4 * p.nbins * sizeof(int);
+  if (rc.pieces == 32) hipLaunchKernelGGL(k_sort_scatter<32>, dim3(grid), dim3(kSortChunk), lds, s, p, rc);
+  else if (rc.pieces == 16) hipLaunchKernelGGL(k_sort_scatter<16>, dim3(grid), dim3(kSortChunk), lds, s, p, rc);
+  else hipLaunchKernelGGL(k_sort_scatter<8>, dim3(grid), dim3(kSortChunk), lds, s, p, rc);
   return hipGetLastError();
 }
 

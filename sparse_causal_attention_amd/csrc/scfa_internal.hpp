@@ -40,9 +40,17 @@ struct RowArgs {
   int BH, Ts, Td, ppr;
 };
 
+// Bucket segments of one block (exact tile test): kSegInts int32 per block,
+// [0] = number of distinct buckets among the block's rows if at most
+// kMaxSegs, else -1; then kMaxSegs records (bucket, min idx, max idx, 0) in
+// ascending bucket order, unused records zero.
+constexpr int kMaxSegs = 3;
+constexpr int kSegInts = 4 + 4 * kMaxSegs;
+
 struct MetaArgs {
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
   int32_t *q_stats, *k_stats;  // [BH, nq, 4], [BH, nk, 4]
+  int32_t *q_segs, *k_segs;    // [BH, nq, kSegInts], [BH, nk, kSegInts]; NULL = range rule only
   int32_t *row_cnt, *row_list, *col_cnt, *col_list;
   int BH, Tq, Tk, nq, nk, block;
 };

@@ -128,12 +128,26 @@ def test_block_meta_validation():
         _lib.ERR_INVALID_ARGUMENT  # col_count without col_list
 
 
+def test_block_meta_exact_validation():
+    lib = _lib.load()
+    f = lib.scfa_block_meta_exact
+    # hash mode needs both segment arrays, 16-byte aligned
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, None, P, P2, P2, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, P, P + 8, P2, P2, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert f(P2, P2, P2, None, 1, 1, 100, 100, 64, P, P, P, P, P2, P2, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 96, P, P, P, P, P2, P2, None, None, None) == \
+        _lib.ERR_UNSUPPORTED
+
+
 def test_workspace_sizes():
     lib = _lib.load()
     ws = lib.scfa_workspace_size
     r = lambda n: (n + 255) // 256 * 256  # noqa: E731
     BH, nq, nk, Tq = 2 * 3, 4, 2, 200
-    fwd = r(BH * nq * 16) + r(BH * nk * 16) + r(BH * nq * 4) + r(BH * nq * nk * 4)
+    fwd = r(BH * nq * 16) + r(BH * nk * 16) + r(BH * nq * 4) + r(BH * nq * nk * 4) + r(BH * nq * 64) + r(BH * nk * 64)
     bwd = fwd + r(BH * nk * 4) + r(BH * nk * nq * 4) + r(2 * BH * Tq * 4)
     assert ws(_lib.OP_QK_FWD, 2, 3, 200, 100, 64, 64, 0) == fwd
     assert ws(_lib.OP_HASH_BWD, 2, 3, 200, 100, 64, 64, 0) == bwd

@@ -219,3 +219,30 @@ def test_ragged_head_lengths_by_padding(mode):
             check_grads([dq[b, h, :a], dk[b, h, :c], dv[b, h, :c]], ref, "bf16", f"ragged {mode} b{b}h{h}")
             assert np.all(o[b, h, a:] == 0) and np.all(np.isneginf(lse[b, h, a:]))
             assert np.all(dq[b, h, a:] == 0) and np.all(dk[b, h, c:] == 0) and np.all(dv[b, h, c:] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_exact_lists_are_bit_identical(dtype):
+    """Attention over exact lists (fewer tiles) equals attention over range-rule lists bit
+    for bit: the extra tiles of the range rule hold no valid pair."""
+    scfa = _lib()
+    c = synthetic_case(41, B=2, H=3, Tq=1500, Tk=1400, d=64, dtype=dtype, mode="hash", nb=6, layout="grouped")
+    note(f"[exact lists] dtype={dtype}")
+    td = _tdtype(dtype)
+    q, k, v, do = (dev(x).to(td) for x in (c.q, c.k, c.v, c.do))
+    qi, ki, qh, kh = (dev(x) for x in (c.q_idx, c.k_idx, c.q_hash, c.k_hash))
+    m_range = scfa.block_meta(qi, ki, qh, kh, block=64, with_cols=True)
+    m_exact = scfa.block_meta(qi, ki, qh, kh, block=64, with_cols=True, exact=True)
+    torch.cuda.synchronize()
+    n_range, n_exact = int(m_range["row_count"].sum()), int(m_exact["row_count"].sum())
+    assert n_exact < n_range
+    assert int(m_exact["col_count"].sum()) == n_exact
+    res = []
+    for m in (m_range, m_exact):
+        o, lse = scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, m, block=64)
+        dq, delta = scfa.attn_bwd_dq_lists(q, k, v, o, lse, do, qi, ki, qh, kh, m, block=64)
+        dk, dv = scfa.attn_bwd_dkdv_lists(q, k, v, lse, do, delta, qi, ki, qh, kh, m, block=64)
+        res.append((o, lse, dq, dk, dv))
+    torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)

@@ -23,15 +23,25 @@ def _scfa():
     return scfa
 
 
-def _compare_meta(out, c, block):
+def _compare_meta(out, c, block, exact=False, heads=None):
     B, H, Tq = c.q_idx.shape
     hashed = c.q_hash is not None
     got = {k: v.cpu().numpy() for k, v in out.items()}
     for b in range(B):
         for h in range(H):
+            if heads is not None and (b, h) not in heads:
+                continue
             qh = c.q_hash[b, h] if hashed else None
             kh = c.k_hash[b, h] if hashed else None
-            qs, ks, live, free = Bk.metadata(c.q_idx[b, h], c.k_idx[b, h], qh, kh, block)
+            if exact:
+                qs, ks, qseg, kseg, live, free = Bk.metadata_exact(c.q_idx[b, h], c.k_idx[b, h], qh, kh, block)
+                if hashed:
+                    np.testing.assert_array_equal(got["q_segs"][b, h], qseg)
+                    np.testing.assert_array_equal(got["k_segs"][b, h], kseg)
+                else:
+                    assert "q_segs" not in got and "k_segs" not in got
+            else:
+                qs, ks, live, free = Bk.metadata(c.q_idx[b, h], c.k_idx[b, h], qh, kh, block)
             np.testing.assert_array_equal(got["q_stats"][b, h], qs)
             np.testing.assert_array_equal(got["k_stats"][b, h], ks)
             for i, row in enumerate(Bk.row_lists(live, free)):
@@ -65,6 +75,28 @@ def test_block_meta_bit_exact(kw, block):
                              None if c.k_hash is None else dev(c.k_hash), block=block)
     torch.cuda.synchronize()
     _compare_meta(out, c, block)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize(
+    "kw",
+    [
+        dict(Tq=700, Tk=700, mode="qk", shared=True),
+        dict(Tq=1000, Tk=900, mode="hash", nb=6, layout="grouped"),
+        dict(Tq=513, Tk=257, mode="hash", nb=3, layout="shuffled"),
+        dict(Tq=5000, Tk=5000, mode="hash", nb=16, layout="grouped", shared=True),
+        dict(Tq=3000, Tk=2500, mode="hash", nb=150, layout="grouped"),  # many blocks with > 3 buckets
+        dict(Tq=1, Tk=130, mode="hash", nb=2, layout="grouped"),
+    ],
+)
+def test_block_meta_exact_bit_exact(kw, block):
+    c = synthetic_case(22, B=2, H=2, **kw)
+    note(f"[meta exact] {kw} block={block}")
+    out = _scfa().block_meta(dev(c.q_idx), dev(c.k_idx),
+                             None if c.q_hash is None else dev(c.q_hash),
+                             None if c.k_hash is None else dev(c.k_hash), block=block, exact=True)
+    torch.cuda.synchronize()
+    _compare_meta(out, c, block, exact=True)
 
 
 def _lsh_case(seed, B, H, T, d, nb, dtype="bf16"):

@@ -130,3 +130,82 @@ def test_lists_are_ascending_and_consistent():
     assert pairs_r == pairs_c and len(pairs_r) == int(live.sum())
     for r in rows:
         assert [j for j, _ in r] == sorted(j for j, _ in r)
+
+
+# ---------------------------------------------------------------------------
+# Exact liveness ("2. Hash-Sparse" rule 1 read as: keep a tile iff its
+# buckets can match on a causal pair), pinned against brute force.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,nb,block,sort_by_hash", [(0, 4, 32, True), (1, 6, 32, True), (2, 3, 16, False),
+                                                        (3, 40, 32, True), (4, 2, 64, True)])
+def test_exact_liveness_equals_brute_force(seed, nb, block, sort_by_hash):
+    """Where both blocks hold <= MAX_SEGS buckets: live iff the tile holds an admissible
+    pair; elsewhere the range rule's answer.  Always a subset of the range rule."""
+    rng = np.random.default_rng(100 + seed)
+    Tq, Tk = 333, 301
+    qi, ki, qh, kh = _random_case(rng, True, Tq, Tk, nb=nb, sort_by_hash=sort_by_hash)
+    mask = A.element_mask(qi, ki, qh, kh)
+    _, _, live_range, _ = Bk.metadata(qi, ki, qh, kh, block)
+    _, _, qseg, kseg, live, _ = Bk.metadata_exact(qi, ki, qh, kh, block)
+    n_small = 0
+    for i in range(live.shape[0]):
+        for j in range(live.shape[1]):
+            has_pair = bool(_tile_pairs(mask, i, j, block).any())
+            assert not (live[i, j] and not live_range[i, j])
+            if has_pair:
+                assert live[i, j]
+            if qseg[i, 0] >= 0 and kseg[j, 0] >= 0:
+                n_small += 1
+                assert live[i, j] == has_pair, (i, j)
+            else:
+                assert live[i, j] == live_range[i, j]
+    assert n_small > 0
+    if nb <= 3 and block <= 32:
+        assert n_small == live.size  # every block holds at most 3 buckets
+
+
+def test_exact_liveness_drops_bucket_matched_acausal_tiles():
+    """A worked case: both blocks hold buckets {0, 1}, bucket ranges overlap and the
+    blocks are causal overall, yet bucket 0 keys follow bucket 0 queries and
+    bucket 1 keys follow bucket 1 queries: no valid pair, so exact liveness drops it."""
+    qi = np.array([10, 11, 50, 51])
+    qh = np.array([0, 0, 1, 1])
+    ki = np.array([20, 21, 60, 61])
+    kh = np.array([0, 0, 1, 1])
+    mask = A.element_mask(qi, ki, qh, kh)
+    assert not mask.any()
+    _, _, live_range, _ = Bk.metadata(qi, ki, qh, kh, 4)
+    _, _, qseg, kseg, live, _ = Bk.metadata_exact(qi, ki, qh, kh, 4)
+    assert live_range[0, 0] and not live[0, 0]
+    np.testing.assert_array_equal(qseg[0], [2, 0, 0, 0, 0, 10, 11, 0, 1, 50, 51, 0, 0, 0, 0, 0])
+    np.testing.assert_array_equal(kseg[0], [2, 0, 0, 0, 0, 20, 21, 0, 1, 60, 61, 0, 0, 0, 0, 0])
+    # one key of bucket 1 moved before the last bucket-1 query makes the tile live
+    ki2 = np.array([20, 21, 51, 61])
+    _, _, _, _, live2, _ = Bk.metadata_exact(qi, ki2, qh, kh, 4)
+    assert live2[0, 0] and A.element_mask(qi, ki2, qh, kh).any()
+
+
+def test_block_segments_overflow_and_unsorted_rows():
+    idx = np.array([9, 3, 7, 1, 5, 2, 8, 6])
+    hs = np.array([2, 0, 2, 0, 5, 1, 9, 3])
+    seg = Bk.block_segments(idx, hs, 4)
+    # block 0: buckets {0, 2}: (0: min 1, max 3), (2: min 7, max 9)
+    np.testing.assert_array_equal(seg[0], [2, 0, 0, 0, 0, 1, 3, 0, 2, 7, 9, 0, 0, 0, 0, 0])
+    # block 1: four distinct buckets -> overflow marker, records zero
+    np.testing.assert_array_equal(seg[1], [-1] + [0] * 15)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_exact_pruned_evaluation_equals_full_mask(seed):
+    rng = np.random.default_rng(30 + seed)
+    Tq, Tk, d, block = 410, 390, 16, 32
+    qi, ki, qh, kh = _random_case(rng, True, Tq, Tk, nb=5)
+    q, k, v = (rng.standard_normal((n, d)) for n in (Tq, Tk, Tk))
+    o, lse = A.forward(q, k, v, qi, ki, qh, kh)
+    o2, lse2 = Bk.forward_live_tiles_only(q, k, v, qi, ki, qh, kh, block, exact=True)
+    np.testing.assert_allclose(o2, o, atol=1e-12, rtol=0)
+    finite = np.isfinite(lse)
+    np.testing.assert_array_equal(np.isfinite(lse2), finite)
+    np.testing.assert_allclose(lse2[finite], lse[finite], atol=1e-12, rtol=0)
+    # and it really prunes more than the range rule on bucket-sorted inputs
+    assert Bk.metadata_exact(qi, ki, qh, kh, block)[4].sum() < Bk.metadata(qi, ki, qh, kh, block)[2].sum()
