@@ -274,7 +274,8 @@ size_t lsh_ws(int B, int H, int T, int d, int nb) {
   const size_t BH = (size_t)B * H;
   const size_t nbins = (size_t)scfa::sort_bins(nb, true);
   return round_up(BH * T * 4) + round_up(BH * nbins * scfa::sort_chunks(T) * 4) + 4 * round_up(BH * T * 4) +
-         round_up((size_t)H * d * scfa::lsh_r64_cols(nb) * 8);
+         round_up((size_t)H * d * scfa::lsh_r64_cols(nb) * 8) + round_up(scfa::lsh_frag_bytes(H, d, nb)) +
+         round_up((size_t)H * (nb / 2) * 4) + round_up(4) + round_up(2 * BH * nbins * 4);
 }
 
 int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B, int H,
@@ -515,6 +516,11 @@ int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int 
     a.tmp_src[0] = cv.take<int32_t>(BH * T * 4);
     a.tmp_src[1] = cv.take<int32_t>(BH * T * 4);
     a.R64 = cv.take<double>((size_t)H * d * scfa::lsh_r64_cols(n_buckets) * 8);
+    a.Rf = cv.take<char>(scfa::lsh_frag_bytes(H, d, n_buckets));
+    a.colnorm = cv.take<float>((size_t)H * (n_buckets / 2) * 4);
+    a.fb_count = cv.take<int32_t>(4);
+    a.scan_tmp = cv.take<int32_t>(2 * BH * scfa::sort_bins(n_buckets, true) * 4);
+    a.fb_list = a.tmp_src[1];  // idle until the position passes, which run after the hash
   }
   hipError_t e = scfa::launch_lsh_bucket_sort(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "lsh bucket sort");

@@ -18,6 +18,8 @@
 // token rows (x and a companion tensor) to their sorted slots, so the whole
 // call is three launches.  Otherwise four byte passes over the position come
 // first.
+#include <algorithm>
+
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
 
@@ -226,6 +228,332 @@ static void launch_hash(const LshArgs &a, const double *R64, int32_t *hist, int 
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core projection with certified buckets (bf16 inputs).
+//
+// The bucket is defined by the float64 projection above.  For bf16 inputs it
+// is computed on the matrix cores instead, and checked:
+//  * R (float32) is split exactly into three bf16 terms, R = R1 + R2 + R3
+//    (each term takes the next 8 significant bits), so x.R = x.R1 + x.R2 +
+//    x.R3 with every bf16 x bf16 product exact in float32; the 3d products
+//    of a column accumulate in float32 (v_mfma_f32_32x32x16_bf16).
+//  * The float32 sum differs from the float64 one by at most
+//    E = (3.25 d + 8) 2^-22 sum_k |x_k R_kc| <= (3.25 d + 8) 2^-22 |x| max_c |R_c|
+//    (Cauchy-Schwarz): four times the worst case of rounding each of the
+//    3d products' additions and the 3d/16 accumulator additions once in
+//    float32, so it also covers truncating adders.
+//  * If the largest of the 2*(nb/2) candidates [p, -p] exceeds the second by
+//    more than 2E (plus a little for the float32 subtraction), its index is
+//    the float64 bucket.  Otherwise (near ties, exact ties, non-finite
+//    values) the token goes to a list that k_lsh_fallback recomputes in
+//    float64, in the same order as k_lsh_hash.
+// So the ids stay bit-exact, and only a small fraction of the tokens (those
+// whose two best candidates are within about 1e-2 of each other at d = 128)
+// pays for float64.
+// ---------------------------------------------------------------------------
+
+// R split into bf16 A-fragments: entry (h, ct, s, kk, lane) holds, for R
+// column c = 32 ct + lane % 32, the 8 coordinates k = 16 kk + 8 (lane / 32) + j
+// of term s (columns past nb/2 are zero).  Threads past the fragments compute
+// the column norms; thread 0 clears the fallback counter.
+template <int D>
+__global__ __launch_bounds__(256) void k_r_split(const float *R, uint4 *Rf, float *colnorm, int32_t *fb_count, int H,
+                                                 int half, int nct) {
+  constexpr int d = D;
+  const int kks = d / 16;
+  const long long nfrag = (long long)H * nct * 3 * kks * 64;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) *fb_count = 0;
+  if (i < nfrag) {
+    const int lane = (int)(i % 64);
+    const int kk = (int)((i / 64) % kks);
+    const int sp = (int)((i / (64 * kks)) % 3);
+    const int ct = (int)((i / (64 * kks * 3)) % nct);
+    const int h = (int)(i / (64LL * kks * 3 * nct));
+    const int c = 32 * ct + (lane & 31);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      float t[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int k = 16 * kk + 8 * (lane >> 5) + j + q;
+        const float r = c < half ? R[((size_t)h * d + k) * half + c] : 0.f;
+        const float r1 = bf16_bits_to_float(pack_bf16x2(r, 0.f) & 0xffffu);
+        const float rr = r - r1;  // exact
+        const float r2 = bf16_bits_to_float(pack_bf16x2(rr, 0.f) & 0xffffu);
+        const float r3 = rr - r2;  // exact, and at most 8 significant bits
+        t[q] = sp == 0 ? r1 : sp == 1 ? r2 : r3;
+      }
+      w[j / 2] = pack_bf16x2(t[0], t[1]);
+    }
+    Rf[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if (i < nfrag + (long long)H * half) {
+    const long long j = i - nfrag;
+    const int h = (int)(j / half), c = (int)(j % half);
+    float rv[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) rv[k] = R[((size_t)h * D + k) * half + c];
+    double ss = 0.0;
+#pragma unroll
+    for (int k = 0; k < D; ++k) ss = fma((double)rv[k], (double)rv[k], ss);
+    colnorm[j] = (float)(sqrt(ss) * (1.0 + 1e-6));  // rounded up past float conversion and sqrt
+  }
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Running top two of the projections of one token (largest and smallest p,
+// with the index of the first) over the columns a lane sees.
+struct Top2 {
+  float mx1, mx2, mn1, mn2;
+  int imx, imn;
+};
+
+__device__ __forceinline__ void top2_init(Top2 &t) {
+  t.mx1 = t.mx2 = -INFINITY;
+  t.mn1 = t.mn2 = INFINITY;
+  t.imx = t.imn = 0;
+}
+
+// Branch-free: the new second value is the median of (first, second, v);
+// an equal value lands in the second slot (gap 0) and keeps the first index.
+__device__ __forceinline__ void top2_add(Top2 &t, float vmax, float vmin, int c) {
+  t.imx = vmax > t.mx1 ? c : t.imx;
+  t.mx2 = __builtin_amdgcn_fmed3f(t.mx1, t.mx2, vmax);
+  t.mx1 = fmaxf(t.mx1, vmax);
+  t.imn = vmin < t.mn1 ? c : t.imn;
+  t.mn2 = __builtin_amdgcn_fmed3f(t.mn1, t.mn2, vmin);
+  t.mn1 = fminf(t.mn1, vmin);
+}
+
+// Merge with the state of lane l ^ 32 (the other 16 columns of each tile).
+__device__ __forceinline__ void top2_merge_pair(Top2 &t) {
+  const float omx1 = __shfl_xor(t.mx1, 32, 64), omx2 = __shfl_xor(t.mx2, 32, 64);
+  const float omn1 = __shfl_xor(t.mn1, 32, 64), omn2 = __shfl_xor(t.mn2, 32, 64);
+  const int oimx = __shfl_xor(t.imx, 32, 64), oimn = __shfl_xor(t.imn, 32, 64);
+  // candidates are distinct columns; equal values end up in both slots (gap 0)
+  if (omx1 > t.mx1 || (omx1 == t.mx1 && oimx < t.imx)) {
+    t.mx2 = fmaxf(t.mx1, omx2);
+    t.mx1 = omx1;
+    t.imx = oimx;
+  } else {
+    t.mx2 = fmaxf(t.mx2, omx1);
+  }
+  if (omn1 < t.mn1 || (omn1 == t.mn1 && oimn < t.imn)) {
+    t.mn2 = fminf(t.mn1, omn2);
+    t.mn1 = omn1;
+    t.imn = oimn;
+  } else {
+    t.mn2 = fminf(t.mn2, omn1);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint4 *Rf, const float *colnorm,
+                                                           int32_t *hist, int nchunks) {
+  constexpr int KK = D / 16;
+  constexpr int NF = 3 * KK * 64;  // uint4 fragments of one 32-column tile of R
+  constexpr int NP = NF / kHashThreads;
+  constexpr float kErr = (3.25f * D + 8.f) * 0x1p-22f;
+  __shared__ int sh[1024];     // bucket histogram of the chunk (nb <= 1024)
+  __shared__ uint4 rt[2][NF];  // column tiles of R, double-buffered, shared by the group's waves
+  const int bh = blockIdx.x / nchunks, tb = blockIdx.x % nchunks, h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int half = a.nb / 2, nct = (half + 31) / 32;
+  const int t0 = tb * kHashThreads;
+
+  // B operands: the wave's 64 tokens as two 32-token tiles (x rows, 8
+  // coordinates per lane and k-step).
+  const uint16_t *X = static_cast<const uint16_t *>(a.x) + (size_t)bh * a.T * D;
+  bf16x8 xf[2][KK];
+  int tok[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    tok[n] = t0 + 64 * w + 32 * n + col;
+    const bool tv = tok[n] < a.T;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      xf[n][kk] = as_bf16x8(tv ? ld16(X + (size_t)tok[n] * D + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0));
+  }
+  const uint4 *Rh = Rf + (size_t)h * nct * NF;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) rt[0][tid + kHashThreads * i] = Rh[tid + kHashThreads * i];
+  if (hist)
+    for (int i = tid; i < a.nb; i += kHashThreads) sh[i] = 0;
+  float rm = 0.f;
+  for (int c = lane; c < half; c += 64) rm = fmaxf(rm, colnorm[(size_t)h * half + c]);
+  rm = wave_max_f(rm);
+  // each token's norm (this lane's half of the coordinates, then the pair)
+  float xn[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 u = __builtin_bit_cast(uint4, xf[n][kk]);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_bits_to_float(wd[e] & 0xffffu), hi = bf16_bits_to_float(wd[e] >> 16);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    xn[n] = sqrtf(pair_sum(ss)) * 1.0001f;  // rounded up past the float32 sum and sqrt
+  }
+  __syncthreads();
+
+  Top2 t2[2];
+  top2_init(t2[0]);
+  top2_init(t2[1]);
+  for (int ct = 0; ct < nct; ++ct) {
+    const int cb = ct & 1;
+    const bool more = ct + 1 < nct;  // wave-uniform
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 pf[NP];  // next tile (the current one again on the last: always in range, never stored)
+    const u32x4 *nsrc = reinterpret_cast<const u32x4 *>(Rh) + (size_t)(more ? ct + 1 : ct) * NF;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) pf[i] = nsrc[tid + kHashThreads * i];
+    f32x16 acc0 = kZero16, acc1 = kZero16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        const bf16x8 af = as_bf16x8(rt[cb][(sp * KK + kk) * 64 + lane]);
+        acc0 = mfma32(af, xf[0][kk], acc0);
+        acc1 = mfma32(af, xf[1][kk], acc1);
+      }
+    if (32 * (ct + 1) <= half) {  // whole tile in range (wave-uniform)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * ct + 8 * (r >> 2) + 4 * hf + (r & 3);
+        top2_add(t2[0], acc0[r], acc0[r], c);
+        top2_add(t2[1], acc1[r], acc1[r], c);
+      }
+    } else {  // columns past nb/2 take no part
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * ct + 8 * (r >> 2) + 4 * hf + (r & 3);
+        top2_add(t2[0], c < half ? acc0[r] : -INFINITY, c < half ? acc0[r] : INFINITY, c);
+        top2_add(t2[1], c < half ? acc1[r] : -INFINITY, c < half ? acc1[r] : INFINITY, c);
+      }
+    }
+    if (more)
+#pragma unroll
+      for (int i = 0; i < NP; ++i) rt[cb ^ 1][tid + kHashThreads * i] = __builtin_bit_cast(uint4, pf[i]);
+    __syncthreads();
+  }
+
+  unsigned long long need[2];
+  int bucket[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    Top2 &t = t2[n];
+    top2_merge_pair(t);
+    // top two of z = [p, -p]
+    float z1, z2;
+    int iz;
+    if (t.mx1 >= -t.mn1) {
+      z1 = t.mx1;
+      iz = t.imx;
+      z2 = fmaxf(t.mx2, -t.mn1);
+    } else {
+      z1 = -t.mn1;
+      iz = half + t.imn;
+      z2 = fmaxf(t.mx1, -t.mn2);
+    }
+    const float prod = xn[n] * rm;
+    const float err = kErr * prod + 0x1p-100f * xn[n];
+    const bool certified = prod < 1e37f && (z1 - z2) > 2.f * err + 0x1p-20f * (fabsf(z1) + fabsf(z2));
+    const bool valid = tok[n] < a.T && hf == 0;
+    bucket[n] = iz;
+    need[n] = __ballot(valid && !certified);
+    if (valid && certified) a.hash[(size_t)bh * a.T + tok[n]] = iz;
+  }
+  // uncertified tokens: append to the fallback list (one atomic per wave and tile)
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    if (need[n] == 0ull) continue;  // wave-uniform
+    int base = 0;
+    if (lane == 0) base = atomicAdd(a.fb_count, __popcll(need[n]));
+    base = __shfl(base, 0, 64);
+    const bool mine = (need[n] >> lane) & 1ull;
+    if (mine) a.fb_list[base + __popcll(need[n] & ((1ull << lane) - 1ull))] = bh * a.T + tok[n];
+  }
+  if (hist) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      if (tok[n] < a.T && hf == 0 && !((need[n] >> lane) & 1ull)) atomicAdd(&sh[bucket[n]], 1);
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.nb; i += kHashThreads) hist[((size_t)bh * a.nb + i) * nchunks + tb] = sh[i];
+  }
+}
+
+// Float64 buckets of the listed tokens, one wave per token, lanes over the R
+// columns: each lane loads its column of R (float32, widened exactly) in one
+// batch and accumulates the projection over the coordinates in increasing
+// order (as k_lsh_hash does), each coordinate of x broadcast by readlane;
+// first max of p and first min of p are reduced over the wave.  The chunk
+// histogram gets the token with an atomic add.  A fixed grid strides over the
+// list.  (Each listed token reads all of R[h] through L2; the list is short.)
+template <int D>
+__global__ __launch_bounds__(256) void k_lsh_fallback(LshArgs a, int32_t *hist, int nchunks) {
+  const int lane = threadIdx.x & 63;
+  const int gw = (int)((blockIdx.x * 256 + threadIdx.x) >> 6), nw = (int)(gridDim.x * 4);
+  const int n = *a.fb_count;
+  const int half = a.nb / 2;
+  for (int i = gw; i < n; i += nw) {
+    const int e = a.fb_list[i];
+    const int bh = e / a.T, t = e % a.T, h = bh % a.H;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x) + (size_t)e * D;
+    // the row, one coordinate per lane (two for D = 128)
+    const float x0 = bf16_bits_to_float(xr[lane]);
+    const float x1 = D > 64 ? bf16_bits_to_float(xr[(64 + lane) % D]) : 0.f;
+    double best = -INFINITY, worst = INFINITY;
+    int besti = 0, worsti = 0;
+    for (int c0 = 0; c0 < half; c0 += 64) {
+      const int c = c0 + lane;
+      const bool cv = c < half;
+      const float *rp = a.R + (size_t)h * D * half + (cv ? c : half - 1);  // column c of R[h], stride half
+      float rv[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) rv[k] = rp[(size_t)k * half];
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the dependent chain
+#endif
+      double acc = 0.0;
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        const float xk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k < 64 ? x0 : x1), k % 64));
+        acc = fma((double)xk, (double)rv[k], acc);
+      }
+      if (cv) {
+        if (acc > best) best = acc, besti = c;
+        if (acc < worst) worst = acc, worsti = c;
+      }
+    }
+    // first max / first min over the wave (lower index wins ties)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(best, o, 64), ow = __shfl_xor(worst, o, 64);
+      const int obi = __shfl_xor(besti, o, 64), owi = __shfl_xor(worsti, o, 64);
+      if (ob > best || (ob == best && obi < besti)) best = ob, besti = obi;
+      if (ow < worst || (ow == worst && owi < worsti)) worst = ow, worsti = owi;
+    }
+    const int bucket = best >= -worst ? besti : half + worsti;
+    if (lane == 0) {
+      a.hash[e] = bucket;
+      if (hist) atomicAdd(&hist[((size_t)bh * a.nb + bucket) * nchunks + t / kSortChunk], 1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One counting-sort pass.
 // ---------------------------------------------------------------------------
 struct SortPass {
@@ -234,6 +562,7 @@ struct SortPass {
   const int32_t *in_src;   // current order: source row of item (NULL => item index)
   int32_t *out_idx, *out_src, *out_hash;  // out_hash only on the bucket pass
   int32_t *hist;           // [BH, nbins, nchunks]
+  const int32_t *rowoff;   // [BH, nbins] digit offsets when hist holds per-row scans (two-level scan), else NULL
   int T, nbins, nbits, nchunks, shift, bucket_pass;
 };
 
@@ -334,6 +663,50 @@ __device__ __forceinline__ void copy_rows(const uint4 *x0_, uint4 *y0_, const ui
   }
 }
 
+// Two-level scan for long segments (nbins * nchunks entries per (b, h)).
+// First level: one work group per (b, h, digit) row; exclusive scan of the
+// row's chunk counts in place, row total to tot.
+__global__ __launch_bounds__(256) void k_sort_scan_rows(SortPass p, int32_t *tot) {
+  __shared__ int part[256];
+  int32_t *row = p.hist + (size_t)blockIdx.x * p.nchunks;
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < p.nchunks; base += 256) {
+    const int i = base + tid;
+    const int v = i < p.nchunks ? row[i] : 0;
+    part[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int u = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += u;
+      __syncthreads();
+    }
+    if (i < p.nchunks) row[i] = carry + part[tid] - v;
+    carry += part[255];
+    __syncthreads();
+  }
+  if (tid == 0) tot[blockIdx.x] = carry;
+}
+
+// Second level: per (b, h), exclusive scan of the row totals over the digits
+// (nbins <= 1024).
+__global__ __launch_bounds__(1024) void k_sort_scan_tot(SortPass p, const int32_t *tot, int32_t *rowoff) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const size_t base = (size_t)blockIdx.x * p.nbins;
+  const int v = tid < p.nbins ? tot[base + tid] : 0;
+  part[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int u = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += u;
+    __syncthreads();
+  }
+  if (tid < p.nbins) rowoff[base + tid] = part[tid] - v;
+}
+
 // Stable scatter of one 256-token chunk; wave w owns tokens 64w .. 64w+63.
 // P = rc.pieces (16-byte pieces per row).
 template <int P>
@@ -362,6 +735,7 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(SortPass p, RowCopy
   int slot = 0;
   if (valid) {
     slot = p.hist[((size_t)bh * p.nbins + digit) * p.nchunks + chunk] + rank;
+    if (p.rowoff) slot += p.rowoff[(size_t)bh * p.nbins + digit];
     for (int ww = 0; ww < w; ++ww) slot += cnt[ww * p.nbins + digit];
     p.out_idx[base + slot] = idx;
     p.out_src[base + slot] = src;
@@ -373,7 +747,10 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(SortPass p, RowCopy
   else if (rc.cs) copy_rows<P, false>(rc.cmp, rc.cs, nullptr, nullptr, base, src, dst_slot, lane);
 }
 
-static hipError_t run_pass(const SortPass &p, const RowCopy &rc, int BH, bool with_hist, hipStream_t s) {
+// Segments longer than this use the two-level scan.
+constexpr int kScanOneGroup = 32768;
+
+static hipError_t run_pass(SortPass p, const RowCopy &rc, int BH, bool with_hist, int32_t *scan_tmp, hipStream_t s) {
   const unsigned grid = (unsigned)(BH * p.nchunks);
   hipError_t e;
   if (with_hist) {
@@ -381,7 +758,17 @@ static hipError_t run_pass(const SortPass &p, const RowCopy &rc, int BH, bool wi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)BH), dim3(1024), 0, s, p);
+  if ((long long)p.nbins * p.nchunks > kScanOneGroup) {
+    int32_t *tot = scan_tmp, *rowoff = scan_tmp + (size_t)BH * p.nbins;
+    hipLaunchKernelGGL(k_sort_scan_rows, dim3((unsigned)(BH * p.nbins)), dim3(256), 0, s, p, tot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sort_scan_tot, dim3((unsigned)BH), dim3(1024), 0, s, p, tot, rowoff);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    p.rowoff = rowoff;
+  } else {
+    p.rowoff = nullptr;
+    hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)BH), dim3(1024), 0, s, p);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = 4 * p.nbins * sizeof(int);
@@ -398,13 +785,31 @@ hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
   const bool idx_passes = a.idx != nullptr && !a.idx_ascending;
   const unsigned hgrid = (unsigned)(BH * nchunks);
   int32_t *fused_hist = idx_passes ? nullptr : a.hist;
-  const int nr = a.H * a.d * lsh_r64_cols(a.nb);
-  hipLaunchKernelGGL(k_r_to_f64, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, a.R, a.R64, a.nb / 2,
-                     lsh_col_group(a.nb), a.d, nr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.d == 64) launch_hash<64>(a, a.R64, fused_hist, nchunks, hgrid, s);
-  else launch_hash<128>(a, a.R64, fused_hist, nchunks, hgrid, s);
+  hipError_t e;
+  if (a.dtype == 0) {
+    // bf16: matrix-core projection, certified; float64 for the rest
+    const int half = a.nb / 2, nct = lsh_col_tiles(a.nb);
+    const long long nsplit = (long long)a.H * nct * 3 * (a.d / 16) * 64 + (long long)a.H * half;
+    const unsigned sgrid = (unsigned)((nsplit + 255) / 256);
+    uint4 *Rf = static_cast<uint4 *>(a.Rf);
+    if (a.d == 64) hipLaunchKernelGGL(k_r_split<64>, dim3(sgrid), dim3(256), 0, s, a.R, Rf, a.colnorm, a.fb_count, a.H, half, nct);
+    else hipLaunchKernelGGL(k_r_split<128>, dim3(sgrid), dim3(256), 0, s, a.R, Rf, a.colnorm, a.fb_count, a.H, half, nct);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.d == 64) hipLaunchKernelGGL(k_lsh_mfma<64>, dim3(hgrid), dim3(kHashThreads), 0, s, a, Rf, a.colnorm, fused_hist, nchunks);
+    else hipLaunchKernelGGL(k_lsh_mfma<128>, dim3(hgrid), dim3(kHashThreads), 0, s, a, Rf, a.colnorm, fused_hist, nchunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const long long ntok = (long long)BH * a.T;
+    const unsigned fgrid = (unsigned)std::min<long long>(2048, (ntok + 3) / 4);
+    if (a.d == 64) hipLaunchKernelGGL(k_lsh_fallback<64>, dim3(fgrid), dim3(256), 0, s, a, fused_hist, nchunks);
+    else hipLaunchKernelGGL(k_lsh_fallback<128>, dim3(fgrid), dim3(256), 0, s, a, fused_hist, nchunks);
+  } else {
+    const int nr = a.H * a.d * lsh_r64_cols(a.nb);
+    hipLaunchKernelGGL(k_r_to_f64, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, a.R, a.R64, a.nb / 2,
+                       lsh_col_group(a.nb), a.d, nr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.d == 64) launch_hash<64>(a, a.R64, fused_hist, nchunks, hgrid, s);
+    else launch_hash<128>(a, a.R64, fused_hist, nchunks, hgrid, s);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -426,7 +831,7 @@ hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
       p.out_idx = a.tmp_idx[buf];
       p.out_src = a.tmp_src[buf];
       p.out_hash = nullptr;
-      e = run_pass(p, none, BH, true, s);
+      e = run_pass(p, none, BH, true, a.scan_tmp, s);
       if (e != hipSuccess) return e;
       p.in_idx = a.tmp_idx[buf];
       p.in_src = a.tmp_src[buf];
@@ -444,7 +849,7 @@ hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s) {
   RowCopy rc{static_cast<const uint4 *>(a.x), static_cast<uint4 *>(a.x_sorted),
              static_cast<const uint4 *>(a.companion), static_cast<uint4 *>(a.companion_sorted),
              a.d * (a.dtype == 1 ? 4 : 2) / 16};
-  return run_pass(p, rc, BH, idx_passes, s);
+  return run_pass(p, rc, BH, idx_passes, a.scan_tmp, s);
 }
 
 }  // namespace scfa

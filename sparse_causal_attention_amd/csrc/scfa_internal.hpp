@@ -70,7 +70,13 @@ struct LshArgs {
   int32_t *hist;            // [BH, nbins, nchunks]
   int32_t *tmp_idx[2];      // [BH, T] ping-pong (radix passes over idx)
   int32_t *tmp_src[2];
-  double *R64;              // [H, lsh_r64_cols(nb) / lsh_col_group(nb), d, lsh_col_group(nb)] float64 R
+  double *R64;              // [H, lsh_r64_cols(nb) / lsh_col_group(nb), d, lsh_col_group(nb)] float64 R (float32 inputs)
+  // matrix-core projection (bf16 inputs)
+  void *Rf;                 // [H, lsh_col_tiles(nb), 3, d/16, 64] uint4: R split into three bf16 terms
+  float *colnorm;           // [H, nb/2] upper bounds of the column 2-norms of R
+  int32_t *fb_count;        // tokens whose bucket the matrix-core pass could not certify
+  int32_t *fb_list;         // [BH * T] their indices (b*H + h) * T + t
+  int32_t *scan_tmp;        // [2, BH, nbins] row totals and digit offsets of the two-level scan
 };
 
 hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s);
@@ -96,5 +102,8 @@ inline int lsh_r64_cols(int nb) {
   const int g = lsh_col_group(nb);
   return (nb / 2 + g - 1) / g * g;
 }
+// Matrix-core projection: 32-column tiles of R and the bytes of its bf16 split.
+inline int lsh_col_tiles(int nb) { return (nb / 2 + 31) / 32; }
+inline size_t lsh_frag_bytes(int H, int d, int nb) { return (size_t)H * lsh_col_tiles(nb) * 3 * (d / 16) * 64 * 16; }
 
 }  // namespace scfa

@@ -111,7 +111,8 @@ def _lsh_case(seed, B, H, T, d, nb, dtype="bf16"):
 @pytest.mark.parametrize(
     "B,H,T,d,nb,dtype",
     [(1, 2, 1000, 64, 16, "bf16"), (2, 3, 4099, 64, 32, "bf16"), (1, 2, 9000, 128, 256, "bf16"),
-     (1, 1, 777, 64, 2, "fp32"), (1, 2, 3000, 128, 1024, "bf16"), (1, 1, 1, 64, 4, "bf16")],
+     (1, 1, 777, 64, 2, "fp32"), (1, 2, 3000, 128, 1024, "bf16"), (1, 1, 1, 64, 4, "bf16"),
+     (1, 1, 40000, 64, 256, "bf16"), (2, 1, 33000, 64, 512, "fp32")],  # the last two: two-level scan
 )
 def test_lsh_sort_bit_exact(B, H, T, d, nb, dtype):
     x, R = _lsh_case(B * 1000 + T, B, H, T, d, nb, dtype)
@@ -135,10 +136,35 @@ def test_lsh_sort_bit_exact(B, H, T, d, nb, dtype):
                                 torch.from_numpy(perm).long().cuda()])
 
 
-@pytest.mark.parametrize("ascending_flag", [False, True])
-def test_lsh_sort_with_given_positions(ascending_flag):
-    """Explicit positions: shuffled (five-pass sort) and ascending (one pass with the flag)."""
-    B, H, T, d, nb = 1, 2, 6000, 64, 8
+@pytest.mark.parametrize("d,nb,T", [(64, 16, 5000), (128, 256, 3000), (128, 8, 2000), (64, 64, 4097)])
+def test_lsh_near_ties_bit_exact(d, nb, T):
+    """R with exactly duplicated columns, columns one float32 ulp apart and a negated column:
+    many tokens' two best candidates tie or nearly tie, so the bf16 matrix-core projection
+    cannot decide them and the float64 recomputation must (first maximum, sequential sums)."""
+    H = 2
+    x, R = _lsh_case(77 + d + nb, 1, H, T, d, nb)
+    half = nb // 2
+    for c in range(1, half, 4):
+        R[:, :, c] = R[:, :, c - 1]  # exact ties
+    for c in range(2, half, 4):
+        R[:, :, c] = np.nextafter(R[:, :, c - 2], np.float32(np.inf))  # one ulp apart
+    if half >= 4:
+        R[:, :, 3] = -R[:, :, 0]  # p_3 = -p_0: ties between +p and -p candidates
+    note(f"[lsh near ties] d={d} nb={nb} T={T}")
+    hs, ids, perm, _, _ = _scfa().lsh_bucket_sort(dev(x, torch.bfloat16), dev(R), nb, want_x=False)
+    torch.cuda.synchronize()
+    for h in range(H):
+        bk = lsh.buckets_c(x[0, h], R[h])
+        p_ref, h_ref, i_ref = lsh.bucket_sort(bk, np.arange(T))
+        np.testing.assert_array_equal(perm[0, h].cpu().numpy(), p_ref)
+        np.testing.assert_array_equal(hs[0, h].cpu().numpy(), h_ref)
+
+
+@pytest.mark.parametrize("ascending_flag,T", [(False, 6000), (True, 6000), (False, 40000)])
+def test_lsh_sort_with_given_positions(ascending_flag, T):
+    """Explicit positions: shuffled (five-pass sort) and ascending (one pass with the flag);
+    at 40000 tokens the position passes use the two-level scan."""
+    B, H, d, nb = 1, 2, 64, 8
     x, R = _lsh_case(5, B, H, T, d, nb)
     rng = np.random.default_rng(6)
     pos = np.stack([np.sort(rng.choice(3 * T, T, replace=False)) for _ in range(H)]).astype(np.int32)[None]
@@ -146,7 +172,7 @@ def test_lsh_sort_with_given_positions(ascending_flag):
         sh = rng.permutation(T)
         pos = pos[..., sh]
         x = x[:, :, sh]
-    note(f"[lsh idx] ascending={ascending_flag}")
+    note(f"[lsh idx] ascending={ascending_flag} T={T}")
     hs, ids, perm, xs, _ = _scfa().lsh_bucket_sort(dev(x, torch.bfloat16), dev(R), nb, idx=dev(pos),
                                                     idx_ascending=ascending_flag)
     torch.cuda.synchronize()
