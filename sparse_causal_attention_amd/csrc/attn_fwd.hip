@@ -113,7 +113,7 @@ __device__ __forceinline__ void issue_kv(KVBuf<D> &b, const AttnArgs &a, const u
 constexpr float kRescaleLog2 = 8.f;
 
 template <int MODE, int D, int BS>
-__global__ __launch_bounds__(BS / 32 * 64) void k_fwd_bf16(AttnArgs a) {
+__global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) KVBuf<D> sb[2];
 
