@@ -150,6 +150,7 @@ def test_lsh_near_ties_bit_exact(d, nb, T):
         R[:, :, c] = np.nextafter(R[:, :, c - 2], np.float32(np.inf))  # one ulp apart
     if half >= 4:
         R[:, :, 3] = -R[:, :, 0]  # p_3 = -p_0: ties between +p and -p candidates
+    x[0, :, ::97] = 0.0  # all-zero rows: every candidate ties at 0, the first (bucket 0) wins
     note(f"[lsh near ties] d={d} nb={nb} T={T}")
     hs, ids, perm, _, _ = _scfa().lsh_bucket_sort(dev(x, torch.bfloat16), dev(R), nb, want_x=False)
     torch.cuda.synchronize()
@@ -158,6 +159,7 @@ def test_lsh_near_ties_bit_exact(d, nb, T):
         p_ref, h_ref, i_ref = lsh.bucket_sort(bk, np.arange(T))
         np.testing.assert_array_equal(perm[0, h].cpu().numpy(), p_ref)
         np.testing.assert_array_equal(hs[0, h].cpu().numpy(), h_ref)
+        assert (bk[::97] == 0).all()
 
 
 @pytest.mark.parametrize("ascending_flag,T", [(False, 6000), (True, 6000), (False, 40000)])
