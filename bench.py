@@ -80,16 +80,17 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(tile_rule):
+def measured_traffic(tile_rule, view):
     """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
-    (None too when the summary was taken with the other tile rule)."""
+    (None too when the summary was taken with the other tile rule or the other view of the rows)."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_digest") != kernel_source_digest() or kv.get("tile_rule") != tile_rule:
+    if (kv.get("source_digest") != kernel_source_digest() or kv.get("tile_rule") != tile_rule
+            or kv.get("rows") != view):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -160,26 +161,40 @@ class Timer:
         return sum(s) / len(s) if s else float("nan")
 
 
-def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True):
+def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False):
+    """One step.  By default the sorts return only bucket ids, positions and the permutations, and
+    the attention kernels read Q, dO, K and V through the permutations (row indirection); with
+    copy_sorted the sorts also copy the rows into sorted order and attention reads the copies.
+    Outputs (O, lse, dQ, dK, dV) are in sorted order either way, bit-identical."""
     nb, blk, sc = w.n_buckets, w.block, w.scale
     if timer:
         timer.begin()
-    qh, qi, _, qs, dos = scfa.lsh_bucket_sort(q, R, nb, companion=do)
+    if copy_sorted:
+        qh, qi, _, qs, dos = scfa.lsh_bucket_sort(q, R, nb, companion=do)
+    else:
+        qh, qi, qp, _, _ = scfa.lsh_bucket_sort(q, R, nb, want_x=False)
     if timer:
         timer.mark()
-    kh, ki, _, ks, vs = scfa.lsh_bucket_sort(k, R, nb, companion=v)
+    if copy_sorted:
+        kh, ki, _, ks, vs = scfa.lsh_bucket_sort(k, R, nb, companion=v)
+        rows = {}
+    else:
+        kh, ki, kp, _, _ = scfa.lsh_bucket_sort(k, R, nb, want_x=False)
+        qs, dos, ks, vs = q, do, k, v
+        rows = {"q_rows": qp, "k_rows": kp}
     if timer:
         timer.mark()
     meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=True, exact=exact)
     if timer:
         timer.mark()
-    o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc)
+    o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc, **rows)
     if timer:
         timer.mark()
-    dq, delta = scfa.attn_bwd_dq_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, block=blk, scale=sc)
+    dq, delta = scfa.attn_bwd_dq_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, block=blk, scale=sc, **rows)
     if timer:
         timer.mark()
-    dk, dv = scfa.attn_bwd_dkdv_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, block=blk, scale=sc)
+    dk, dv = scfa.attn_bwd_dkdv_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, block=blk, scale=sc,
+                                      **rows)
     if timer:
         timer.mark()
     return meta, (o, lse, dq, dk, dv)
@@ -381,7 +396,8 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, nbs, args):
         wn = dataclasses.replace(w, n_buckets=nb, name=f"{w.name.rsplit('_nb', 1)[0]}_nb{nb}")
         R = torch.from_numpy(np.stack([lsh_rotation(wn, h) for h in range(w.H)])).to("cuda:0")
         timer = Timer(torch, STEP_CALLS)
-        ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists),
+        ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists,
+                                                              args.copy_sorted),
                                     args.steps,
                                     args.warmup, timer)
         timer.collect()
@@ -405,6 +421,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-causal reference (short profiled runs)")
+    ap.add_argument("--copy-sorted", action="store_true",
+                    help="copy Q, dO, K, V into sorted order in the sorts (default: attention reads them through "
+                         "the sort permutations)")
     ap.add_argument("--range-lists", action="store_true",
                     help="build the tile lists with the bucket-range rule only (keep tiles that hold no valid pair)")
     ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
@@ -456,7 +475,7 @@ def main():
 
     _log("[bench] warmup")
     for _ in range(args.warmup):
-        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists)
+        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists, copy_sorted=args.copy_sorted)
     torch.cuda.synchronize()
 
     # HIP events between the calls, on the stream the kernels run on, inside the timed region
@@ -465,7 +484,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        meta, _ = run_step(scfa, w, q, k, v, do, R, timer, exact=not args.range_lists)
+        meta, _ = run_step(scfa, w, q, k, v, do, R, timer, exact=not args.range_lists, copy_sorted=args.copy_sorted)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -505,14 +524,16 @@ def main():
     dominant = max(kernel_flops, key=lambda n: per_call[n])
     achieved = kernel_flops[dominant] / (per_call[dominant] * 1e-3) / 1e12
     roofline = {
-        "kernel": {"fwd": "k_fwd_bf16<kHash,64,64>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64>",
-                   "bwd_dkdv": "k_bwd_dkdv_bf16<kHash,64,64>"}[dominant],
+        "kernel": {"fwd": "k_fwd_bf16<kHash,64,64,%s>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64,%s>",
+                   "bwd_dkdv": "k_bwd_dkdv_bf16<kHash,64,64,%s>"}[dominant] % (
+                       "false" if args.copy_sorted else "true"),
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": measured_traffic("range" if args.range_lists else "exact") if dominant == "bwd_dkdv" else None,
+        "traffic": (measured_traffic("range" if args.range_lists else "exact", "copied" if args.copy_sorted else
+                                     "permuted") if dominant == "bwd_dkdv" else None),
         "avg_launch_ms": per_call[dominant],
         "algorithmic_flops_per_launch": kernel_flops[dominant],
     }
@@ -543,8 +564,10 @@ def main():
             "d": w.d,
             "block": w.block,
             "n_buckets": w.n_buckets,
-            "step": "lsh+sort(Q,dO) + lsh+sort(K,V) + block lists + fwd + bwd",
+            "step": ("lsh+sort(Q,dO) + lsh+sort(K,V) + block lists + fwd + bwd" if args.copy_sorted else
+                     "lsh+sort(Q) + lsh+sort(K) + block lists + fwd + bwd, rows read through the sort permutations"),
             "tile_rule": "range" if args.range_lists else "exact",
+            "rows": "copied" if args.copy_sorted else "permuted",
         },
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "executed_tiles": tiles,

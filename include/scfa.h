@@ -247,11 +247,22 @@ int scfa_block_meta_exact(const int32_t *q_idx, const int32_t *k_idx,
  *   row_count/row_list and col_count/col_list must be scfa_block_meta's output
  *   for the same positions, buckets and block (list entries naming a block
  *   outside the sequence are skipped, never dereferenced).
+ *   Row indirection (bf16 only; both NULL = none): q_rows [B,H,Tq] and k_rows
+ *   [B,H,Tk] int32 make row i of the attention's Q (and of dout) row
+ *   q_rows[b,h,i] of q (dout), and row j of its K and V row k_rows[b,h,j] of
+ *   k and v, so a caller can attend over a reordered view (the sort
+ *   permutation of scfa_lsh_bucket_sort) without copying Q, K, V and dO into
+ *   that order.  Positions, buckets, lse, o (the forward's output, read by
+ *   the dq call), delta and every output stay indexed by the view's rows i
+ *   and j.  Indices are clamped into [0, Tq) / [0, Tk) on the device (an
+ *   index out of range reads a wrong row, never outside the tensor).  fp32
+ *   with row indirection is SCFA_ERR_UNSUPPORTED.
  *   Other arguments, layouts and flags as in scfa_*_sparse_fwd / _bwd.
  */
 int scfa_attn_fwd_lists(const void *q, const void *k, const void *v,
                         const int32_t *q_idx, const int32_t *k_idx,
                         const int32_t *q_hash, const int32_t *k_hash,
+                        const int32_t *q_rows, const int32_t *k_rows,
                         const int32_t *row_count, const int32_t *row_list,
                         void *o, float *lse,
                         int B, int H, int Tq, int Tk, int d, int block, float scale,
@@ -264,6 +275,7 @@ int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v,
                            const void *o, const float *lse, const void *dout,
                            const int32_t *q_idx, const int32_t *k_idx,
                            const int32_t *q_hash, const int32_t *k_hash,
+                           const int32_t *q_rows, const int32_t *k_rows,
                            const int32_t *row_count, const int32_t *row_list,
                            void *dq, float *delta,
                            int B, int H, int Tq, int Tk, int d, int block, float scale,
@@ -276,6 +288,7 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
                              const float *lse, const void *dout, const float *delta,
                              const int32_t *q_idx, const int32_t *k_idx,
                              const int32_t *q_hash, const int32_t *k_hash,
+                             const int32_t *q_rows, const int32_t *k_rows,
                              const int32_t *col_count, const int32_t *col_list,
                              void *dk, void *dv,
                              int B, int H, int Tq, int Tk, int d, int block, float scale,

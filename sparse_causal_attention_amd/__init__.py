@@ -243,10 +243,20 @@ def _list_args(meta, key_cnt, key_list):
     return meta[key_cnt], meta[key_list]
 
 
-def attn_fwd_lists(q, k, v, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0, out=None):
+def _rows_args(q_rows, k_rows, q, k):
+    B, H, Tq = q.shape[:3]
+    _need(q_rows, "q_rows", torch.int32, (B, H, Tq))
+    _need(k_rows, "k_rows", torch.int32, (B, H, k.shape[2]))
+    return _ptr(q_rows), _ptr(k_rows)
+
+
+def attn_fwd_lists(q, k, v, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0, out=None,
+                   q_rows=None, k_rows=None):
     """Forward over lists from ``block_meta`` (one kernel).  Positions None = dense causal.
 
-    ``out`` optionally supplies preallocated (o, lse).
+    ``out`` optionally supplies preallocated (o, lse).  ``q_rows`` / ``k_rows`` (int32 [B,H,T]) make
+    row i of the attention's Q row q_rows[i] of q and row j of K, V row k_rows[j] of k, v (a
+    reordered view without copies; outputs indexed by the view's rows).
     """
     B, H, Tq, Tk, d = _attn_shapes(q, k, v)
     if scale is None:
@@ -255,14 +265,14 @@ def attn_fwd_lists(q, k, v, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, sca
                                           torch.empty((B, H, Tq), dtype=torch.float32, device=q.device))
     rc_, rl_ = _list_args(meta, "row_count", "row_list")
     rc = _LIB.scfa_attn_fwd_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
-                                  _ptr(rc_), _ptr(rl_), _ptr(o), _ptr(lse), B, H, Tq, Tk, d, block, float(scale),
-                                  _dtype_code(q), int(flags), _stream())
+                                  *_rows_args(q_rows, k_rows, q, k), _ptr(rc_), _ptr(rl_), _ptr(o), _ptr(lse), B, H,
+                                  Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_fwd_lists", rc)
     return o, lse
 
 
 def attn_bwd_dq_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0,
-                      out=None):
+                      out=None, q_rows=None, k_rows=None):
     """dQ over row lists (one kernel).  Returns (dq, delta) with delta [2,B,H,Tq] float32 scratch
     (rowsum(dout * o), lse * log2 e) for attn_bwd_dkdv_lists."""
     B, H, Tq, Tk, d = _attn_shapes(q, k, v)
@@ -272,15 +282,15 @@ def attn_bwd_dq_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta,
                                              torch.empty((2, B, H, Tq), dtype=torch.float32, device=q.device))
     rc_, rl_ = _list_args(meta, "row_count", "row_list")
     rc = _LIB.scfa_attn_bwd_dq_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_idx),
-                                     _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), _ptr(rc_), _ptr(rl_), _ptr(dq),
-                                     _ptr(delta), B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags),
-                                     _stream())
+                                     _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, q, k),
+                                     _ptr(rc_), _ptr(rl_), _ptr(dq), _ptr(delta), B, H, Tq, Tk, d, block, float(scale),
+                                     _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_bwd_dq_lists", rc)
     return dq, delta
 
 
 def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None,
-                        flags=0, out=None):
+                        flags=0, out=None, q_rows=None, k_rows=None):
     """dK and dV over column lists (one kernel), reading delta from attn_bwd_dq_lists."""
     B, H, Tq, Tk, d = _attn_shapes(q, k, v)
     if scale is None:
@@ -288,9 +298,9 @@ def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash,
     dk, dv = out if out is not None else (torch.empty_like(k), torch.empty_like(v))
     cc_, cl_ = _list_args(meta, "col_count", "col_list")
     rc = _LIB.scfa_attn_bwd_dkdv_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta), _ptr(q_idx),
-                                       _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), _ptr(cc_), _ptr(cl_), _ptr(dk),
-                                       _ptr(dv), B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags),
-                                       _stream())
+                                       _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, q, k),
+                                       _ptr(cc_), _ptr(cl_), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, block,
+                                       float(scale), _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_bwd_dkdv_lists", rc)
     return dk, dv
 

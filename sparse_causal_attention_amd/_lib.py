@@ -68,9 +68,9 @@ _SIGNATURES = {
     "scfa_lsh_bucket_sort": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_block_meta": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p],
     "scfa_block_meta_exact": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p],
-    "scfa_attn_fwd_lists": [_p] * 11 + _LISTS_TAIL,
-    "scfa_attn_bwd_dq_lists": [_p] * 14 + _LISTS_TAIL,
-    "scfa_attn_bwd_dkdv_lists": [_p] * 14 + _LISTS_TAIL,
+    "scfa_attn_fwd_lists": [_p] * 13 + _LISTS_TAIL,
+    "scfa_attn_bwd_dq_lists": [_p] * 16 + _LISTS_TAIL,
+    "scfa_attn_bwd_dkdv_lists": [_p] * 16 + _LISTS_TAIL,
     "scfa_gather_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p],
     "scfa_scatter_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p],
     "scfa_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],

@@ -106,6 +106,7 @@ struct AttnCall {
   const void *dout;
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
   const int32_t *row_cnt, *row_list, *col_cnt, *col_list;  // list entry points only
+  const int32_t *q_rows, *k_rows;                          // list entry points only (nullable)
   void *out_o;
   float *out_lse;
   void *dq, *dk, *dv;
@@ -167,6 +168,13 @@ int attention(const AttnCall &c) {
         return rc;
       break;
   }
+  if (c.q_rows || c.k_rows) {
+    if (s.dtype != SCFA_DTYPE_BF16)
+      return fail(SCFA_ERR_UNSUPPORTED, "q_rows / k_rows (row indirection) need dtype bf16");
+    if ((rc = check_ptr(c.q_rows, c.q_rows ? nQi : 0, 4, "q_rows")) ||
+        (rc = check_ptr(c.k_rows, c.k_rows ? nKi : 0, 4, "k_rows")))
+      return rc;
+  }
   const bool no_prune = (c.flags & SCFA_FLAG_NO_PRUNE) != 0;
   // lists (list entry points) or workspace (the others)
   if (c.api == kApiLists) {
@@ -202,6 +210,8 @@ int attention(const AttnCall &c) {
   a.k_idx = c.k_idx;
   a.q_hash = hashed ? c.q_hash : nullptr;
   a.k_hash = hashed ? c.k_hash : nullptr;
+  a.q_rows = c.q_rows;
+  a.k_rows = c.k_rows;
   a.BH = (int)BH;
   a.Tq = s.Tq;
   a.Tk = s.Tk;
@@ -417,13 +427,14 @@ int scfa_hash_sparse_bwd(const void *q, const void *k, const void *v, const void
 }
 
 int scfa_attn_fwd_lists(const void *q, const void *k, const void *v, const int32_t *q_idx, const int32_t *k_idx,
-                        const int32_t *q_hash, const int32_t *k_hash, const int32_t *row_count,
-                        const int32_t *row_list, void *o, float *lse, int B, int H, int Tq, int Tk, int d, int block,
-                        float scale, int dtype, unsigned flags, void *stream) {
+                        const int32_t *q_hash, const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                        const int32_t *row_count, const int32_t *row_list, void *o, float *lse, int B, int H, int Tq,
+                        int Tk, int d, int block, float scale, int dtype, unsigned flags, void *stream) {
   AttnCall c{};
   c.kind = kFwd;
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.q_rows = q_rows, c.k_rows = k_rows;
   c.row_cnt = row_count, c.row_list = row_list, c.out_o = o, c.out_lse = lse;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;
@@ -432,14 +443,15 @@ int scfa_attn_fwd_lists(const void *q, const void *k, const void *v, const int32
 
 int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v, const void *o, const float *lse,
                            const void *dout, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
-                           const int32_t *k_hash, const int32_t *row_count, const int32_t *row_list, void *dq,
-                           float *delta, int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype,
-                           unsigned flags, void *stream) {
+                           const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                           const int32_t *row_count, const int32_t *row_list, void *dq, float *delta, int B, int H,
+                           int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags, void *stream) {
   AttnCall c{};
   c.kind = kBwdDq;
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.q_rows = q_rows, c.k_rows = k_rows;
   c.row_cnt = row_count, c.row_list = row_list, c.dq = dq, c.delta = delta;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;
@@ -448,14 +460,15 @@ int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v, const vo
 
 int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v, const float *lse, const void *dout,
                              const float *delta, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
-                             const int32_t *k_hash, const int32_t *col_count, const int32_t *col_list, void *dk,
-                             void *dv, int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype,
-                             unsigned flags, void *stream) {
+                             const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                             const int32_t *col_count, const int32_t *col_list, void *dk, void *dv, int B, int H,
+                             int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags, void *stream) {
   AttnCall c{};
   c.kind = kBwdDkdv;
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.lse = lse, c.dout = dout, c.delta = const_cast<float *>(delta);
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.q_rows = q_rows, c.k_rows = k_rows;
   c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;

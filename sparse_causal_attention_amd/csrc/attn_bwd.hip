@@ -141,7 +141,9 @@ struct QGBuf {
 // ---------------------------------------------------------------------------
 // bf16 dQ (+ D, lse*log2 e) kernel.  Lanes own query columns.
 // ---------------------------------------------------------------------------
-template <int MODE, int D, int BS>
+// KROWS: K and V chunk rows come through a.k_rows (indices loaded one chunk
+// ahead); Q and dO rows come through a.q_rows when it is set.
+template <int MODE, int D, int BS, bool KROWS>
 __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_bwd_dq_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) KVBufB<D> sb[2];
@@ -163,9 +165,16 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const List rl = row_list_b<MODE, BS>(a, bh, qb);
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
+  const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
+  DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
   auto issue = [&](KVBufB<D> &b, const Chunk &c) {
-    dma_matrix<D, NW>(b.k, K, c.r0, c.nvalid, dmo);
-    dma_matrix<D, NW>(b.v, V, c.r0, c.nvalid, dmo);
+    if constexpr (KROWS) {
+      dma_matrix_rows<D, NW>(b.k, K, a.Tk, drn);
+      dma_matrix_rows<D, NW>(b.v, V, a.Tk, drn);
+    } else {
+      dma_matrix<D, NW>(b.k, K, c.r0, c.nvalid, dmo);
+      dma_matrix<D, NW>(b.v, V, c.r0, c.nvalid, dmo);
+    }
     if (MODE != kDense && !(c.free && c.nvalid == kChunk)) {
       if (w == 0) dma_vec(b.idx, a.k_idx + (size_t)bh * a.Tk, c.r0, c.nvalid);
       if (MODE == kHash && w == NW - 1) dma_vec(b.hash, a.k_hash + (size_t)bh * a.Tk, c.r0, c.nvalid);
@@ -173,16 +182,27 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   };
   Chunk cur;
   bool have = next_chunk<MODE, BS, true>(a, rl, qb, 0, 0, cur);
-  if (have) issue(sb[0], cur);
+  if (have) {
+    if constexpr (KROWS) dma_rows_load<D, NW>(drn, krows, cur.r0, cur.nvalid);
+    issue(sb[0], cur);
+  }
+  Chunk nxt;  // KROWS: looked up one chunk ahead, so its row indices can load early
+  bool have_next = false;
+  if constexpr (KROWS) {
+    have_next = have && next_chunk<MODE, BS, true>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.r0, nxt.nvalid);
+  }
 
+  const int qsrc = a.q_rows && qvalid ? min(max(a.q_rows[qoff + qrow], 0), a.Tq - 1) : qrow;
   bf16x8 qf[D / 16], dof[D / 16];
   float dsum = 0.f;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const size_t off = (size_t)qrow * D + 16 * kk + 8 * half;
+    const size_t soff = (size_t)qsrc * D + 16 * kk + 8 * half;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 uq = qvalid ? ld16(Q + off) : z;
-    const uint4 ud = qvalid ? ld16(dO + off) : z;
+    const uint4 uq = qvalid ? ld16(Q + soff) : z;
+    const uint4 ud = qvalid ? ld16(dO + soff) : z;
     const uint4 uo = qvalid ? ld16(O + off) : z;
     qf[kk] = as_bf16x8(uq);
     dof[kk] = as_bf16x8(ud);
@@ -214,11 +234,15 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
 
   int buf = 0;
   while (have) {
-    Chunk nxt;
-    const bool have_next = next_chunk<MODE, BS, true>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    Chunk nxt2;
+    bool have_next2 = false;
+    if constexpr (KROWS) have_next2 = have_next && next_chunk<MODE, BS, true>(a, rl, qb, nxt.t, nxt.ch + 1, nxt2);
+    else have_next = next_chunk<MODE, BS, true>(a, rl, qb, cur.t, cur.ch + 1, nxt);
     wait_vmem();
     __syncthreads();
     if (have_next) issue(sb[buf ^ 1], nxt);
+    if constexpr (KROWS)
+      if (have_next2) dma_rows_load<D, NW>(drn, krows, nxt2.r0, nxt2.nvalid);
     const KVBufB<D> &b = sb[buf];
 
     // Fragments first, then four independent accumulator chains (S^T and
@@ -275,6 +299,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     buf ^= 1;
     cur = nxt;
     have = have_next;
+    if constexpr (KROWS) {
+      nxt = nxt2;
+      have_next = have_next2;
+    }
   }
 
   if (qvalid) {
@@ -294,7 +322,9 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
 // ---------------------------------------------------------------------------
 // bf16 dK / dV kernel.  Lanes own key columns.
 // ---------------------------------------------------------------------------
-template <int MODE, int D, int BS>
+// QROWS: Q and dO chunk rows come through a.q_rows (indices loaded one chunk
+// ahead); K and V rows come through a.k_rows when it is set.
+template <int MODE, int D, int BS, bool QROWS>
 __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_bwd_dkdv_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) QGBuf<D> sb[2];
@@ -318,9 +348,16 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const List cl = col_list_b<MODE, BS>(a, bh, kb);
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
+  const int32_t *qrows = QROWS ? a.q_rows + qoff : nullptr;
+  DmaRows<D, NW> drn;  // QROWS: source rows of the next chunk to copy
   auto issue = [&](QGBuf<D> &b, const Chunk &c) {
-    dma_matrix<D, NW>(b.q, Q, c.r0, c.nvalid, dmo);
-    dma_matrix<D, NW>(b.g, dO, c.r0, c.nvalid, dmo);
+    if constexpr (QROWS) {
+      dma_matrix_rows<D, NW>(b.q, Q, a.Tq, drn);
+      dma_matrix_rows<D, NW>(b.g, dO, a.Tq, drn);
+    } else {
+      dma_matrix<D, NW>(b.q, Q, c.r0, c.nvalid, dmo);
+      dma_matrix<D, NW>(b.g, dO, c.r0, c.nvalid, dmo);
+    }
     if (w == 0) dma_vec(b.lse2, lse2g, c.r0, c.nvalid);
     if (w == NW - 1) dma_vec(b.del, delg, c.r0, c.nvalid);
     if (MODE != kDense && !(c.free && c.nvalid == kChunk)) {
@@ -330,12 +367,22 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   };
   Chunk cur;
   bool have = next_chunk<MODE, BS, false>(a, cl, kb, 0, 0, cur);
-  if (have) issue(sb[0], cur);
+  if (have) {
+    if constexpr (QROWS) dma_rows_load<D, NW>(drn, qrows, cur.r0, cur.nvalid);
+    issue(sb[0], cur);
+  }
+  Chunk nxt;  // QROWS: looked up one chunk ahead, so its row indices can load early
+  bool have_next = false;
+  if constexpr (QROWS) {
+    have_next = have && next_chunk<MODE, BS, false>(a, cl, kb, cur.t, cur.ch + 1, nxt);
+    if (have_next) dma_rows_load<D, NW>(drn, qrows, nxt.r0, nxt.nvalid);
+  }
 
+  const int ksrc = a.k_rows && kvalid_row ? min(max(a.k_rows[koff + krow], 0), a.Tk - 1) : krow;
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const size_t off = (size_t)krow * D + 16 * kk + 8 * half;
+    const size_t off = (size_t)ksrc * D + 16 * kk + 8 * half;
     kf[kk] = as_bf16x8(kvalid_row ? ld16(K + off) : make_uint4(0, 0, 0, 0));
     vf[kk] = as_bf16x8(kvalid_row ? ld16(V + off) : make_uint4(0, 0, 0, 0));
   }
@@ -356,11 +403,15 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
 
   int buf = 0;
   while (have) {
-    Chunk nxt;
-    const bool have_next = next_chunk<MODE, BS, false>(a, cl, kb, cur.t, cur.ch + 1, nxt);
+    Chunk nxt2;
+    bool have_next2 = false;
+    if constexpr (QROWS) have_next2 = have_next && next_chunk<MODE, BS, false>(a, cl, kb, nxt.t, nxt.ch + 1, nxt2);
+    else have_next = next_chunk<MODE, BS, false>(a, cl, kb, cur.t, cur.ch + 1, nxt);
     wait_vmem();
     __syncthreads();
     if (have_next) issue(sb[buf ^ 1], nxt);
+    if constexpr (QROWS)
+      if (have_next2) dma_rows_load<D, NW>(drn, qrows, nxt2.r0, nxt2.nvalid);
     const QGBuf<D> &b = sb[buf];
     // Key rows past Tk only pollute their own (never stored) columns, so a
     // mask-free tile needs masking only for query rows past Tq.
@@ -428,6 +479,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     buf ^= 1;
     cur = nxt;
     have = have_next;
+    if constexpr (QROWS) {
+      nxt = nxt2;
+      have_next = have_next2;
+    }
   }
 
   if (kvalid_row) {
@@ -616,12 +671,18 @@ __global__ __launch_bounds__(BS) void k_bwd_dkdv_f32(AttnArgs a) {
 template <int MODE, int D, int BS>
 static hipError_t run_bwd_bf16(const AttnArgs &a, int part, hipStream_t s) {
   if ((part & 1) && a.nq > 0) {
-    hipLaunchKernelGGL((k_bwd_dq_bf16<MODE, D, BS>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
+    if (a.k_rows)
+      hipLaunchKernelGGL((k_bwd_dq_bf16<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_dq_bf16<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((part & 2) && a.nk > 0) {
-    hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0, s, a);
+    if (a.q_rows)
+      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

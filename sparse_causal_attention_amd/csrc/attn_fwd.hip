@@ -112,7 +112,22 @@ __device__ __forceinline__ void issue_kv(KVBuf<D> &b, const AttnArgs &a, const u
 // max is only raised when a score exceeds it by more than this, so P <= 2^8.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int MODE, int D, int BS>
+template <int MODE, int D, int NW>
+__device__ __forceinline__ void issue_kv_rows(KVBuf<D> &b, const AttnArgs &a, const uint16_t *K, const uint16_t *V,
+                                              int bh, const ChunkPos &c, const DmaRows<D, NW> &dr) {
+  dma_matrix_rows<D, NW>(b.k, K, a.Tk, dr);
+  dma_matrix_rows<D, NW>(b.v, V, a.Tk, dr);
+  if (MODE != kDense && !(c.free && c.kvalid == kChunk)) {
+    const int w = threadIdx.x >> 6;
+    if (w == 0) dma_vec(b.idx, a.k_idx + (size_t)bh * a.Tk, c.k0, c.kvalid);
+    if (MODE == kHash && w == NW - 1) dma_vec(b.hash, a.k_hash + (size_t)bh * a.Tk, c.k0, c.kvalid);
+  }
+}
+
+// KROWS: K and V rows come through a.k_rows (the chunk copies read row
+// k_rows[j] for chunk row j; the next chunk's indices are loaded one chunk
+// ahead).  Q rows come through a.q_rows when it is set.
+template <int MODE, int D, int BS, bool KROWS>
 __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) KVBuf<D> sb[2];
@@ -130,15 +145,31 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   const RowList rl = row_list<MODE, BS>(a, bh, qb);
   const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
+  const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   ChunkPos cur;
   bool have = find_chunk<MODE, BS>(a, rl, qb, 0, 0, cur);
-  if (have) issue_kv<MODE, D, NW>(sb[0], a, K, V, bh, cur, dof);
+  DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
+  if (have) {
+    if constexpr (KROWS) {
+      dma_rows_load<D, NW>(drn, krows, cur.k0, cur.kvalid);
+      issue_kv_rows<MODE, D, NW>(sb[0], a, K, V, bh, cur, drn);
+    } else {
+      issue_kv<MODE, D, NW>(sb[0], a, K, V, bh, cur, dof);
+    }
+  }
+  ChunkPos nxt;  // KROWS: looked up one chunk ahead, so its row indices can load early
+  bool have_next = false;
+  if constexpr (KROWS) {
+    have_next = have && find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.k0, nxt.kvalid);
+  }
   const LaneOffsets<D> lo = lane_offsets<D>();
 
+  const int qsrc = a.q_rows && qvalid ? min(max(a.q_rows[(size_t)bh * a.Tq + qrow], 0), a.Tq - 1) : qrow;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    qf[kk] = as_bf16x8(qvalid ? ld16(Q + (size_t)qrow * D + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0));
+    qf[kk] = as_bf16x8(qvalid ? ld16(Q + (size_t)qsrc * D + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0));
   int my_idx = kIdxTailQ, my_hash = 0;
   if (qvalid) {
     my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
@@ -155,11 +186,18 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   int buf = 0;
   while (have) {
-    ChunkPos nxt;
-    const bool have_next = find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    ChunkPos nxt2;
+    bool have_next2 = false;
+    if constexpr (KROWS) have_next2 = have_next && find_chunk<MODE, BS>(a, rl, qb, nxt.t, nxt.ch + 1, nxt2);
+    else have_next = find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
     wait_vmem();
     __syncthreads();
-    if (have_next) issue_kv<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, dof);
+    if (have_next) {
+      if constexpr (KROWS) issue_kv_rows<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, drn);
+      else issue_kv<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, dof);
+    }
+    if constexpr (KROWS)
+      if (have_next2) dma_rows_load<D, NW>(drn, krows, nxt2.k0, nxt2.kvalid);
     const KVBuf<D> &b = sb[buf];
 
     // All K fragments of the chunk are requested first, then the two
@@ -230,6 +268,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)
     buf ^= 1;
     cur = nxt;
     have = have_next;
+    if constexpr (KROWS) {
+      nxt = nxt2;
+      have_next = have_next2;
+    }
   }
 
   const float lt = pair_sum(l);
@@ -338,7 +380,10 @@ __global__ __launch_bounds__(BS) void k_fwd_f32(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
 static hipError_t run_fwd_bf16(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_fwd_bf16<MODE, D, BS>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
+  if (a.k_rows)
+    hipLaunchKernelGGL((k_fwd_bf16<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_fwd_bf16<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
   return hipGetLastError();
 }
 template <int MODE, int D, int BS>

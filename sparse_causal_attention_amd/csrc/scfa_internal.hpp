@@ -23,6 +23,9 @@ struct AttnArgs {
   float *delta;  // backward scratch [BH, Tq]: rowsum(dO * O)
   // positions / buckets [BH, T] (idx NULL => dense causal)
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
+  // optional row indirection [BH, T]: row i of Q (dO) is row q_rows[i] of q (dout), row j of K, V is
+  // row k_rows[j] of k, v (NULL = identity); outputs stay indexed by i and j
+  const int32_t *q_rows, *k_rows;
   // live-tile lists (NULL in dense mode)
   const int32_t *row_cnt, *row_list;  // [BH, nq], [BH, nq, nk]
   const int32_t *col_cnt, *col_list;  // [BH, nk], [BH, nk, nq]

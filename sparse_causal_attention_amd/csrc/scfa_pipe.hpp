@@ -117,6 +117,47 @@ __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, 
   }
 }
 
+// Row indirection: the source rows this lane copies in each of its DMA
+// instructions for one chunk, read from rows[row0 ..] (tail rows repeat the
+// last real one).  Loaded one chunk ahead of the copy that uses them;
+// dma_matrix_rows clamps them into [0, T) so a bad index cannot leave the
+// head's matrix.
+template <int D, int NW>
+struct DmaRows {
+  int row[DmaOffsets<D, NW>::PER_WAVE];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void dma_rows_load(DmaRows<D, NW> &dr, const int32_t *rows, int row0, int nvalid) {
+  using O = DmaOffsets<D, NW>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < O::PER_WAVE; ++k) {
+    const int i = k * NW + w;
+    const int r = (i * 64 + lane) / O::CPR;
+    dr.row[k] = rows[row0 + min(r, nvalid - 1)];
+  }
+}
+
+// dma_matrix through the row indirection: g is the head's matrix base.
+template <int D, int NW>
+__device__ __forceinline__ void dma_matrix_rows(MatChunk<D> &dst, const uint16_t *g, int T, const DmaRows<D, NW> &dr) {
+  using O = DmaOffsets<D, NW>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < O::PER_WAVE; ++k) {
+    const int i = k * NW + w;
+    if (O::NINST % NW == 0 || i < O::NINST) {
+      const int s = i * 64 + lane;
+      const int r = s / O::CPR, p = s % O::CPR;
+      const int src = min(max(dr.row[k], 0), T - 1);
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_global_load_lds(g + (size_t)src * D + ((p ^ (r & 7)) << 3), to_lds(dst.v + i * 512), 16, 0, 0);
+#endif
+    }
+  }
+}
+
 // Copy 64 consecutive 4-byte values (clamped like dma_matrix) with one wave.
 __device__ __forceinline__ void dma_vec(void *dst, const void *g, int row0, int nvalid) {
   const int lane = threadIdx.x & 63;

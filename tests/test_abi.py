@@ -142,6 +142,20 @@ def test_block_meta_exact_validation():
         _lib.ERR_UNSUPPORTED
 
 
+def test_row_indirection_validation():
+    lib = _lib.load()
+
+    def fwd(q_rows=None, k_rows=None, dtype=0):
+        return lib.scfa_attn_fwd_lists(P, P, P, P2, P2, None, None, q_rows, k_rows, P2, P2, P, P2, 1, 1, 100, 100,
+                                       64, 64, 0.125, dtype, 0, None)
+
+    assert fwd(q_rows=P2 + 2) == _lib.ERR_INVALID_ARGUMENT  # 4-byte alignment
+    assert fwd(k_rows=P2 + 1) == _lib.ERR_INVALID_ARGUMENT
+    assert fwd(q_rows=P2, dtype=1) == _lib.ERR_UNSUPPORTED  # bf16 only
+    assert lib.scfa_attn_bwd_dkdv_lists(P, P, P, P2, P, P2, P2, P2, None, None, None, P2 + 3, P2, P2, P, P, 1, 1,
+                                        100, 100, 64, 64, 0.125, 0, 0, None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_workspace_sizes():
     lib = _lib.load()
     ws = lib.scfa_workspace_size

@@ -246,3 +246,43 @@ def test_exact_lists_are_bit_identical(dtype):
     torch.cuda.synchronize()
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode,d,block,Tq,Tk", [("hash", 64, 64, 1500, 1400), ("qk", 64, 64, 777, 1000),
+                                                ("dense", 64, 64, 650, 650), ("hash", 128, 128, 1300, 1300),
+                                                ("hash", 128, 64, 500, 450)])
+def test_row_indirection_bit_identical(mode, d, block, Tq, Tk):
+    """Attention over a permuted view (q_rows / k_rows) equals attention over the gathered copies bit
+    for bit, for the forward and both backward kernels; indices out of range behave as clamped."""
+    scfa = _lib()
+    c = synthetic_case(51, B=2, H=2, Tq=Tq, Tk=Tk, d=d, dtype="bf16", mode="hash" if mode == "hash" else "qk",
+                       nb=5, layout="grouped")
+    note(f"[row indirection] {mode} d={d} block={block} Tq={Tq} Tk={Tk}")
+    q, k, v, do = (dev(x).to(torch.bfloat16) for x in (c.q, c.k, c.v, c.do))
+    if mode == "dense":
+        qi = ki = qh = kh = None
+    else:
+        qi, ki = dev(c.q_idx), dev(c.k_idx)
+        qh, kh = (dev(c.q_hash), dev(c.k_hash)) if mode == "hash" else (None, None)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(9)
+    qr = torch.stack([torch.stack([torch.randperm(Tq, generator=g, device="cuda:0") for _ in range(2)])
+                      for _ in range(2)]).to(torch.int32)
+    kr = torch.stack([torch.stack([torch.randperm(Tk, generator=g, device="cuda:0") for _ in range(2)])
+                      for _ in range(2)]).to(torch.int32)
+    qr[0, 0, 3], kr[1, 1, 5] = -7, Tk + 11  # out of range: clamped on the device
+    gather = lambda x, r, T: torch.gather(  # noqa: E731
+        x, 2, r.clamp(0, T - 1).long()[..., None].expand(-1, -1, -1, x.shape[-1]).contiguous())
+    qs, dos = gather(q, qr, Tq), gather(do, qr, Tq)
+    ks, vs = gather(k, kr, Tk), gather(v, kr, Tk)
+    meta = None if mode == "dense" else scfa.block_meta(qi, ki, qh, kh, block=block, with_cols=True, exact=True)
+    o1, l1 = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=block)
+    dq1, de1 = scfa.attn_bwd_dq_lists(qs, ks, vs, o1, l1, dos, qi, ki, qh, kh, meta, block=block)
+    dk1, dv1 = scfa.attn_bwd_dkdv_lists(qs, ks, vs, l1, dos, de1, qi, ki, qh, kh, meta, block=block)
+    o2, l2 = scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=block, q_rows=qr, k_rows=kr)
+    dq2, de2 = scfa.attn_bwd_dq_lists(q, k, v, o2, l2, do, qi, ki, qh, kh, meta, block=block, q_rows=qr, k_rows=kr)
+    dk2, dv2 = scfa.attn_bwd_dkdv_lists(q, k, v, l2, do, de2, qi, ki, qh, kh, meta, block=block, q_rows=qr,
+                                        k_rows=kr)
+    torch.cuda.synchronize()
+    for a_, b_ in [(o1, o2), (l1, l2), (dq1, dq2), (de1, de2), (dk1, dk2), (dv1, dv2)]:
+        assert torch.equal(a_, b_)
