@@ -22,15 +22,9 @@
 
 namespace scfa {
 
-struct List {
-  int n;
-  int first;
-  const int32_t *list;
-};
-
 template <int MODE, int BS>
-__device__ __forceinline__ List row_list_b(const AttnArgs &a, int bh, int qb) {
-  List r{0, 0, nullptr};
+__device__ __forceinline__ LiveList row_list_b(const AttnArgs &a, int bh, int qb) {
+  LiveList r{0, 0, nullptr, 0, 0, 0};
   if (a.no_prune) {
     r.n = a.nk;
   } else if (MODE == kDense) {
@@ -38,13 +32,15 @@ __device__ __forceinline__ List row_list_b(const AttnArgs &a, int bh, int qb) {
     r.n = min(a.nk, qmax / BS + 1);
   } else {
     r.n = min(a.row_cnt[(size_t)bh * a.nq + qb], a.nk);  // malformed counts never overrun the row
-    r.list = a.row_list + ((size_t)bh * a.nq + qb) * a.nk;
+    r.p = a.row_list + ((size_t)bh * a.nq + qb) * a.nk;
+    r.lim = a.nk;
+    list_window(r, 0);
   }
   return r;
 }
 
 template <int MODE, int BS>
-__device__ __forceinline__ void row_tile(const AttnArgs &a, const List &rl, int t, int qb, int &kb, bool &free) {
+__device__ __forceinline__ void row_tile(const AttnArgs &a, LiveList &rl, int t, int qb, int &kb, bool &free) {
   if (a.no_prune) {
     kb = t;
     free = false;
@@ -52,7 +48,7 @@ __device__ __forceinline__ void row_tile(const AttnArgs &a, const List &rl, int 
     kb = t;
     free = min((kb + 1) * BS, a.Tk) - 1 <= qb * BS;
   } else {
-    const int e = rl.list[t];
+    const int e = list_entry(rl, t);
     kb = e & 0x7fffffff;
     free = e < 0;
   }
@@ -60,8 +56,8 @@ __device__ __forceinline__ void row_tile(const AttnArgs &a, const List &rl, int 
 }
 
 template <int MODE, int BS>
-__device__ __forceinline__ List col_list_b(const AttnArgs &a, int bh, int kb) {
-  List r{0, 0, nullptr};
+__device__ __forceinline__ LiveList col_list_b(const AttnArgs &a, int bh, int kb) {
+  LiveList r{0, 0, nullptr, 0, 0, 0};
   if (a.no_prune) {
     r.n = a.nq;
   } else if (MODE == kDense) {
@@ -70,13 +66,15 @@ __device__ __forceinline__ List col_list_b(const AttnArgs &a, int bh, int kb) {
     r.n = kb * BS < a.Tq ? a.nq - kb : 0;
   } else {
     r.n = min(a.col_cnt[(size_t)bh * a.nk + kb], a.nq);
-    r.list = a.col_list + ((size_t)bh * a.nk + kb) * a.nq;
+    r.p = a.col_list + ((size_t)bh * a.nk + kb) * a.nq;
+    r.lim = a.nq;
+    list_window(r, 0);
   }
   return r;
 }
 
 template <int MODE, int BS>
-__device__ __forceinline__ void col_tile(const AttnArgs &a, const List &cl, int t, int kb, int &qb, bool &free) {
+__device__ __forceinline__ void col_tile(const AttnArgs &a, LiveList &cl, int t, int kb, int &qb, bool &free) {
   if (a.no_prune) {
     qb = t;
     free = false;
@@ -84,7 +82,7 @@ __device__ __forceinline__ void col_tile(const AttnArgs &a, const List &cl, int 
     qb = cl.first + t;
     free = min((kb + 1) * BS, a.Tk) - 1 <= qb * BS;
   } else {
-    const int e = cl.list[t];
+    const int e = list_entry(cl, t);
     qb = e & 0x7fffffff;
     free = e < 0;
   }
@@ -100,7 +98,7 @@ struct Chunk {
 };
 
 template <int MODE, int BS, bool ROWS>
-__device__ __forceinline__ bool next_chunk(const AttnArgs &a, const List &ls, int self, int t, int ch, Chunk &out) {
+__device__ __forceinline__ bool next_chunk(const AttnArgs &a, LiveList &ls, int self, int t, int ch, Chunk &out) {
   constexpr int NCH = BS / kChunk;
   const int n_other = ROWS ? a.nk : a.nq;
   const int T_other = ROWS ? a.Tk : a.Tq;
@@ -162,7 +160,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
 
-  const List rl = row_list_b<MODE, BS>(a, bh, qb);
+  LiveList rl = row_list_b<MODE, BS>(a, bh, qb);
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
@@ -345,7 +343,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const float *lse2g = a.delta + (size_t)a.BH * a.Tq + qoff;
   const float *delg = a.delta + qoff;
 
-  const List cl = col_list_b<MODE, BS>(a, bh, kb);
+  LiveList cl = col_list_b<MODE, BS>(a, bh, kb);
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
   const int32_t *qrows = QROWS ? a.q_rows + qoff : nullptr;
@@ -539,7 +537,7 @@ __global__ __launch_bounds__(BS) void k_bwd_dq_f32(AttnArgs a) {
     my_idx = MODE == kDense ? qrow : a.q_idx[qoff + qrow];
     if (MODE == kHash) my_hash = a.q_hash[qoff + qrow];
   }
-  const List rl = row_list_b<MODE, BS>(a, bh, qb);
+  LiveList rl = row_list_b<MODE, BS>(a, bh, qb);
   for (int t = 0; t < rl.n; ++t) {
     int kb;
     bool free;
@@ -613,7 +611,7 @@ __global__ __launch_bounds__(BS) void k_bwd_dkdv_f32(AttnArgs a) {
     my_idx = MODE == kDense ? krow : a.k_idx[koff + krow];
     if (MODE == kHash) my_hash = a.k_hash[koff + krow];
   }
-  const List cl = col_list_b<MODE, BS>(a, bh, kb);
+  LiveList cl = col_list_b<MODE, BS>(a, bh, kb);
   for (int t = 0; t < cl.n; ++t) {
     int qb;
     bool free;

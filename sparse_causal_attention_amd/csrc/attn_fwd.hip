@@ -22,16 +22,11 @@
 
 namespace scfa {
 
-// Live list of a query block: returns the count; entry t is read by tile_at.
-struct RowList {
-  int n;
-  const int32_t *list;
-};
-
+// Live list of a query block: the count, and for stored lists the first
+// window of entries; entry t is read by tile_at.
 template <int MODE, int BS>
-__device__ __forceinline__ RowList row_list(const AttnArgs &a, int bh, int qb) {
-  RowList r;
-  r.list = nullptr;
+__device__ __forceinline__ LiveList row_list(const AttnArgs &a, int bh, int qb) {
+  LiveList r{0, 0, nullptr, 0, 0, 0};
   if (a.no_prune) {
     r.n = a.nk;
   } else if (MODE == kDense) {
@@ -39,14 +34,16 @@ __device__ __forceinline__ RowList row_list(const AttnArgs &a, int bh, int qb) {
     r.n = min(a.nk, qmax / BS + 1);
   } else {
     r.n = min(a.row_cnt[(size_t)bh * a.nq + qb], a.nk);  // malformed counts never overrun the row
-    r.list = a.row_list + ((size_t)bh * a.nq + qb) * a.nk;
+    r.p = a.row_list + ((size_t)bh * a.nq + qb) * a.nk;
+    r.lim = a.nk;
+    list_window(r, 0);
   }
   return r;
 }
 
 // Key block of entry t and whether the whole tile is admissible (mask-free).
 template <int MODE, int BS>
-__device__ __forceinline__ void tile_at(const AttnArgs &a, const RowList &rl, int t, int qb, int &kb, bool &free) {
+__device__ __forceinline__ void tile_at(const AttnArgs &a, LiveList &rl, int t, int qb, int &kb, bool &free) {
   if (a.no_prune) {
     kb = t;
     free = false;
@@ -54,7 +51,7 @@ __device__ __forceinline__ void tile_at(const AttnArgs &a, const RowList &rl, in
     kb = t;
     free = min((kb + 1) * BS, a.Tk) - 1 <= qb * BS;
   } else {
-    const int e = rl.list[t];
+    const int e = list_entry(rl, t);
     kb = e & 0x7fffffff;
     free = e < 0;
   }
@@ -70,7 +67,7 @@ struct ChunkPos {
 // First usable chunk at or after entry t, chunk ch (entries naming a block
 // outside the sequence and chunks past Tk are skipped).  Scalar code.
 template <int MODE, int BS>
-__device__ __forceinline__ bool find_chunk(const AttnArgs &a, const RowList &rl, int qb, int t, int ch, ChunkPos &out) {
+__device__ __forceinline__ bool find_chunk(const AttnArgs &a, LiveList &rl, int qb, int t, int ch, ChunkPos &out) {
   constexpr int NCH = BS / kChunk;
   for (; t < rl.n; ++t, ch = 0) {
     int kb;
@@ -143,7 +140,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
 
-  const RowList rl = row_list<MODE, BS>(a, bh, qb);
+  LiveList rl = row_list<MODE, BS>(a, bh, qb);
   const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   ChunkPos cur;
@@ -320,7 +317,7 @@ __global__ __launch_bounds__(BS) void k_fwd_f32(AttnArgs a) {
     my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
     if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
   }
-  const RowList rl = row_list<MODE, BS>(a, bh, qb);
+  LiveList rl = row_list<MODE, BS>(a, bh, qb);
   float m = -INFINITY, l = 0.f;
   for (int t = 0; t < rl.n; ++t) {
     int kb;

@@ -40,8 +40,69 @@ __device__ __forceinline__ lds_void *to_lds(const void *p) {
 }
 
 // Wait until this wave's outstanding vector-memory operations (including
-// global->LDS copies) have completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// global->LDS copies) have completed: s_waitcnt vmcnt(0) (expcnt and lgkmcnt
+// fields at their maxima, i.e. not waited for).  Issued through the builtin so
+// the compiler's wait-count pass sees it and knows that every earlier load has
+// landed; an asm wait would leave loads issued before the chunk loop looking
+// outstanding inside it, and the pass would then wait for the loop's own
+// loads.
+__device__ __forceinline__ void wait_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+}
+
+// A block's live list (row list: key blocks of a query block; column list:
+// query blocks of a key block).  Stored entries are read through a register
+// window: lane l holds entry base + l, so entry t costs one v_readlane and the
+// chunk loop issues no list loads (a load there would be waited for together
+// with the chunk copies in flight).  The window moves forward 64 entries at a
+// time; lists are walked in increasing t.
+struct LiveList {
+  int n;             // live entries
+  int first;         // dense-causal column lists: first live query block
+  const int32_t *p;  // stored entries (pruned modes), a row of `lim` slots; else nullptr
+  int lim;           // slots in the stored row (entries past n are never used)
+  int base;          // first entry held in win
+  int win;           // this lane's entry p[base + lane] (0 past lim)
+};
+
+// The empty asm consumes the loaded value where it is issued, so the wait for
+// it happens here (once per 64 entries) and the readlane in the chunk loop has
+// no load outstanding; without it the wait lands in the loop and also drains
+// the chunk copies in flight.
+__device__ __forceinline__ void list_window(LiveList &l, int base) {
+  l.base = base;
+  const int i = base + (int)(threadIdx.x & 63);
+  l.win = i < l.lim ? l.p[i] : 0;
+  asm volatile("" : "+v"(l.win));
+}
+
+// Stored entry t (t >= base; uniform across the wave).
+__device__ __forceinline__ int list_entry(LiveList &l, int t) {
+  if (t - l.base >= 64) list_window(l, t & ~63);
+  return __builtin_amdgcn_readlane(l.win, t - l.base);
+}
+
+// Global -> LDS copies (lane l's `size` bytes land at dst + size*l, M0 holding
+// dst).  They are issued as inline asm, not through the compiler builtin: the
+// compiler's wait-count pass cannot tell which LDS bytes a builtin copy
+// writes, so it made every LDS read wait for all copies in flight, including
+// the next chunk's copy into the other buffer, which serialised the double
+// buffer.  Hidden in asm, a copy is waited for only where the kernels say so:
+// the vmcnt(0) + barrier at the top of each chunk loop, which every read of
+// copied data follows.  (Vector-memory loads complete in order, so the
+// compiler's own waits for register loads stay correct with these in the
+// count.)  Nothing else in these kernels uses M0; the s_nop is the wait state
+// between the M0 write and the copy.
+__device__ __forceinline__ void lds_copy16(const void *src, void *dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(dst));  // dst is wave-uniform
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void *src, void *dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(dst));  // dst is wave-uniform
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
+}
 
 // Hardware dispatches work group i to XCD i % 8.  Give each XCD a contiguous
 // range of logical ids so the blocks of one head share that XCD's L2.
@@ -96,9 +157,7 @@ __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, 
     for (int k = 0; k < O::PER_WAVE; ++k) {
       const int i = k * NW + w;
       if (O::NINST % NW == 0 || i < O::NINST) {
-#if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only (the host pass never emits this code)
-        __builtin_amdgcn_global_load_lds(base + o.off[k], to_lds(dst.v + i * 512), 16, 0, 0);
-#endif
+        lds_copy16(base + o.off[k], dst.v + i * 512);
       }
     }
   } else {
@@ -109,9 +168,7 @@ __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, 
         const int s = i * 64 + lane;
         const int r = s / O::CPR, p = s % O::CPR;
         const int rr = r < nvalid ? r : nvalid - 1;
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_global_load_lds(base + rr * D + ((p ^ (r & 7)) << 3), to_lds(dst.v + i * 512), 16, 0, 0);
-#endif
+        lds_copy16(base + rr * D + ((p ^ (r & 7)) << 3), dst.v + i * 512);
       }
     }
   }
@@ -151,9 +208,7 @@ __device__ __forceinline__ void dma_matrix_rows(MatChunk<D> &dst, const uint16_t
       const int s = i * 64 + lane;
       const int r = s / O::CPR, p = s % O::CPR;
       const int src = min(max(dr.row[k], 0), T - 1);
-#if defined(__HIP_DEVICE_COMPILE__)
-      __builtin_amdgcn_global_load_lds(g + (size_t)src * D + ((p ^ (r & 7)) << 3), to_lds(dst.v + i * 512), 16, 0, 0);
-#endif
+      lds_copy16(g + (size_t)src * D + ((p ^ (r & 7)) << 3), dst.v + i * 512);
     }
   }
 }
@@ -162,9 +217,7 @@ __device__ __forceinline__ void dma_matrix_rows(MatChunk<D> &dst, const uint16_t
 __device__ __forceinline__ void dma_vec(void *dst, const void *g, int row0, int nvalid) {
   const int lane = threadIdx.x & 63;
   const int rr = lane < nvalid ? lane : nvalid - 1;
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(static_cast<const uint32_t *>(g) + row0 + rr, to_lds(dst), 4, 0, 0);
-#endif
+  lds_copy4(static_cast<const uint32_t *>(g) + row0 + rr, dst);
 }
 
 // Per-lane element offsets of the fragment reads inside a MatChunk<D>, computed
