@@ -4,9 +4,12 @@ Workload (synthetic, seeded): B=2, H=12, T=16384, d=64, 32 LSH buckets,
 block 64, bf16 -- the GPT-2-small attention shape at 16k tokens.  One step is
 the whole hot path over one batch, with every input already in HBM:
 
-  LSH bucket ids + (bucket, position) sort of Q (dO gathered alongside),
-  the same for K (V gathered alongside), block metadata (row and column
-  live-tile lists), forward, backward dQ (+ rowsum(dO*O)), backward dK/dV.
+  LSH bucket ids + (bucket, position) sort of Q and of K (one call over the
+  two stacked in one [2B, H, T, d] allocation), block metadata (row and
+  column live-tile lists), forward, backward dQ (+ rowsum(dO*O)), backward
+  dK/dV; the attention kernels read Q, dO, K and V through the sort
+  permutations (--copy-sorted: the sorts copy Q with dO and K with V into
+  sorted order instead, in two calls).
 
 Reported value: effective TFLOP/s on executed tiles (forward 4*bq*bk*d and
 backward 10*bq*bk*d flops per executed tile of real extent bq x bk) over the
@@ -114,9 +117,13 @@ def make_inputs(w, torch):
 
     dev = torch.device("cuda:0")
     to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
-    q, k, v, do = to(st(lambda x: x.q)), to(st(lambda x: x.k)), to(st(lambda x: x.v)), to(st(lambda x: x.do))
+    # Q and K share one allocation, Q first: [2B, H, T, d].  R is per head and shared by the batch, so one
+    # LSH + sort call over the stacked tensor hashes and orders both (batch entries B.. are K's).
+    qk = to(np.concatenate([st(lambda x: x.q), st(lambda x: x.k)]))
+    q, k = qk[: w.B], qk[w.B:]
+    v, do = to(st(lambda x: x.v)), to(st(lambda x: x.do))
     R = torch.from_numpy(np.stack([lsh_rotation(w, h) for h in range(w.H)])).to(dev)
-    return q, k, v, do, R
+    return q, k, v, do, R, qk
 
 
 def tile_work(meta, Tq, Tk, block, torch):
@@ -161,24 +168,33 @@ class Timer:
         return sum(s) / len(s) if s else float("nan")
 
 
-def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False):
+def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False, qk=None):
     """One step.  By default the sorts return only bucket ids, positions and the permutations, and
     the attention kernels read Q, dO, K and V through the permutations (row indirection); with
     copy_sorted the sorts also copy the rows into sorted order and attention reads the copies.
-    Outputs (O, lse, dQ, dK, dV) are in sorted order either way, bit-identical."""
+    Outputs (O, lse, dQ, dK, dV) are in sorted order either way, bit-identical.
+
+    With qk (Q and K stacked in one [2B, H, T, d] allocation, q and k its halves) and rows read
+    through the permutations, one LSH + sort call serves both tensors."""
     nb, blk, sc = w.n_buckets, w.block, w.scale
+    B = q.shape[0]
     if timer:
         timer.begin()
     if copy_sorted:
         qh, qi, _, qs, dos = scfa.lsh_bucket_sort(q, R, nb, companion=do)
-    else:
-        qh, qi, qp, _, _ = scfa.lsh_bucket_sort(q, R, nb, want_x=False)
-    if timer:
-        timer.mark()
-    if copy_sorted:
+        if timer:
+            timer.mark()
         kh, ki, _, ks, vs = scfa.lsh_bucket_sort(k, R, nb, companion=v)
         rows = {}
+    elif qk is not None:
+        hh, ii, pp, _, _ = scfa.lsh_bucket_sort(qk, R, nb, want_x=False)
+        qh, kh, qi, ki, qp, kp = hh[:B], hh[B:], ii[:B], ii[B:], pp[:B], pp[B:]
+        qs, dos, ks, vs = q, do, k, v
+        rows = {"q_rows": qp, "k_rows": kp}
     else:
+        qh, qi, qp, _, _ = scfa.lsh_bucket_sort(q, R, nb, want_x=False)
+        if timer:
+            timer.mark()
         kh, ki, kp, _, _ = scfa.lsh_bucket_sort(k, R, nb, want_x=False)
         qs, dos, ks, vs = q, do, k, v
         rows = {"q_rows": qp, "k_rows": kp}
@@ -200,7 +216,12 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False)
     return meta, (o, lse, dq, dk, dv)
 
 
-STEP_CALLS = ["lsh_sort_q", "lsh_sort_k", "block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
+STEP_CALLS = ["lsh_sort_qk", "block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
+STEP_CALLS_COPIED = ["lsh_sort_q", "lsh_sort_k", "block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
+
+
+def step_calls(copy_sorted):
+    return STEP_CALLS_COPIED if copy_sorted else STEP_CALLS
 
 
 def run_dense(scfa, w, q, k, v, do, timer=None):
@@ -382,7 +403,7 @@ def measure_rows(scfa, torch, w, q, k, v, do, R, args):
     }), flush=True)
 
 
-def sweep_buckets(scfa, torch, w, q, k, v, do, nbs, args):
+def sweep_buckets(scfa, torch, w, q, k, v, do, qk, nbs, args):
     """Same shape and inputs, LSH rotations drawn per bucket count (seeded by the workload)."""
     import dataclasses
 
@@ -395,14 +416,15 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, nbs, args):
     for nb in nbs:
         wn = dataclasses.replace(w, n_buckets=nb, name=f"{w.name.rsplit('_nb', 1)[0]}_nb{nb}")
         R = torch.from_numpy(np.stack([lsh_rotation(wn, h) for h in range(w.H)])).to("cuda:0")
-        timer = Timer(torch, STEP_CALLS)
+        calls = step_calls(args.copy_sorted)
+        timer = Timer(torch, calls)
         ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists,
-                                                              args.copy_sorted),
+                                                              args.copy_sorted, qk),
                                     args.steps,
                                     args.warmup, timer)
         timer.collect()
         units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
-        per_call = {n: round(timer.mean_ms(n), 4) for n in STEP_CALLS}
+        per_call = {n: round(timer.mean_ms(n), 4) for n in calls}
         attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
         nq = (w.T + w.block - 1) // w.block
         print(json.dumps({
@@ -454,10 +476,10 @@ def main():
 
     w = WORKLOADS[WORKLOAD_ID]
     _log(f"[bench] workload {w.name}: generating inputs")
-    q, k, v, do, R = make_inputs(w, torch)
+    q, k, v, do, R, qk = make_inputs(w, torch)
     torch.cuda.synchronize()
     if args.sweep_nb:
-        sweep_buckets(scfa, torch, w, q, k, v, do, [int(x) for x in args.sweep_nb.split(",")], args)
+        sweep_buckets(scfa, torch, w, q, k, v, do, qk, [int(x) for x in args.sweep_nb.split(",")], args)
         return
     if args.measure_rows:
         measure_rows(scfa, torch, w, q, k, v, do, R, args)
@@ -475,16 +497,18 @@ def main():
 
     _log("[bench] warmup")
     for _ in range(args.warmup):
-        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists, copy_sorted=args.copy_sorted)
+        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists, copy_sorted=args.copy_sorted, qk=qk)
     torch.cuda.synchronize()
 
     # HIP events between the calls, on the stream the kernels run on, inside the timed region
     _log(f"[bench] timing {args.steps} steps")
-    timer = Timer(torch, STEP_CALLS)
+    calls = step_calls(args.copy_sorted)
+    timer = Timer(torch, calls)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        meta, _ = run_step(scfa, w, q, k, v, do, R, timer, exact=not args.range_lists, copy_sorted=args.copy_sorted)
+        meta, _ = run_step(scfa, w, q, k, v, do, R, timer, exact=not args.range_lists, copy_sorted=args.copy_sorted,
+                           qk=qk)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -517,14 +541,14 @@ def main():
         torch.cuda.synchronize()
         dtimer.collect()
 
-    per_call = {n: round(timer.mean_ms(n), 4) for n in STEP_CALLS}
+    per_call = {n: round(timer.mean_ms(n), 4) for n in calls}
     attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
     # algorithmic flops per launch of each attention kernel (tile units x d)
     kernel_flops = {"fwd": 4.0 * units * w.d, "bwd_dq": 6.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
     dominant = max(kernel_flops, key=lambda n: per_call[n])
     achieved = kernel_flops[dominant] / (per_call[dominant] * 1e-3) / 1e12
     roofline = {
-        "kernel": {"fwd": "k_fwd_bf16<kHash,64,64,%s>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64,%s>",
+        "kernel": {"fwd": "k_fwd_bf16_ks<kHash,64,64,%s>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64,%s>",
                    "bwd_dkdv": "k_bwd_dkdv_bf16<kHash,64,64,%s>"}[dominant] % (
                        "false" if args.copy_sorted else "true"),
         "bound": "mfma",
@@ -565,7 +589,8 @@ def main():
             "block": w.block,
             "n_buckets": w.n_buckets,
             "step": ("lsh+sort(Q,dO) + lsh+sort(K,V) + block lists + fwd + bwd" if args.copy_sorted else
-                     "lsh+sort(Q) + lsh+sort(K) + block lists + fwd + bwd, rows read through the sort permutations"),
+                     "lsh+sort of Q and K (one call over the stacked [2B,H,T,d] tensor) + block lists + fwd + bwd, "
+                     "rows read through the sort permutations"),
             "tile_rule": "range" if args.range_lists else "exact",
             "rows": "copied" if args.copy_sorted else "permuted",
         },

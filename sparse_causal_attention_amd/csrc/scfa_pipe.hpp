@@ -327,6 +327,39 @@ __device__ __forceinline__ void mask_rows(f32x16 (&s)[2], const int *sidx, const
 }
 
 // mask_rows for one C tile whose rows are chunk rows sub0 + 8g + 4*half + e
+// (sub0 = 0 or 32) and whose lane column is a query: admissible iff the row's
+// key position <= my_idx (dense mode: the position is chunk_r0 + chunk row),
+// and equal buckets in hash mode; with TAIL, rows at or past nvalid are
+// inadmissible.  Inadmissible entries become `fill`.
+template <int MODE, bool TAIL>
+__device__ __forceinline__ void mask_tile_q(f32x16 &s, const int *sidx, const int *shash, int sub0, int chunk_r0,
+                                            int nvalid, int my_idx, int my_hash, int half, float fill) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int rr = sub0 + 8 * g + 4 * half;
+    int iv[4], hv[4] = {0, 0, 0, 0};
+    if (MODE == kDense) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) iv[e] = chunk_r0 + rr + e;
+    } else {
+      const int4 ki = *reinterpret_cast<const int4 *>(sidx + rr);
+      iv[0] = ki.x, iv[1] = ki.y, iv[2] = ki.z, iv[3] = ki.w;
+      if (MODE == kHash) {
+        const int4 kh = *reinterpret_cast<const int4 *>(shash + rr);
+        hv[0] = kh.x, hv[1] = kh.y, hv[2] = kh.z, hv[3] = kh.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool ok = iv[e] <= my_idx;
+      if (MODE == kHash) ok = ok & (hv[e] == my_hash);
+      if (TAIL) ok = ok & (rr + e < nvalid);
+      s[4 * g + e] = ok ? s[4 * g + e] : fill;
+    }
+  }
+}
+
+// mask_rows for one C tile whose rows are chunk rows sub0 + 8g + 4*half + e
 // (sub0 = 0 or 32); the lane's column is a key and rows are queries:
 // admissible iff my_idx <= row position (dense mode: the position is
 // chunk_r0 + chunk row), and equal buckets in hash mode; with TAIL, rows at

@@ -208,3 +208,24 @@ def test_lsh_golden_accumulation_order_and_ties():
     got = np.empty(x.shape[2], dtype=np.int64)
     got[perm[0, 0].cpu().numpy()] = hs[0, 0].cpu().numpy()
     assert got.tolist() == want
+
+
+def test_lsh_sort_of_stacked_q_and_k():
+    """Q and K in one [2B, H, T, d] allocation (Q first), as the benchmark step passes them: one
+    call orders both, and each half matches the oracle for its own tensor with the shared R."""
+    B, H, T, d, nb = 2, 3, 3000, 64, 32
+    xq, R = _lsh_case(91, B, H, T, d, nb)
+    xk, _ = _lsh_case(92, B, H, T, d, nb)
+    x = np.concatenate([xq, xk])
+    note(f"[lsh stacked q,k] B={B} H={H} T={T}")
+    hs, ids, perm, _, _ = _scfa().lsh_bucket_sort(dev(x, torch.bfloat16), dev(R), nb, want_x=False)
+    torch.cuda.synchronize()
+    hs, ids, perm = hs.cpu().numpy(), ids.cpu().numpy(), perm.cpu().numpy()
+    for half, src in enumerate((xq, xk)):
+        for b in range(B):
+            for h in range(H):
+                bk = lsh.buckets_c(src[b, h], R[h])
+                p_ref, h_ref, i_ref = lsh.bucket_sort(bk, np.arange(T))
+                np.testing.assert_array_equal(perm[half * B + b, h], p_ref)
+                np.testing.assert_array_equal(hs[half * B + b, h], h_ref)
+                np.testing.assert_array_equal(ids[half * B + b, h], i_ref)
