@@ -8,8 +8,12 @@
 // ds_write instructions are spent on staging.
 //
 // LDS layout of a matrix: row-major, 16-byte pieces XOR-swizzled inside each
-// row: logical piece c of row r sits at physical piece c ^ (r & 7).  The
-// swizzle is applied through the DMA source addresses.  Rows past the end of
+// row: logical piece c of row r sits at physical piece c ^ swz(r), where
+// swz(r) = 2*(r & 3) + ((r >> 2) & 1) takes the eight values 0..7 over r & 7.
+// The row-fragment reads (eight consecutive rows, one logical piece) then hit
+// eight different pieces, and the transposed reads (four rows 4h..4h+3 at a
+// logical piece pair) hit four different piece pairs, so neither conflicts on
+// the LDS banks.  The swizzle is applied through the DMA source addresses.  Rows past the end of
 // the sequence are filled with copies of the last real row (finite values);
 // the kernels mask them explicitly.
 //
@@ -29,7 +33,12 @@
 
 #include "scfa_device.hpp"
 
+
+
 namespace scfa {
+
+// Piece swizzle of row r (depends on r & 7 only).
+__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -137,7 +146,7 @@ __device__ __forceinline__ DmaOffsets<D, NW> dma_offsets() {
     const int i = k * NW + w;
     const int s = i * 64 + lane;
     const int r = s / O::CPR, p = s % O::CPR;
-    o.off[k] = r * D + ((p ^ (r & 7)) << 3);
+    o.off[k] = r * D + ((p ^ swz(r)) << 3);
   }
   return o;
 }
@@ -168,7 +177,7 @@ __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, 
         const int s = i * 64 + lane;
         const int r = s / O::CPR, p = s % O::CPR;
         const int rr = r < nvalid ? r : nvalid - 1;
-        lds_copy16(base + rr * D + ((p ^ (r & 7)) << 3), dst.v + i * 512);
+        lds_copy16(base + rr * D + ((p ^ swz(r)) << 3), dst.v + i * 512);
       }
     }
   }
@@ -208,7 +217,7 @@ __device__ __forceinline__ void dma_matrix_rows(MatChunk<D> &dst, const uint16_t
       const int s = i * 64 + lane;
       const int r = s / O::CPR, p = s % O::CPR;
       const int src = min(max(dr.row[k], 0), T - 1);
-      lds_copy16(g + (size_t)src * D + ((p ^ (r & 7)) << 3), dst.v + i * 512);
+      lds_copy16(g + (size_t)src * D + ((p ^ swz(r)) << 3), dst.v + i * 512);
     }
   }
 }
@@ -225,7 +234,7 @@ __device__ __forceinline__ void dma_vec(void *dst, const void *g, int row0, int 
 // compile-time constant (an LDS instruction immediate).
 //  rows[kk]: frag_rows(row = col, kk); add 32*sub*D for sub-tile sub.
 //  trans[mt]: first read of frag_trans(mt, t = 0); add 16*t*D for k-step t and
-//             8*D for the second read (rows r and r + 8 share r & 7).
+//             8*D for the second read (rows r and r + 8 share swz(r)).
 template <int D>
 struct LaneOffsets {
   int rows[D / 16];
@@ -238,13 +247,13 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets() {
   const int col = lane & 31, half = lane >> 5;
   LaneOffsets<D> o;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) o.rows[kk] = col * D + (((2 * kk + half) ^ (col & 7)) << 3);
+  for (int kk = 0; kk < D / 16; ++kk) o.rows[kk] = col * D + (((2 * kk + half) ^ swz(col)) << 3);
   const int j = lane & 15, a = j & 3, mm = j >> 2, g = lane >> 4, h = g >> 1;
-  const int x = 4 * h + mm;  // == r & 7 for both rows a lane reads
+  const int x = 4 * h + mm;  // == r & 7 for both rows a lane reads (r and r + 8)
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
     const int c = 4 * mt + 2 * (g & 1) + (a >> 1);
-    o.trans[mt] = x * D + ((c ^ x) << 3) + 4 * (a & 1);
+    o.trans[mt] = x * D + ((c ^ swz(x)) << 3) + 4 * (a & 1);
   }
   return o;
 }
