@@ -160,7 +160,19 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
 
+  // Loads that depend only on this lane's own row go first: issued after the
+  // list and chunk copies, a wait for them would also wait for those copies.
+  int qsrc_raw = a.q_rows && qvalid ? a.q_rows[qoff + qrow] : qrow;  // clamped where used
+  float lse_raw = qvalid ? a.lse[qoff + qrow] : 0.f;
+  int my_idx = kIdxTailQ, my_hash = 0;
+  if (qvalid) {
+    my_idx = MODE == kDense ? qrow : a.q_idx[qoff + qrow];
+    if (MODE == kHash) my_hash = a.q_hash[qoff + qrow];
+  }
   LiveList rl = row_list_b<MODE, BS>(a, bh, qb);
+  // Consumed here, where the list window's wait already covers these older loads;
+  // first used after the chunk copies, their wait would also drain them.
+  asm volatile("" : "+v"(qsrc_raw), "+v"(lse_raw));
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.r0, nxt.nvalid);
   }
 
-  const int qsrc = a.q_rows && qvalid ? min(max(a.q_rows[qoff + qrow], 0), a.Tq - 1) : qrow;
+  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
   bf16x8 qf[D / 16], dof[D / 16];
   float dsum = 0.f;
 #pragma unroll
@@ -213,15 +225,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     }
   }
   dsum = pair_sum(dsum);
-  const float lse2 = qvalid ? a.lse[qoff + qrow] * kLog2e : INFINITY;
+  const float lse2 = qvalid ? lse_raw * kLog2e : INFINITY;
   if (qvalid && half == 0) {
     a.delta[qoff + qrow] = dsum;
     a.delta[(size_t)a.BH * a.Tq + qoff + qrow] = lse2;
-  }
-  int my_idx = kIdxTailQ, my_hash = 0;
-  if (qvalid) {
-    my_idx = MODE == kDense ? qrow : a.q_idx[qoff + qrow];
-    if (MODE == kHash) my_hash = a.q_hash[qoff + qrow];
   }
   const float c = a.scale * kLog2e;
   f32x16 dqa[D / 32];
@@ -343,7 +350,18 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const float *lse2g = a.delta + (size_t)a.BH * a.Tq + qoff;
   const float *delg = a.delta + qoff;
 
+  // Loads that depend only on this lane's own row go first: issued after the
+  // list and chunk copies, a wait for them would also wait for those copies.
+  int ksrc_raw = a.k_rows && kvalid_row ? a.k_rows[koff + krow] : krow;  // clamped where used
+  int my_idx = kIdxTailK, my_hash = 0;
+  if (kvalid_row) {
+    my_idx = MODE == kDense ? krow : a.k_idx[koff + krow];
+    if (MODE == kHash) my_hash = a.k_hash[koff + krow];
+  }
   LiveList cl = col_list_b<MODE, BS>(a, bh, kb);
+  // Consumed here, where the list window's wait already covers this older load;
+  // first used after the chunk copies, its wait would also drain them.
+  asm volatile("" : "+v"(ksrc_raw));
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
   const int32_t *qrows = QROWS ? a.q_rows + qoff : nullptr;
@@ -376,18 +394,13 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (have_next) dma_rows_load<D, NW>(drn, qrows, nxt.r0, nxt.nvalid);
   }
 
-  const int ksrc = a.k_rows && kvalid_row ? min(max(a.k_rows[koff + krow], 0), a.Tk - 1) : krow;
+  const int ksrc = a.k_rows && kvalid_row ? min(max(ksrc_raw, 0), a.Tk - 1) : krow;
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const size_t off = (size_t)ksrc * D + 16 * kk + 8 * half;
     kf[kk] = as_bf16x8(kvalid_row ? ld16(K + off) : make_uint4(0, 0, 0, 0));
     vf[kk] = as_bf16x8(kvalid_row ? ld16(V + off) : make_uint4(0, 0, 0, 0));
-  }
-  int my_idx = kIdxTailK, my_hash = 0;
-  if (kvalid_row) {
-    my_idx = MODE == kDense ? krow : a.k_idx[koff + krow];
-    if (MODE == kHash) my_hash = a.k_hash[koff + krow];
   }
   const float c = a.scale * kLog2e;
   f32x16 dka[D / 32], dva[D / 32];

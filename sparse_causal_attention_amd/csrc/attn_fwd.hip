@@ -142,7 +142,18 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
 
+  // Loads that depend only on this lane's own row go first: issued after the
+  // list and chunk copies, a wait for them would also wait for those copies.
+  int qsrc_raw = a.q_rows && qvalid ? a.q_rows[(size_t)bh * a.Tq + qrow] : qrow;  // clamped where used
+  int my_idx = kIdxTailQ, my_hash = 0;
+  if (qvalid) {
+    my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
+    if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
+  }
   LiveList rl = row_list<MODE, BS>(a, bh, qb);
+  // Consumed here, where the list window's wait already covers this older load;
+  // first used after the chunk copies, its wait would also drain them.
+  asm volatile("" : "+v"(qsrc_raw));
   const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   ChunkPos cur;
@@ -164,16 +175,11 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)
   }
   const LaneOffsets<D> lo = lane_offsets<D>();
 
-  const int qsrc = a.q_rows && qvalid ? min(max(a.q_rows[(size_t)bh * a.Tq + qrow], 0), a.Tq - 1) : qrow;
+  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     qf[kk] = as_bf16x8(qvalid ? ld16(Q + (size_t)qsrc * D + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0));
-  int my_idx = kIdxTailQ, my_hash = 0;
-  if (qvalid) {
-    my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
-    if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
-  }
 
   const float c = a.scale * kLog2e;
   float mref = -INFINITY, l = 0.f;
@@ -318,7 +324,18 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(4)
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
 
+  // Loads that depend only on this lane's own row go first: issued after the
+  // list and chunk copies, a wait for them would also wait for those copies.
+  int qsrc_raw = a.q_rows && qvalid ? a.q_rows[(size_t)bh * a.Tq + qrow] : qrow;  // clamped where used
+  int my_idx = kIdxTailQ, my_hash = 0;
+  if (qvalid) {
+    my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
+    if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
+  }
   LiveList rl = row_list<MODE, BS>(a, bh, qb);
+  // Consumed here, where the list window's wait already covers this older load;
+  // first used after the chunk copies, its wait would also drain them.
+  asm volatile("" : "+v"(qsrc_raw));
   const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   ChunkPos cur;
@@ -340,16 +357,11 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(4)
   }
   const LaneOffsets<D> lo = lane_offsets<D>();
 
-  const int qsrc = a.q_rows && qvalid ? min(max(a.q_rows[(size_t)bh * a.Tq + qrow], 0), a.Tq - 1) : qrow;
+  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     qf[kk] = as_bf16x8(qvalid ? ld16(Q + (size_t)qsrc * D + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0));
-  int my_idx = kIdxTailQ, my_hash = 0;
-  if (qvalid) {
-    my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
-    if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
-  }
 
   const float c = a.scale * kLog2e;
   float mref = -INFINITY, l = 0.f;
