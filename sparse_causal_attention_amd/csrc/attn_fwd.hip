@@ -8,11 +8,11 @@
 // the softmax exact).
 //
 // bf16 kernel (gfx950 matrix cores).  One work group per (batch*head, query
-// block of BS rows); wave w owns queries 32w..32w+31 (block 64: the
-// key-split kernel below, whose waves also split each chunk's keys in two
-// halves and merge their softmax states at the end).  Each live key block is
-// streamed through LDS in 64-key chunks: K row-major, V transposed.  The
-// kernel computes S^T = K Q^T so that every lane owns ONE query column: the
+// block of BS rows) with 2*BS/32 waves: each 32-query tile has two waves, one
+// per half of every 64-key chunk, whose softmax states merge at the end.
+// Each live key block is streamed through LDS in 64-key chunks: K row-major,
+// V transposed.  The kernel computes S^T = K Q^T so that every lane owns ONE
+// query column: the
 // row max and row sum of the online softmax are in-lane except for a single
 // exchange with lane l^32, the O^T accumulator rescale is in-lane, and the
 // S^T registers feed the O^T += V^T P^T product directly as B operands.
@@ -126,187 +126,19 @@ __device__ __forceinline__ void issue_kv_rows(KVBuf<D> &b, const AttnArgs &a, co
 // KROWS: K and V rows come through a.k_rows (the chunk copies read row
 // k_rows[j] for chunk row j; the next chunk's indices are loaded one chunk
 // ahead).  Q rows come through a.q_rows when it is set.
-template <int MODE, int D, int BS, bool KROWS>
-__global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_bf16(AttnArgs a) {
-  constexpr int NW = BS / 32;
-  __shared__ __attribute__((aligned(16))) KVBuf<D> sb[2];
-
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wg / a.nq;
-  const int qb = wg % a.nq;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 31, half = lane >> 5;
-  const int qrow = qb * BS + 32 * w + col;
-  const bool qvalid = qrow < a.Tq;
-  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + (size_t)bh * a.Tq * D;
-  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
-  const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
-
-  // Loads that depend only on this lane's own row go first: issued after the
-  // list and chunk copies, a wait for them would also wait for those copies.
-  int qsrc_raw = a.q_rows && qvalid ? a.q_rows[(size_t)bh * a.Tq + qrow] : qrow;  // clamped where used
-  int my_idx = kIdxTailQ, my_hash = 0;
-  if (qvalid) {
-    my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
-    if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
-  }
-  LiveList rl = row_list<MODE, BS>(a, bh, qb);
-  // Consumed here, where the list window's wait already covers this older load;
-  // first used after the chunk copies, its wait would also drain them.
-  asm volatile("" : "+v"(qsrc_raw));
-  const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
-  const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
-  ChunkPos cur;
-  bool have = find_chunk<MODE, BS>(a, rl, qb, 0, 0, cur);
-  DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
-  if (have) {
-    if constexpr (KROWS) {
-      dma_rows_load<D, NW>(drn, krows, cur.k0, cur.kvalid);
-      issue_kv_rows<MODE, D, NW>(sb[0], a, K, V, bh, cur, drn);
-    } else {
-      issue_kv<MODE, D, NW>(sb[0], a, K, V, bh, cur, dof);
-    }
-  }
-  ChunkPos nxt;  // KROWS: looked up one chunk ahead, so its row indices can load early
-  bool have_next = false;
-  if constexpr (KROWS) {
-    have_next = have && find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
-    if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.k0, nxt.kvalid);
-  }
-  const LaneOffsets<D> lo = lane_offsets<D>();
-
-  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    qf[kk] = as_bf16x8(qvalid ? ld16(Q + (size_t)qsrc * D + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0));
-
-  const float c = a.scale * kLog2e;
-  float mref = -INFINITY, l = 0.f;
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-
-  int buf = 0;
-  while (have) {
-    ChunkPos nxt2;
-    bool have_next2 = false;
-    if constexpr (KROWS) have_next2 = have_next && find_chunk<MODE, BS>(a, rl, qb, nxt.t, nxt.ch + 1, nxt2);
-    else have_next = find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
-    wait_vmem();
-    __syncthreads();
-    if (have_next) {
-      if constexpr (KROWS) issue_kv_rows<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, drn);
-      else issue_kv<MODE, D, NW>(sb[buf ^ 1], a, K, V, bh, nxt, dof);
-    }
-    if constexpr (KROWS)
-      if (have_next2) dma_rows_load<D, NW>(drn, krows, nxt2.k0, nxt2.kvalid);
-    const KVBuf<D> &b = sb[buf];
-
-    // All K fragments of the chunk are requested first, then the two
-    // independent S^T accumulator chains run interleaved (k-step outer).
-    bf16x8 kfr[2][D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) kfr[sub][kk] = frag_rows<D>(b.k, lo, sub, kk);
-    f32x16 s[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) s[sub] = mfma32(kfr[sub][0], qf[0], kZero16);
-#pragma unroll
-    for (int kk = 1; kk < D / 16; ++kk)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) s[sub] = mfma32(kfr[sub][kk], qf[kk], s[sub]);
-    // V^T fragments do not depend on the softmax: request them now so their
-    // latency overlaps the mask / max / exp work below.
-    bf16x8 vfr[4][D / 32];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) vfr[t][mt] = frag_trans<D>(b.v, lo, mt, t);
-    if (cur.kvalid < kChunk)
-      mask_rows<MODE, true, true>(s, b.idx, b.hash, cur.k0, cur.kvalid, my_idx, my_hash, half, -INFINITY);
-    else if (!cur.free)
-      mask_rows<MODE, false, true>(s, b.idx, b.hash, cur.k0, cur.kvalid, my_idx, my_hash, half, -INFINITY);
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    mx = pair_max(mx);
-    // Only real query rows vote: rows past Tq are unmasked on mask-free tiles
-    // and must not change the rescale schedule of the others.
-    const bool need = qvalid & (mx * c > mref * c + kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-      const float m_new = fmaxf(mref, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mref - m_new) * c);
-      // A lane whose reference is still -inf has seen no admissible key: its
-      // accumulator is zero, so the multiply is skipped while that holds for all.
-      if (__builtin_amdgcn_ballot_w64(mref != -INFINITY) != 0ull) {
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
-      }
-      l *= alpha;
-      mref = m_new;
-    }
-    const float mc = mref == -INFINITY ? 0.f : mref * c;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[sub][r] = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -mc));
-
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const uint4 pk = c_regs_to_u4(s[sub], t2);
-        l = add_bf16x8(pk, l);
-        const bf16x8 pb = as_bf16x8(pk);
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma32(vfr[2 * sub + t2][mt], pb, acc[mt]);
-      }
-    buf ^= 1;
-    cur = nxt;
-    have = have_next;
-    if constexpr (KROWS) {
-      nxt = nxt2;
-      have_next = have_next2;
-    }
-  }
-
-  const float lt = pair_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qvalid) {
-    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + qrow) * D;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * half;
-        const uint2 val = make_uint2(pack_bf16x2(acc[mt][4 * g] * inv, acc[mt][4 * g + 1] * inv),
-                                     pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv));
-        *reinterpret_cast<uint2 *>(O + d0) = val;
-      }
-    if (half == 0) a.out_lse[(size_t)bh * a.Tq + qrow] = lt > 0.f ? mref * a.scale + logf(lt) : -INFINITY;
-  }
-}
-
-// Key-split variant of k_fwd_bf16: 2*BS/32 waves per work group.  Wave w
+//
+// 2*BS/32 waves per work group.  Wave w
 // owns queries 32*(w % QW)..+31 (QW = BS/32) and keys 32*(w / QW)..+31 of
 // every 64-key chunk, so each wave keeps its own online-softmax state over
-// its half of the keys.  Twice the waves share each LDS chunk, which doubles
-// the waves per SIMD at the same LDS footprint.  At the end the second half's
+// its half of the keys.  Twice the waves share each LDS chunk, so each wave
+// needs about half the registers at the same LDS footprint: four waves per
+// SIMD at d = 64 (128 VGPRs), no spills at d = 128.  At the end the second half's
 // state (reference max, sum, O^T accumulator) goes through LDS and the
 // first-half wave merges the two, as two partial softmaxes over disjoint key
 // sets combine: m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m) (log2 units),
 // O = (acc0 2^(m0-m) + acc1 2^(m1-m)) / l.
 template <int MODE, int D, int BS, bool KROWS>
-__global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_fwd_bf16_ks(
+__global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void k_fwd_bf16_ks(
     AttnArgs a) {
   constexpr int QW = BS / 32;
   constexpr int NW = 2 * QW;
@@ -442,32 +274,42 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(4)
   }
 
   // Merge the two key halves.  No copy is in flight here (the last chunk
-  // issued none); the barrier ends every wave's reads of the chunk buffers
-  // before they are reused for the exchange.
+  // issued none); the first barrier ends every wave's reads of the chunk
+  // buffers before they are reused for the exchange.  The exchange goes in
+  // rounds of QX query waves when all QW do not fit the buffers at once.
   float lt = pair_sum(l);
   constexpr int XN = 2 + 16 * (D / 32);  // floats per lane: reference max, sum, accumulator
-  static_assert(sizeof(float) * XN * 64 * QW <= sizeof(sb), "exchange does not fit the chunk buffers");
-  float *xch = reinterpret_cast<float *>(sb) + (size_t)qw * XN * 64 + lane;
-  __syncthreads();
-  if (kh == 1) {
-    xch[0] = mref;
-    xch[64] = lt;
+  constexpr int FIT = (int)(sizeof(sb) / (sizeof(float) * XN * 64));
+  constexpr int QX = FIT >= QW ? QW : (FIT >= 2 ? 2 : 1);
+  static_assert(FIT >= 1 && QW % QX == 0, "exchange does not fit the chunk buffers");
+  float *xch = reinterpret_cast<float *>(sb) + (size_t)(qw % QX) * XN * 64 + lane;
+  float m = mref;
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
+  for (int round = 0; round < QW / QX; ++round) {
+    const bool mine = qw / QX == round;  // wave-uniform
+    __syncthreads();
+    if (kh == 1 && mine) {
+      xch[0] = mref;
+      xch[64] = lt;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xch[64 * (2 + 16 * mt + r)] = acc[mt][r];
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[64 * (2 + 16 * mt + r)] = acc[mt][r];
+    }
+    __syncthreads();
+    if (kh == 0 && mine) {
+      const float m1 = xch[0], l1 = xch[64];
+      m = fmaxf(mref, m1);
+      const float a0 = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mref - m) * c);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
+      lt = lt * a0 + l1 * a1;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] = acc[mt][r] * a0 + xch[64 * (2 + 16 * mt + r)] * a1;
+    }
   }
-  __syncthreads();
   if (kh == 1) return;
-  const float m1 = xch[0], l1 = xch[64];
-  const float m = fmaxf(mref, m1);
-  const float a0 = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mref - m) * c);
-  const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
-  lt = lt * a0 + l1 * a1;
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = acc[mt][r] * a0 + xch[64 * (2 + 16 * mt + r)] * a1;
 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qvalid) {
@@ -574,19 +416,10 @@ __global__ __launch_bounds__(BS) void k_fwd_f32(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
 static hipError_t run_fwd_bf16(const AttnArgs &a, hipStream_t s) {
-  if constexpr (BS == 64) {  // key-split kernel: four waves per SIMD at the same LDS
-    if (a.k_rows)
-      hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s,
-                         a);
-    else
-      hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s,
-                         a);
-    return hipGetLastError();
-  }
   if (a.k_rows)
-    hipLaunchKernelGGL((k_fwd_bf16<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
+    hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((k_fwd_bf16<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, a);
+    hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s, a);
   return hipGetLastError();
 }
 template <int MODE, int D, int BS>
