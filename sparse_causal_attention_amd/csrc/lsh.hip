@@ -308,47 +308,47 @@ __device__ __forceinline__ float wave_max_f(float v) {
 
 // Running top two of the projections of one token (largest and smallest p,
 // with the index of the first) over the columns a lane sees.
+// The two largest entries of z = [p, -p] are the largest |p_c| (as +p_c or
+// -p_c, by its sign) and the largest |p_c| over the other columns (the
+// opposite-sign entry of the winning column is <= 0 <= that), or -|p_c| when
+// there is a single column.  So the kernel tracks the top two of |p| over
+// distinct columns, the winner's column and its signed value.
 struct Top2 {
-  float mx1, mx2, mn1, mn2;
-  int imx, imn;
+  float a1, a2;  // largest |p|, second largest over the other columns
+  float v1;      // signed p of the largest
+  int i1;        // its column
 };
 
 __device__ __forceinline__ void top2_init(Top2 &t) {
-  t.mx1 = t.mx2 = -INFINITY;
-  t.mn1 = t.mn2 = INFINITY;
-  t.imx = t.imn = 0;
+  t.a1 = t.a2 = -INFINITY;
+  t.v1 = 0.f;
+  t.i1 = 0;
 }
 
-// Branch-free: the new second value is the median of (first, second, v);
-// an equal value lands in the second slot (gap 0) and keeps the first index.
-__device__ __forceinline__ void top2_add(Top2 &t, float vmax, float vmin, int c) {
-  t.imx = vmax > t.mx1 ? c : t.imx;
-  t.mx2 = __builtin_amdgcn_fmed3f(t.mx1, t.mx2, vmax);
-  t.mx1 = fmaxf(t.mx1, vmax);
-  t.imn = vmin < t.mn1 ? c : t.imn;
-  t.mn2 = __builtin_amdgcn_fmed3f(t.mn1, t.mn2, vmin);
-  t.mn1 = fminf(t.mn1, vmin);
+// Branch-free: the new second value is the median of (first, second, |v|); an
+// equal value lands in the second slot (gap 0) and keeps the first column.
+// Columns that take no part pass a = -inf.
+__device__ __forceinline__ void top2_add(Top2 &t, float v, float a, int c) {
+  const bool gt = a > t.a1;
+  t.i1 = gt ? c : t.i1;
+  t.v1 = gt ? v : t.v1;
+  t.a2 = __builtin_amdgcn_fmed3f(t.a1, t.a2, a);
+  t.a1 = fmaxf(t.a1, a);
 }
 
 // Merge with the state of lane l ^ 32 (the other 16 columns of each tile).
 __device__ __forceinline__ void top2_merge_pair(Top2 &t) {
-  const float omx1 = __shfl_xor(t.mx1, 32, 64), omx2 = __shfl_xor(t.mx2, 32, 64);
-  const float omn1 = __shfl_xor(t.mn1, 32, 64), omn2 = __shfl_xor(t.mn2, 32, 64);
-  const int oimx = __shfl_xor(t.imx, 32, 64), oimn = __shfl_xor(t.imn, 32, 64);
+  const float oa1 = __shfl_xor(t.a1, 32, 64), oa2 = __shfl_xor(t.a2, 32, 64);
+  const float ov1 = __shfl_xor(t.v1, 32, 64);
+  const int oi1 = __shfl_xor(t.i1, 32, 64);
   // candidates are distinct columns; equal values end up in both slots (gap 0)
-  if (omx1 > t.mx1 || (omx1 == t.mx1 && oimx < t.imx)) {
-    t.mx2 = fmaxf(t.mx1, omx2);
-    t.mx1 = omx1;
-    t.imx = oimx;
+  if (oa1 > t.a1 || (oa1 == t.a1 && oi1 < t.i1)) {
+    t.a2 = fmaxf(t.a1, oa2);
+    t.a1 = oa1;
+    t.i1 = oi1;
+    t.v1 = ov1;
   } else {
-    t.mx2 = fmaxf(t.mx2, omx1);
-  }
-  if (omn1 < t.mn1 || (omn1 == t.mn1 && oimn < t.imn)) {
-    t.mn2 = fminf(t.mn1, omn2);
-    t.mn1 = omn1;
-    t.imn = oimn;
-  } else {
-    t.mn2 = fminf(t.mn2, omn1);
+    t.a2 = fmaxf(t.a2, oa1);
   }
 }
 
@@ -432,15 +432,15 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 32 * ct + 8 * (r >> 2) + 4 * hf + (r & 3);
-        top2_add(t2[0], acc0[r], acc0[r], c);
-        top2_add(t2[1], acc1[r], acc1[r], c);
+        top2_add(t2[0], acc0[r], fabsf(acc0[r]), c);
+        top2_add(t2[1], acc1[r], fabsf(acc1[r]), c);
       }
     } else {  // columns past nb/2 take no part
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 32 * ct + 8 * (r >> 2) + 4 * hf + (r & 3);
-        top2_add(t2[0], c < half ? acc0[r] : -INFINITY, c < half ? acc0[r] : INFINITY, c);
-        top2_add(t2[1], c < half ? acc1[r] : -INFINITY, c < half ? acc1[r] : INFINITY, c);
+        top2_add(t2[0], acc0[r], c < half ? fabsf(acc0[r]) : -INFINITY, c);
+        top2_add(t2[1], acc1[r], c < half ? fabsf(acc1[r]) : -INFINITY, c);
       }
     }
     if (more)
@@ -456,17 +456,8 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint
     Top2 &t = t2[n];
     top2_merge_pair(t);
     // top two of z = [p, -p]
-    float z1, z2;
-    int iz;
-    if (t.mx1 >= -t.mn1) {
-      z1 = t.mx1;
-      iz = t.imx;
-      z2 = fmaxf(t.mx2, -t.mn1);
-    } else {
-      z1 = -t.mn1;
-      iz = half + t.imn;
-      z2 = fmaxf(t.mx1, -t.mn2);
-    }
+    const float z1 = t.a1, z2 = fmaxf(t.a2, -t.a1);
+    const int iz = t.v1 < 0.f ? half + t.i1 : t.i1;
     const float prod = xn[n] * rm;
     const float err = kErr * prod + 0x1p-100f * xn[n];
     const bool certified = prod < 1e37f && (z1 - z2) > 2.f * err + 0x1p-20f * (fabsf(z1) + fabsf(z2));
