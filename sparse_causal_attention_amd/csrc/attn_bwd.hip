@@ -286,9 +286,9 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sub][r] = __builtin_amdgcn_exp2f(fmaf(s[sub][r], c, -lse2));
     if (cur.nvalid < kChunk)
-      mask_rows<MODE, true, true>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+      mask_rows<MODE, true>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
     else if (!cur.free)
-      mask_rows<MODE, false, true>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
+      mask_rows<MODE, false>(s, b.idx, b.hash, cur.r0, cur.nvalid, my_idx, my_hash, half, 0.f);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll

@@ -13,9 +13,9 @@
 // The row-fragment reads (eight consecutive rows, one logical piece) then hit
 // eight different pieces, and the transposed reads (four rows 4h..4h+3 at a
 // logical piece pair) hit four different piece pairs, so neither conflicts on
-// the LDS banks.  The swizzle is applied through the DMA source addresses.  Rows past the end of
-// the sequence are filled with copies of the last real row (finite values);
-// the kernels mask them explicitly.
+// the LDS banks.  The swizzle is applied through the DMA source addresses.
+// Rows past the end of the sequence are filled with copies of the last real
+// row (finite values); the kernels mask them explicitly.
 //
 // Fragment reads for v_mfma_f32_32x32x16_bf16 (lane l, col = l % 32,
 // half = l / 32):
@@ -32,8 +32,6 @@
 #pragma once
 
 #include "scfa_device.hpp"
-
-
 
 namespace scfa {
 
@@ -299,13 +297,12 @@ __device__ __forceinline__ uint4 c_regs_to_u4(const f32x16 &c, int t) {
 }
 
 // Element mask over a pair of C tiles whose rows are chunk rows r0 + 32*sub +
-// 8g + 4*half + e.  LANE_IS_QUERY: the lane's column is a query (my_idx is a
-// query position, rows are keys): admissible iff row_idx <= my_idx.
-// Otherwise the lane's column is a key and rows are queries: admissible iff
-// my_idx <= row_idx.  Hash mode also needs equal bucket ids; with TAIL, rows at
-// or past nvalid (copies of a real row) are inadmissible.  Inadmissible entries
-// are replaced by `fill`.  Branch-free (compare + select).
-template <int MODE, bool TAIL, bool LANE_IS_QUERY>
+// 8g + 4*half + e.  The lane's column is a query (my_idx is a query position,
+// rows are keys): admissible iff row_idx <= my_idx.  Hash mode also needs
+// equal bucket ids; with TAIL, rows at or past nvalid (copies of a real row)
+// are inadmissible.  Inadmissible entries are replaced by `fill`.
+// Branch-free (compare + select).
+template <int MODE, bool TAIL>
 __device__ __forceinline__ void mask_rows(f32x16 (&s)[2], const int *sidx, const int *shash, int r0, int nvalid,
                                           int my_idx, int my_hash, int half, float fill) {
 #pragma unroll
@@ -327,7 +324,7 @@ __device__ __forceinline__ void mask_rows(f32x16 (&s)[2], const int *sidx, const
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        bool ok = LANE_IS_QUERY ? iv[e] <= my_idx : my_idx <= iv[e];
+        bool ok = iv[e] <= my_idx;
         if (MODE == kHash) ok = ok & (hv[e] == my_hash);
         if (TAIL) ok = ok & (rr + e < nvalid);
         s[sub][4 * g + e] = ok ? s[sub][4 * g + e] : fill;
