@@ -562,6 +562,14 @@ def main():
         "algorithmic_flops_per_launch": kernel_flops[dominant],
     }
 
+    # the same figures for each attention kernel (context; "roofline" is the dominant one)
+    names = {"fwd": "k_fwd_bf16_ks", "bwd_dq": "k_bwd_dq_bf16", "bwd_dkdv": "k_bwd_dkdv_bf16"}
+    kernel_rooflines = {
+        n: {"kernel": names[n], "achieved": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12, 2),
+            "frac": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": per_call[n], "algorithmic_flops_per_launch": kernel_flops[n]}
+        for n in kernel_flops}
+
     cpu = None
     if not args.no_cpu_baseline:
         _log("[bench] cpu oracle baseline (one head)")
@@ -605,6 +613,7 @@ def main():
         "per_call_ms": per_call,
         "dense_per_call_ms": None if args.no_dense else {n: round(dtimer.mean_ms(n), 4) for n in DENSE_CALLS},
         "roofline": roofline,
+        "kernel_rooflines": kernel_rooflines,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -286,3 +286,33 @@ def test_row_indirection_bit_identical(mode, d, block, Tq, Tk):
     torch.cuda.synchronize()
     for a_, b_ in [(o1, o2), (l1, l2), (dq1, dq2), (de1, de2), (dk1, dk2), (dv1, dv2)]:
         assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("d,block", [(64, 64), (128, 128)])
+def test_key_half_merge_with_one_empty_half_and_wide_scores(d, block):
+    """The forward splits every 64-key chunk into two halves handled by different waves and merges
+    their softmax states at the end.  Keys 0-31 of every chunk are in bucket 0 and keys 32-63 in
+    bucket 1, so each query's admissible keys all lie in its bucket's half of each chunk and the
+    other half's state stays empty (reference max -inf); random query positions also leave some
+    rows with no admissible key at all and cut others inside a chunk.  Scores are widened (inputs
+    scaled by 4, score std about 16) so the lazy rescale fires often and the merge's factors span a
+    wide range."""
+    rng = np.random.default_rng(71 + d)
+    B, H, Tq, Tk = 1, 2, 320, 448
+    q = bf16_round(4.0 * rng.standard_normal((B, H, Tq, d), dtype=np.float32))
+    k = bf16_round(4.0 * rng.standard_normal((B, H, Tk, d), dtype=np.float32))
+    v = bf16_round(rng.standard_normal((B, H, Tk, d), dtype=np.float32))
+    k_hash = np.broadcast_to(((np.arange(Tk) % 64) >= 32).astype(np.int32), (B, H, Tk)).copy()
+    k_idx = np.broadcast_to(np.arange(Tk, dtype=np.int32) * 2, (B, H, Tk)).copy()
+    q_hash = np.broadcast_to((np.arange(Tq) % 2).astype(np.int32), (B, H, Tq)).copy()
+    q_idx = np.broadcast_to(rng.integers(0, 2 * Tk + 8, size=Tq).astype(np.int32), (B, H, Tq)).copy()
+    note(f"[key-half merge] d={d} block={block}")
+    scfa = _lib()
+    tq, tk, tv = (dev(x, torch.bfloat16) for x in (q, k, v))
+    o, lse = scfa.hash_sparse_fwd(tq, tk, tv, dev(q_idx), dev(k_idx), dev(q_hash), dev(k_hash), block=block)
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(d)
+    for h in range(H):
+        o_ref, lse_ref = A.forward(q[0, h], k[0, h], v[0, h], q_idx[0, h], k_idx[0, h], q_hash[0, h], k_hash[0, h],
+                                   scale)
+        check_forward(to_np(o[0, h]), to_np(lse[0, h]), o_ref, lse_ref, "bf16", f"key-half merge h={h}")
