@@ -543,10 +543,13 @@ def main():
 
     per_call = {n: round(timer.mean_ms(n), 4) for n in calls}
     attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
-    # algorithmic flops per launch of each attention kernel (tile units x d)
+    # executed matrix flops per launch of each attention kernel (tile units x d); all algorithmic except the
+    # dQ kernel's recompute of Q K^T and dO V^T
     kernel_flops = {"fwd": 4.0 * units * w.d, "bwd_dq": 6.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
+    # algorithmic flops per launch: the dQ kernel's share is dS K only (2*d per tile unit)
+    alg = {"fwd": 4.0 * units * w.d, "bwd_dq": 2.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
     dominant = max(kernel_flops, key=lambda n: per_call[n])
-    achieved = kernel_flops[dominant] / (per_call[dominant] * 1e-3) / 1e12
+    achieved = alg[dominant] / (per_call[dominant] * 1e-3) / 1e12
     roofline = {
         "kernel": {"fwd": "k_fwd_bf16_ks<kHash,64,64,%s>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64,%s>",
                    "bwd_dkdv": "k_bwd_dkdv_bf16<kHash,64,64,%s>"}[dominant] % (
@@ -559,15 +562,18 @@ def main():
         "traffic": (measured_traffic("range" if args.range_lists else "exact", "copied" if args.copy_sorted else
                                      "permuted") if dominant == "bwd_dkdv" else None),
         "avg_launch_ms": per_call[dominant],
-        "algorithmic_flops_per_launch": kernel_flops[dominant],
+        "algorithmic_flops_per_launch": alg[dominant],
     }
 
-    # the same figures for each attention kernel (context; "roofline" is the dominant one)
+    # each attention kernel's executed matrix flops per launch over its event time (context; "roofline" is
+    # the dominant kernel's).  The dQ kernel executes 6*d per tile unit, of which 2*d (dS K) is algorithmic:
+    # it recomputes Q K^T and dO V^T, which the dK/dV kernel's 8*d already counts.
     names = {"fwd": "k_fwd_bf16_ks", "bwd_dq": "k_bwd_dq_bf16", "bwd_dkdv": "k_bwd_dkdv_bf16"}
     kernel_rooflines = {
-        n: {"kernel": names[n], "achieved": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12, 2),
-            "frac": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "avg_launch_ms": per_call[n], "algorithmic_flops_per_launch": kernel_flops[n]}
+        n: {"kernel": names[n], "executed_tflops": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12, 2),
+            "executed_frac": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": per_call[n], "executed_flops_per_launch": kernel_flops[n],
+            "algorithmic_flops_per_launch": alg[n]}
         for n in kernel_flops}
 
     cpu = None
