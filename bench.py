@@ -163,16 +163,29 @@ class Timer:
                 self.samples[n].append(a.elapsed_time(b))
         self.pending = []
 
-    def mean_ms(self, n):
-        s = self.samples[n]
-        return sum(s) / len(s) if s else float("nan")
+    def median_ms(self, n):
+        s = sorted(self.samples[n])
+        if not s:
+            return float("nan")
+        m = len(s) // 2
+        return s[m] if len(s) % 2 else 0.5 * (s[m - 1] + s[m])
+
+    def step_median_ms(self):
+        """Median over steps of the event time from the first call's start to the last call's end."""
+        tot = sorted(sum(self.samples[n][i] for n in self.names) for i in range(len(self.samples[self.names[0]])))
+        if not tot:
+            return float("nan")
+        m = len(tot) // 2
+        return tot[m] if len(tot) % 2 else 0.5 * (tot[m - 1] + tot[m])
 
 
 def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False, qk=None):
     """One step.  By default the sorts return only bucket ids, positions and the permutations, and
     the attention kernels read Q, dO, K and V through the permutations (row indirection); with
     copy_sorted the sorts also copy the rows into sorted order and attention reads the copies.
-    Outputs (O, lse, dQ, dK, dV) are in sorted order either way, bit-identical.
+    Outputs (O, lse, dQ, dK, dV) are in sorted order either way, bit-identical.  The returned
+    metadata dict also holds the sort results (bucket ids, positions and, for the permuted view,
+    the permutations).
 
     With qk (Q and K stacked in one [2B, H, T, d] allocation, q and k its halves) and rows read
     through the permutations, one LSH + sort call serves both tensors."""
@@ -203,6 +216,8 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False,
     meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=True, exact=exact)
     if timer:
         timer.mark()
+    meta.update(q_hash=qh, q_idx=qi, k_hash=kh, k_idx=ki, **({"q_perm": rows["q_rows"], "k_perm": rows["k_rows"]}
+                                                             if rows else {}))
     o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc, **rows)
     if timer:
         timer.mark()
@@ -424,7 +439,7 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, qk, nbs, args):
                                     args.warmup, timer)
         timer.collect()
         units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
-        per_call = {n: round(timer.mean_ms(n), 4) for n in calls}
+        per_call = {n: round(timer.median_ms(n), 4) for n in calls}
         attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
         nq = (w.T + w.block - 1) // w.block
         print(json.dumps({
@@ -541,7 +556,7 @@ def main():
         torch.cuda.synchronize()
         dtimer.collect()
 
-    per_call = {n: round(timer.mean_ms(n), 4) for n in calls}
+    per_call = {n: round(timer.median_ms(n), 4) for n in calls}
     attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
     # executed matrix flops per launch of each attention kernel (tile units x d); all algorithmic except the
     # dQ kernel's recompute of Q K^T and dO V^T
@@ -617,7 +632,9 @@ def main():
         "speedup_vs_dense_causal": None if args.no_dense else round(dense_ms / ms_per_step, 3),
         "speedup_vs_dense_causal_excl_lsh": None if args.no_dense else round(dense_ms / attn_ms, 3),
         "per_call_ms": per_call,
-        "dense_per_call_ms": None if args.no_dense else {n: round(dtimer.mean_ms(n), 4) for n in DENSE_CALLS},
+        "step_median_ms_events": round(timer.step_median_ms(), 4),
+        "per_call_stat": f"median of {args.steps} HIP-event samples per call",
+        "dense_per_call_ms": None if args.no_dense else {n: round(dtimer.median_ms(n), 4) for n in DENSE_CALLS},
         "roofline": roofline,
         "kernel_rooflines": kernel_rooflines,
         "cpu_baseline": cpu,

@@ -103,6 +103,7 @@ extern "C" {
 #define SCFA_OP_HASH_FWD 2
 #define SCFA_OP_HASH_BWD 3
 #define SCFA_OP_LSH_SORT 4
+#define SCFA_OP_BLOCK_META_EXACT 5
 
 /*
  * QK-sparse forward ("1. QK-Sparse": compact Q/K/V plus the original indices
@@ -123,6 +124,12 @@ int scfa_qk_sparse_fwd(const void *q, const void *k, const void *v,
 /*
  * QK-sparse backward: gradients of sum(O * dout) with respect to q, k, v,
  * recomputing P from the forward's lse (no T x T state is kept).
+ *   Source: the page describes no backward pass.  Its LM-training results
+ *   ("实验与结果" > "QK-Sparse LM training", Fig. 8: the model that drops 30 %
+ *   of queries and keys trains 1.9x faster) need one; this is the analytic
+ *   gradient of the forward above: dV = P^T dO, dS = P * (dO V^T - D) with
+ *   D_i = dO_i . O_i, dQ = scale dS K, dK = scale dS^T Q, over the same live
+ *   tiles and element mask.
  *   o and lse must be the forward's outputs for the same inputs; dout is
  *   [B,H,Tq,d].  Outputs dq [B,H,Tq,d], dk and dv [B,H,Tk,d] (dtype), fully
  *   overwritten.  Rows with no valid key contribute nothing.
@@ -149,7 +156,13 @@ int scfa_hash_sparse_fwd(const void *q, const void *k, const void *v,
                          int dtype, unsigned flags,
                          void *workspace, size_t workspace_bytes, void *stream);
 
-/* Hash-sparse backward; arguments as scfa_qk_sparse_bwd plus q_hash, k_hash. */
+/*
+ * Hash-sparse backward; arguments as scfa_qk_sparse_bwd plus q_hash, k_hash.
+ *   Source: as for the QK-sparse backward, the page gives no backward; its
+ *   Hash-sparse LM-training results ("实验与结果" > "Hash-Sparse LM training",
+ *   Fig. 6: 2.0x at 8k and 3.3x at 16k tokens, and the introduction) need one.
+ *   Same analytic gradient, with the Hash-sparse element mask.
+ */
 int scfa_hash_sparse_bwd(const void *q, const void *k, const void *v,
                          const void *o, const float *lse, const void *dout,
                          const int32_t *q_idx, const int32_t *k_idx,
@@ -211,30 +224,31 @@ int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx,
 
 /*
  * scfa_block_meta with exact tile liveness in Hash-sparse mode.  The page's
- * block rule ("2. Hash-Sparse" rules 1-2) keeps a tile when the blocks'
- * bucket ranges overlap, which also keeps tiles where every bucket the blocks
- * share has all its keys after all its queries; such a tile holds no valid
- * pair.  Here a tile is live iff it passes the range test and some bucket h
- * present in both blocks has min k_idx over the key rows of bucket h <= max
- * q_idx over the query rows of bucket h, which is exactly "the tile holds a
- * valid pair".  A block with more than 3 distinct buckets keeps the range
- * test's answer for its tiles.  Mask-free flags, list layout and all other
- * arguments are as in scfa_block_meta; attention over these lists gives
- * bit-identical results (a skipped tile would only add exact zeros).
- *   q_segs [B,H,nq,16], k_segs [B,H,nk,16] int32, 16-byte aligned, written:
- *   per block, [0] = number of distinct buckets if <= 3, else -1; [1..3] = 0;
- *   then 3 records (bucket, min idx, max idx, 0) in ascending bucket order
- *   (unused records 0; all records 0 when [0] is -1).  In QK-sparse mode (hashes NULL) the range test is
- *   already exact: segs may be NULL, are not written, and the lists equal
- *   scfa_block_meta's.
+ * block rule ("2. Hash-Sparse" rules 1-2: keep the tiles whose query and key
+ * buckets match, drop the acausal ones) read literally keeps a tile only when
+ * one of its queries and one of its keys share a bucket in causal order, i.e.
+ * when the tile holds a valid pair.  The bucket-range test of scfa_block_meta
+ * also keeps tiles where every bucket the blocks share has all its keys after
+ * all its queries.  Here a tile is live iff it passes the range test and some
+ * bucket h present in both blocks has min k_idx over the key rows of bucket h
+ * <= max q_idx over the query rows of bucket h, which is exactly "the tile
+ * holds a valid pair", for any number of distinct buckets per block.
+ * Mask-free flags, list layout and the other arguments are as in
+ * scfa_block_meta; attention over these lists gives bit-identical results (a
+ * skipped tile would only add exact zeros).  In QK-sparse mode (hashes NULL)
+ * the range test is already exact and the lists equal scfa_block_meta's.
+ *   workspace: device scratch of scfa_workspace_size(SCFA_OP_BLOCK_META_EXACT,
+ *   B, H, Tq, Tk, 0, block, 0) bytes, 256-byte aligned (per block: one record
+ *   per distinct bucket with the min and max position of its rows); unused
+ *   (may be NULL) in QK-sparse mode.
  */
 int scfa_block_meta_exact(const int32_t *q_idx, const int32_t *k_idx,
                           const int32_t *q_hash, const int32_t *k_hash,
                           int B, int H, int Tq, int Tk, int block,
                           int32_t *q_stats, int32_t *k_stats,
-                          int32_t *q_segs, int32_t *k_segs,
                           int32_t *row_count, int32_t *row_list,
-                          int32_t *col_count, int32_t *col_list, void *stream);
+                          int32_t *col_count, int32_t *col_list,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Attention over precomputed block lists: the single-kernel building blocks of
@@ -322,8 +336,8 @@ int scfa_scatter_rows(const void *src, const int32_t *index, void *dst,
 
 /*
  * Bytes of workspace an operation needs (0 for invalid arguments).  For the
- * attention ops d and n_buckets are ignored; for SCFA_OP_LSH_SORT Tq is the
- * sequence length T and Tk, d, block are ignored.  The size is an upper
+ * attention ops and SCFA_OP_BLOCK_META_EXACT d and n_buckets are ignored; for
+ * SCFA_OP_LSH_SORT Tq is the sequence length T and Tk, d, block are ignored.  The size is an upper
  * bound valid for every flag combination.
  */
 size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int block, int n_buckets);

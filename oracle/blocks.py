@@ -22,14 +22,11 @@ Tile (i, j) pairs query block i with key block j.
 * Lists.  Row list of query block i: live key blocks j in ascending order
   (forward and dQ); column list of key block j: live query blocks i in
   ascending order (dK/dV).
-* Exact liveness (a stricter reading of "2. Hash-Sparse" rule 1: keep the
-  tiles whose buckets match).  A tile that passes the range test can still
-  hold no valid pair.  With the distinct buckets of each block and, per
-  bucket, the min and max original position of its rows ("segments"), a tile
-  holds a valid pair iff some bucket h occurs in both blocks with
-  min(k_idx over the key rows of h) <= max(q_idx over the query rows of h).
-  Exact liveness is that test on top of the range test; for a block with
-  more than MAX_SEGS distinct buckets the range test's answer is kept.
+* Exact liveness (the literal reading of "2. Hash-Sparse" rules 1 and 2: keep
+  a tile only when a query and a key of it share a bucket, in causal order).
+  A tile is exactly live iff it holds at least one admissible pair of the
+  element mask.  ``tile_has_pair`` evaluates that from the mask itself, with
+  no summary of the blocks; in QK-sparse mode it equals the range rule.
 """
 
 from __future__ import annotations
@@ -62,47 +59,6 @@ def block_stats(idx: np.ndarray, hsh: Optional[np.ndarray], block: int) -> np.nd
             hs = np.asarray(hsh, dtype=np.int64)[r0:r1]
             out[b, 2], out[b, 3] = hs.min(), hs.max()
     return out
-
-
-MAX_SEGS = 3
-SEG_INTS = 4 + 4 * MAX_SEGS
-
-
-def block_segments(idx: np.ndarray, hsh: np.ndarray, block: int) -> np.ndarray:
-    """int64 [nblocks, SEG_INTS]: per block, [0] = number of distinct buckets if
-    at most MAX_SEGS, else -1; then MAX_SEGS records (bucket, min idx, max idx, 0)
-    in ascending bucket order (zero when unused, and all zero when the count is -1).
-    """
-    idx = np.asarray(idx, dtype=np.int64)
-    hsh = np.asarray(hsh, dtype=np.int64)
-    T = idx.shape[0]
-    nb = n_blocks(T, block)
-    out = np.zeros((nb, SEG_INTS), dtype=np.int64)
-    for b in range(nb):
-        r0, r1 = b * block, min((b + 1) * block, T)
-        buckets = sorted(set(int(h) for h in hsh[r0:r1]))
-        if len(buckets) > MAX_SEGS:
-            out[b, 0] = -1
-            continue
-        out[b, 0] = len(buckets)
-        for s, h in enumerate(buckets):
-            rows = [int(idx[r]) for r in range(r0, r1) if hsh[r] == h]
-            out[b, 4 + 4 * s : 4 + 4 * s + 3] = (h, min(rows), max(rows))
-    return out
-
-
-def segments_admit(qseg: np.ndarray, kseg: np.ndarray) -> bool:
-    """Some bucket present in both blocks has a key at or before one of its queries
-    (True when either block has more than MAX_SEGS buckets)."""
-    if qseg[0] < 0 or kseg[0] < 0:
-        return True
-    for s in range(int(qseg[0])):
-        qh, _, qmax = qseg[4 + 4 * s : 4 + 4 * s + 3]
-        for t in range(int(kseg[0])):
-            kh, kmin, _ = kseg[4 + 4 * t : 4 + 4 * t + 3]
-            if qh == kh and kmin <= qmax:
-                return True
-    return False
 
 
 def tile_live(qs: np.ndarray, ks: np.ndarray, hash_mode: bool) -> np.ndarray:
@@ -155,6 +111,35 @@ def metadata(
     return qs, ks, tile_live(qs, ks, hash_mode), tile_maskfree(qs, ks, hash_mode)
 
 
+def tile_has_pair(
+    q_idx: np.ndarray,
+    k_idx: np.ndarray,
+    q_hash: Optional[np.ndarray],
+    k_hash: Optional[np.ndarray],
+    block: int,
+) -> np.ndarray:
+    """bool [nq, nk]: tile (i, j) holds at least one admissible (query, key) pair.
+
+    Evaluated from the element mask itself, one query block at a time: the
+    mask rows of block i are reduced with ``any`` over each key block's
+    columns.  This is exact liveness: "2. Hash-Sparse" rule 1 keeps the tiles
+    whose buckets match, rule 2 drops the acausal ones, and a tile survives
+    both on some pair exactly when that pair is admissible.
+    """
+    Tq, Tk = len(q_idx), len(k_idx)
+    nq, nk = n_blocks(Tq, block), n_blocks(Tk, block)
+    out = np.zeros((nq, nk), dtype=bool)
+    if Tk == 0:
+        return out
+    k_block = np.arange(Tk) // block
+    for i in range(nq):
+        r0, r1 = i * block, min((i + 1) * block, Tq)
+        m = attention.element_mask(q_idx[r0:r1], k_idx, None if q_hash is None else q_hash[r0:r1], k_hash)
+        hit = m.any(axis=0)
+        out[i, np.unique(k_block[hit])] = True
+    return out
+
+
 def metadata_exact(
     q_idx: np.ndarray,
     k_idx: np.ndarray,
@@ -162,18 +147,9 @@ def metadata_exact(
     k_hash: Optional[np.ndarray],
     block: int,
 ):
-    """Stats, segments (None without hashes), exact live and mask-free matrices."""
-    qs, ks, live, free = metadata(q_idx, k_idx, q_hash, k_hash, block)
-    if q_hash is None:
-        return qs, ks, None, None, live, free
-    qseg = block_segments(q_idx, q_hash, block)
-    kseg = block_segments(k_idx, k_hash, block)
-    live = live.copy()
-    for i in range(live.shape[0]):
-        for j in range(live.shape[1]):
-            if live[i, j]:
-                live[i, j] = segments_admit(qseg[i], kseg[j])
-    return qs, ks, qseg, kseg, live, free
+    """Stats, exact live and mask-free matrices for one head (live = tile_has_pair)."""
+    qs, ks, _, free = metadata(q_idx, k_idx, q_hash, k_hash, block)
+    return qs, ks, tile_has_pair(q_idx, k_idx, q_hash, k_hash, block), free
 
 
 def forward_live_tiles_only(
@@ -196,7 +172,7 @@ def forward_live_tiles_only(
     """
     q = np.asarray(q, dtype=np.float64)
     if exact:
-        live = metadata_exact(q_idx, k_idx, q_hash, k_hash, block)[4]
+        live = metadata_exact(q_idx, k_idx, q_hash, k_hash, block)[2]
     else:
         _, _, live, _ = metadata(q_idx, k_idx, q_hash, k_hash, block)
     Tq, Tk = q.shape[0], np.asarray(k).shape[0]

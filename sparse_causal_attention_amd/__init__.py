@@ -197,12 +197,12 @@ def lsh_bucket_sort(x, R, n_buckets, idx=None, companion=None, *, idx_ascending=
     return hs, ids, perm, xs, cs
 
 
-def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=True, exact=False):
+def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=True, exact=False, workspace=None):
     """Block statistics and live-tile lists (see include/scfa.h, scfa_block_meta).
 
     ``exact=True`` calls scfa_block_meta_exact: in Hash-sparse mode the lists
-    also drop tiles that pass the bucket-range test yet hold no valid pair, and
-    the per-block bucket segments are returned as "q_segs" / "k_segs".
+    also drop tiles that pass the bucket-range test yet hold no valid pair.
+    ``workspace`` optionally supplies its scratch (uint8, see workspace_size).
     """
     B, H, Tq = q_idx.shape
     Tk = k_idx.shape[2]
@@ -223,12 +223,12 @@ def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=Tr
         out["col_list"] = torch.empty((B, H, nk, nq), dtype=torch.int32, device=dev)
     lists = (_ptr(out["row_count"]), _ptr(out["row_list"]), _ptr(out.get("col_count")), _ptr(out.get("col_list")))
     if exact:
+        ws, nws = (None, 0)
         if q_hash is not None:
-            out["q_segs"] = torch.empty((B, H, nq, 16), dtype=torch.int32, device=dev)
-            out["k_segs"] = torch.empty((B, H, nk, 16), dtype=torch.int32, device=dev)
+            ws, nws = _workspace(_lib.OP_BLOCK_META_EXACT, B, H, Tq, Tk, 0, block, dev, workspace=workspace)
         rc = _LIB.scfa_block_meta_exact(_ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), B, H, Tq, Tk, block,
-                                        _ptr(out["q_stats"]), _ptr(out["k_stats"]), _ptr(out.get("q_segs")),
-                                        _ptr(out.get("k_segs")), *lists, _stream())
+                                        _ptr(out["q_stats"]), _ptr(out["k_stats"]), *lists, _ptr(ws), nws,
+                                        _stream())
         _lib.check("scfa_block_meta_exact", rc)
     else:
         rc = _LIB.scfa_block_meta(_ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), B, H, Tq, Tk, block,

@@ -50,6 +50,7 @@ OP_QK_BWD = 1
 OP_HASH_FWD = 2
 OP_HASH_BWD = 3
 OP_LSH_SORT = 4
+OP_BLOCK_META_EXACT = 5
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -67,7 +68,7 @@ _SIGNATURES = {
     "scfa_hash_sparse_bwd": [_p] * 13 + _ATTN_TAIL,
     "scfa_lsh_bucket_sort": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_block_meta": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p],
-    "scfa_block_meta_exact": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p],
+    "scfa_block_meta_exact": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_attn_fwd_lists": [_p] * 13 + _LISTS_TAIL,
     "scfa_attn_bwd_dq_lists": [_p] * 16 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_lists": [_p] * 16 + _LISTS_TAIL,

@@ -34,8 +34,8 @@ int hip_fail(hipError_t e, const char *where) {
   return fail(SCFA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
 }
 
-constexpr size_t kAlign = 256;
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr size_t kAlign = scfa::kWsAlign;
+size_t round_up(size_t x) { return scfa::ws_round(x); }
 int nblocks(int T, int block) { return (T + block - 1) / block; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -71,7 +71,7 @@ size_t attn_ws(bool bwd, int B, int H, int Tq, int Tk, int block) {
   const size_t BH = (size_t)B * H;
   const size_t nq = nblocks(Tq, block), nk = nblocks(Tk, block);
   size_t n = round_up(BH * nq * 16) + round_up(BH * nk * 16) + round_up(BH * nq * 4) + round_up(BH * nq * nk * 4) +
-             round_up(BH * nq * scfa::kSegInts * 4) + round_up(BH * nk * scfa::kSegInts * 4);
+             scfa::meta_seg_bytes(BH, nq, nk, block);
   if (bwd) n += round_up(BH * nk * 4) + round_up(BH * nk * nq * 4) + round_up(2 * BH * (size_t)Tq * 4);
   return n;
 }
@@ -242,9 +242,11 @@ int attention(const AttnCall &c) {
       m.k_stats = cv.take<int32_t>((size_t)BH * nk * 16);
       m.row_cnt = cv.take<int32_t>((size_t)BH * nq * 4);
       m.row_list = cv.take<int32_t>((size_t)BH * nq * nk * 4);
-      int32_t *qsg = cv.take<int32_t>((size_t)BH * nq * scfa::kSegInts * 4);
-      int32_t *ksg = cv.take<int32_t>((size_t)BH * nk * scfa::kSegInts * 4);
-      if (hashed) m.q_segs = qsg, m.k_segs = ksg;  // exact tile test
+      int32_t *qsg = cv.take<int32_t>((size_t)BH * nq * s.block * 16);
+      int32_t *ksg = cv.take<int32_t>((size_t)BH * nk * s.block * 16);
+      int32_t *qns = cv.take<int32_t>((size_t)BH * nq * 4);
+      int32_t *kns = cv.take<int32_t>((size_t)BH * nk * 4);
+      if (hashed) m.q_segs = qsg, m.k_segs = ksg, m.q_nseg = qns, m.k_nseg = kns;  // exact tile test
       if (bwd) {
         m.col_cnt = cv.take<int32_t>((size_t)BH * nk * 4);
         m.col_list = cv.take<int32_t>((size_t)BH * nk * nq * 4);
@@ -289,9 +291,8 @@ size_t lsh_ws(int B, int H, int T, int d, int nb) {
 }
 
 int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B, int H,
-              int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, int32_t *q_segs, int32_t *k_segs,
-              bool exact, int32_t *row_count, int32_t *row_list, int32_t *col_count, int32_t *col_list,
-              void *stream) {
+              int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, bool exact, int32_t *row_count,
+              int32_t *row_list, int32_t *col_count, int32_t *col_list, void *ws, size_t ws_bytes, void *stream) {
   if (B < 1 || H < 1 || Tq < 0 || Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tk >= 0 required");
   if (block != 64 && block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
   if ((q_hash == nullptr) != (k_hash == nullptr))
@@ -313,9 +314,7 @@ int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
                     (rc = check_ptr(col_list, BH * nk * nq, 4, "col_list"))))
     return rc;
   const bool use_segs = exact && q_hash != nullptr;  // QK-sparse: the range test is already exact
-  if (use_segs && ((rc = check_ptr(q_segs, BH * nq * scfa::kSegInts, 16, "q_segs")) ||
-                   (rc = check_ptr(k_segs, BH * nk * scfa::kSegInts, 16, "k_segs"))))
-    return rc;
+  if (use_segs && (rc = check_ws(ws, ws_bytes, scfa::meta_seg_bytes(BH, nq, nk, block)))) return rc;
   scfa::MetaArgs m{};
   m.q_idx = q_idx;
   m.k_idx = k_idx;
@@ -323,8 +322,13 @@ int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
   m.k_hash = k_hash;
   m.q_stats = q_stats;
   m.k_stats = k_stats;
-  m.q_segs = use_segs ? q_segs : nullptr;
-  m.k_segs = use_segs ? k_segs : nullptr;
+  if (use_segs) {
+    Carver cv{static_cast<char *>(ws)};
+    m.q_segs = cv.take<int32_t>((size_t)BH * nq * block * 16);
+    m.k_segs = cv.take<int32_t>((size_t)BH * nk * block * 16);
+    m.q_nseg = cv.take<int32_t>((size_t)BH * nq * 4);
+    m.k_nseg = cv.take<int32_t>((size_t)BH * nk * 4);
+  }
   m.row_cnt = row_count;
   m.row_list = row_list;
   m.col_cnt = col_count;
@@ -543,16 +547,16 @@ int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int 
 int scfa_block_meta(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B,
                     int H, int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, int32_t *row_count,
                     int32_t *row_list, int32_t *col_count, int32_t *col_list, void *stream) {
-  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, Tq, Tk, block, q_stats, k_stats, nullptr, nullptr, false,
-                   row_count, row_list, col_count, col_list, stream);
+  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, Tq, Tk, block, q_stats, k_stats, false, row_count, row_list,
+                   col_count, col_list, nullptr, 0, stream);
 }
 
 int scfa_block_meta_exact(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash,
                           int B, int H, int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats,
-                          int32_t *q_segs, int32_t *k_segs, int32_t *row_count, int32_t *row_list,
-                          int32_t *col_count, int32_t *col_list, void *stream) {
-  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, Tq, Tk, block, q_stats, k_stats, q_segs, k_segs, true,
-                   row_count, row_list, col_count, col_list, stream);
+                          int32_t *row_count, int32_t *row_list, int32_t *col_count, int32_t *col_list,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, Tq, Tk, block, q_stats, k_stats, true, row_count, row_list,
+                   col_count, col_list, workspace, workspace_bytes, stream);
 }
 
 int scfa_gather_rows(const void *src, const int32_t *index, void *dst, int B, int H, int T_src, int T_dst, int d,
@@ -575,6 +579,9 @@ size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int bloc
     case SCFA_OP_HASH_BWD:
       if (Tk < 0 || (block != 64 && block != 128)) return 0;
       return attn_ws(op == SCFA_OP_QK_BWD || op == SCFA_OP_HASH_BWD, B, H, Tq, Tk, block);
+    case SCFA_OP_BLOCK_META_EXACT:
+      if (Tk < 0 || (block != 64 && block != 128)) return 0;
+      return scfa::meta_seg_bytes((size_t)B * H, nblocks(Tq, block), nblocks(Tk, block), block);
     case SCFA_OP_LSH_SORT:
       if (n_buckets < 2 || n_buckets > 1024 || (n_buckets & 1) || (d != 64 && d != 128)) return 0;
       return Tq > 0 ? lsh_ws(B, H, Tq, d, n_buckets) : 0;

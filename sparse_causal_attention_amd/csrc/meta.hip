@@ -10,11 +10,12 @@
 //
 // Exact variant (Hash-sparse): a tile that passes the range test can still
 // hold no valid pair, when every bucket the two blocks share has all its keys
-// after all its queries.  With per-block bucket segments (bucket, min
-// position, max position) such tiles are dropped too: the tile is live iff
-// some common bucket h has min key position <= max query position among the
-// rows of bucket h.  Blocks with more than kMaxSegs distinct buckets keep the
-// range test.  In QK-sparse mode the range test is already exact.
+// after all its queries.  Each block's distinct buckets are listed with the
+// min and max position of their rows ("segments", as many as the block has
+// buckets); the tile is live iff some common bucket h has min key position
+// <= max query position among the rows of bucket h, which is exactly "the
+// tile holds a valid pair".  In QK-sparse mode the range test is already
+// exact.
 //
 // Two launches: block statistics (one wave per block), then one wave per list
 // row that tests 64 partner blocks per step and compacts the live ones in
@@ -71,51 +72,55 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
   }
   int32_t *segs = isq ? a.q_segs : a.k_segs;
   if (segs == nullptr || hs == nullptr) return;
-  // Bucket segments.  A block holds at most 128 rows: two per lane.
+  // Bucket segments: the smallest remaining bucket id, then the min and max
+  // position of its rows, until every row is taken (one record per distinct
+  // bucket, at most `block`).  A block holds at most 128 rows: two per lane.
   const int lane = threadIdx.x;
   bool rem0 = r0 + lane < r1, rem1 = r0 + 64 + lane < r1;
   int h0 = 0, i0 = 0, h1 = 0, i1 = 0;
   if (rem0) h0 = hs[(size_t)bh * T + r0 + lane], i0 = idx[r0 + lane];
   if (rem1) h1 = hs[(size_t)bh * T + r0 + 64 + lane], i1 = idx[r0 + 64 + lane];
-  int rec[3 * kMaxSegs];
+  const int nblk_side = isq ? a.nq : a.nk;
+  int4 *out = reinterpret_cast<int4 *>(segs) + ((size_t)bh * nblk_side + blk) * a.block;
   int nseg = 0;
-#pragma unroll
-  for (int sg = 0; sg < kMaxSegs; ++sg) {
-    rec[3 * sg] = rec[3 * sg + 1] = rec[3 * sg + 2] = 0;
-    if (__ballot(rem0 || rem1) == 0ull) continue;  // wave-uniform
+  while (__ballot(rem0 || rem1) != 0ull) {  // wave-uniform; each pass takes at least one row
     const int h = wave_min(min(rem0 ? h0 : INT32_MAX, rem1 ? h1 : INT32_MAX));
     const bool in0 = rem0 && h0 == h, in1 = rem1 && h1 == h;
-    rec[3 * sg] = h;
-    rec[3 * sg + 1] = wave_min(min(in0 ? i0 : INT32_MAX, in1 ? i1 : INT32_MAX));
-    rec[3 * sg + 2] = wave_max(max(in0 ? i0 : INT32_MIN, in1 ? i1 : INT32_MIN));
+    const int mn2 = wave_min(min(in0 ? i0 : INT32_MAX, in1 ? i1 : INT32_MAX));
+    const int mx2 = wave_max(max(in0 ? i0 : INT32_MIN, in1 ? i1 : INT32_MIN));
+    if (lane == 0) out[nseg] = make_int4(h, mn2, mx2, 0);
     rem0 = rem0 && !in0;
     rem1 = rem1 && !in1;
     ++nseg;
   }
-  const bool over = __ballot(rem0 || rem1) != 0ull;  // more than kMaxSegs buckets: count -1, records 0
-  if (lane == 0) {
-    int4 *out = reinterpret_cast<int4 *>(segs + ((size_t)bh * (isq ? a.nq : a.nk) + blk) * kSegInts);
-    out[0] = make_int4(over ? -1 : nseg, 0, 0, 0);
-#pragma unroll
-    for (int sg = 0; sg < kMaxSegs; ++sg)
-      out[1 + sg] = over ? make_int4(0, 0, 0, 0) : make_int4(rec[3 * sg], rec[3 * sg + 1], rec[3 * sg + 2], 0);
-  }
+  if (lane == 0) (isq ? a.q_nseg : a.k_nseg)[(size_t)bh * nblk_side + blk] = nseg;
 }
 
 // Exact test for a tile that passed the range test: some bucket common to the
-// two blocks has a key at or before one of its queries.
-__device__ __forceinline__ bool segs_admit(const int4 (&q)[1 + kMaxSegs], const int4 (&k)[1 + kMaxSegs]) {
-  if (q[0].x < 0 || k[0].x < 0) return true;  // too many buckets: keep the range test's answer
-  bool any = false;
-#pragma unroll
-  for (int s = 0; s < kMaxSegs; ++s)
-#pragma unroll
-    for (int t = 0; t < kMaxSegs; ++t)
-      any = any || (s < q[0].x && t < k[0].x && q[1 + s].x == k[1 + t].x && k[1 + t].y <= q[1 + s].z);
-  return any;
+// two blocks has a key at or before one of its queries.  Both record lists are
+// in ascending bucket order, so one merge pass finds the common buckets.
+// `mine` (in LDS) belongs to the list's own block, `other` to the partner;
+// mine_is_q says which side holds the queries.
+__device__ __forceinline__ bool segs_admit(const int4 *mine, int n_mine, const int4 *other, int n_other,
+                                           bool mine_is_q) {
+  int a = 0, b = 0;
+  while (a < n_mine && b < n_other) {
+    const int4 m = mine[a], o = other[b];
+    if (m.x < o.x) {
+      ++a;
+    } else if (m.x > o.x) {
+      ++b;
+    } else {
+      if (mine_is_q ? o.y <= m.z : m.y <= o.z) return true;  // min key position <= max query position
+      ++a;
+      ++b;
+    }
+  }
+  return false;
 }
 
 __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, int with_cols) {
+  __shared__ int4 mine_seg[128];  // this list's block's segments (block <= 128 rows)
   const int nrow = a.nq + (with_cols ? a.nk : 0);
   const int bh = blockIdx.x / nrow;
   const int r = blockIdx.x % nrow;
@@ -124,34 +129,40 @@ __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, i
   const int4 *qst = reinterpret_cast<const int4 *>(a.q_stats) + (size_t)bh * a.nq;
   const int4 *kst = reinterpret_cast<const int4 *>(a.k_stats) + (size_t)bh * a.nk;
   const bool exact = hash_mode && a.q_segs != nullptr;
-  const int4 *qsg = exact ? reinterpret_cast<const int4 *>(a.q_segs) + (size_t)bh * a.nq * (1 + kMaxSegs) : nullptr;
-  const int4 *ksg = exact ? reinterpret_cast<const int4 *>(a.k_segs) + (size_t)bh * a.nk * (1 + kMaxSegs) : nullptr;
   int n_other;
   int32_t *list;
   int32_t *cnt_out;
   int4 mine;
-  int4 mseg[1 + kMaxSegs];
-  const int4 *other_seg;
+  const int4 *other_seg = nullptr;  // partner blocks' records, `block` slots each
+  const int32_t *other_n = nullptr;
+  int n_mine = 0;
   if (is_row) {
     n_other = a.nk;
     mine = qst[r];
     list = a.row_list + ((size_t)bh * a.nq + r) * a.nk;
     cnt_out = a.row_cnt + (size_t)bh * a.nq + r;
-    other_seg = ksg;
-    if (exact)
-#pragma unroll
-      for (int i = 0; i <= kMaxSegs; ++i) mseg[i] = qsg[(size_t)r * (1 + kMaxSegs) + i];
+    if (exact) {
+      const int4 *src = reinterpret_cast<const int4 *>(a.q_segs) + ((size_t)bh * a.nq + r) * a.block;
+      n_mine = a.q_nseg[(size_t)bh * a.nq + r];
+      for (int t = lane; t < n_mine; t += 64) mine_seg[t] = src[t];
+      other_seg = reinterpret_cast<const int4 *>(a.k_segs) + (size_t)bh * a.nk * a.block;
+      other_n = a.k_nseg + (size_t)bh * a.nk;
+    }
   } else {
     const int j = r - a.nq;
     n_other = a.nq;
     mine = kst[j];
     list = a.col_list + ((size_t)bh * a.nk + j) * a.nq;
     cnt_out = a.col_cnt + (size_t)bh * a.nk + j;
-    other_seg = qsg;
-    if (exact)
-#pragma unroll
-      for (int i = 0; i <= kMaxSegs; ++i) mseg[i] = ksg[(size_t)j * (1 + kMaxSegs) + i];
+    if (exact) {
+      const int4 *src = reinterpret_cast<const int4 *>(a.k_segs) + ((size_t)bh * a.nk + j) * a.block;
+      n_mine = a.k_nseg[(size_t)bh * a.nk + j];
+      for (int t = lane; t < n_mine; t += 64) mine_seg[t] = src[t];
+      other_seg = reinterpret_cast<const int4 *>(a.q_segs) + (size_t)bh * a.nq * a.block;
+      other_n = a.q_nseg + (size_t)bh * a.nq;
+    }
   }
+  __syncthreads();  // mine_seg written by the wave's lanes, read by all
   int count = 0;
   for (int base = 0; base < n_other; base += 64) {
     const int o = base + lane;
@@ -165,12 +176,9 @@ __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, i
         live = live && qs.w >= ks.z && qs.z <= ks.w;
         free = free && qs.z == qs.w && ks.z == ks.w && qs.z == ks.z;
       }
-      if (exact && live) {
-        int4 oseg[1 + kMaxSegs];
-#pragma unroll
-        for (int i = 0; i <= kMaxSegs; ++i) oseg[i] = other_seg[(size_t)o * (1 + kMaxSegs) + i];
-        live = is_row ? segs_admit(mseg, oseg) : segs_admit(oseg, mseg);
-      }
+      // With one bucket on each side the range test is already exact.
+      if (exact && live && !(qs.z == qs.w && ks.z == ks.w))
+        live = segs_admit(mine_seg, n_mine, other_seg + (size_t)o * a.block, other_n[o], is_row);
     }
     const unsigned long long m = __ballot(live);
     if (live) {

@@ -43,20 +43,28 @@ struct RowArgs {
   int BH, Ts, Td, ppr;
 };
 
-// Bucket segments of one block (exact tile test): kSegInts int32 per block,
-// [0] = number of distinct buckets among the block's rows if at most
-// kMaxSegs, else -1; then kMaxSegs records (bucket, min idx, max idx, 0) in
-// ascending bucket order, unused records zero.
-constexpr int kMaxSegs = 3;
-constexpr int kSegInts = 4 + 4 * kMaxSegs;
-
+// Bucket segments of a block (exact tile test): one int4 record (bucket, min
+// position, max position, 0) per distinct bucket among the block's real rows,
+// in ascending bucket order, `block` record slots per block; the number of
+// records is in the block's count entry.
 struct MetaArgs {
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
   int32_t *q_stats, *k_stats;  // [BH, nq, 4], [BH, nk, 4]
-  int32_t *q_segs, *k_segs;    // [BH, nq, kSegInts], [BH, nk, kSegInts]; NULL = range rule only
+  int32_t *q_segs, *k_segs;    // [BH, nq, block, 4], [BH, nk, block, 4]; NULL = range rule only
+  int32_t *q_nseg, *k_nseg;    // [BH, nq], [BH, nk] record counts (with the segments)
   int32_t *row_cnt, *row_list, *col_cnt, *col_list;
   int BH, Tq, Tk, nq, nk, block;
 };
+
+// Workspace slices are 256-byte aligned.
+constexpr size_t kWsAlign = 256;
+inline size_t ws_round(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Workspace bytes of the exact tile test's segments (records and counts).
+inline size_t meta_seg_bytes(size_t BH, size_t nq, size_t nk, int block) {
+  return ws_round(BH * nq * block * 16) + ws_round(BH * nk * block * 16) + ws_round(BH * nq * 4) +
+         ws_round(BH * nk * 4);
+}
 
 struct LshArgs {
   const void *x;

@@ -131,14 +131,18 @@ def test_block_meta_validation():
 def test_block_meta_exact_validation():
     lib = _lib.load()
     f = lib.scfa_block_meta_exact
-    # hash mode needs both segment arrays, 16-byte aligned
-    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, None, P, P2, P2, None, None, None) == \
+    need = lib.scfa_workspace_size(_lib.OP_BLOCK_META_EXACT, 1, 1, 100, 100, 0, 64, 0)
+    assert need > 0
+    # hash mode needs its workspace, 256-byte aligned and large enough
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, P2, P2, None, None, None, 0, None) == \
         _lib.ERR_INVALID_ARGUMENT
-    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, P, P + 8, P2, P2, None, None, None) == \
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, P2, P2, None, None, P + 16, need, None) == \
         _lib.ERR_INVALID_ARGUMENT
-    assert f(P2, P2, P2, None, 1, 1, 100, 100, 64, P, P, P, P, P2, P2, None, None, None) == \
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 64, P, P, P2, P2, None, None, P, need - 1, None) == \
+        _lib.ERR_WORKSPACE_TOO_SMALL
+    assert f(P2, P2, P2, None, 1, 1, 100, 100, 64, P, P, P2, P2, None, None, P, need, None) == \
         _lib.ERR_INVALID_ARGUMENT
-    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 96, P, P, P, P, P2, P2, None, None, None) == \
+    assert f(P2, P2, P2, P2, 1, 1, 100, 100, 96, P, P, P2, P2, None, None, P, need, None) == \
         _lib.ERR_UNSUPPORTED
 
 
@@ -161,12 +165,14 @@ def test_workspace_sizes():
     ws = lib.scfa_workspace_size
     r = lambda n: (n + 255) // 256 * 256  # noqa: E731
     BH, nq, nk, Tq = 2 * 3, 4, 2, 200
-    fwd = r(BH * nq * 16) + r(BH * nk * 16) + r(BH * nq * 4) + r(BH * nq * nk * 4) + r(BH * nq * 64) + r(BH * nk * 64)
+    segs = r(BH * nq * 64 * 16) + r(BH * nk * 64 * 16) + r(BH * nq * 4) + r(BH * nk * 4)  # one record per row
+    fwd = r(BH * nq * 16) + r(BH * nk * 16) + r(BH * nq * 4) + r(BH * nq * nk * 4) + segs
     bwd = fwd + r(BH * nk * 4) + r(BH * nk * nq * 4) + r(2 * BH * Tq * 4)
     assert ws(_lib.OP_QK_FWD, 2, 3, 200, 100, 64, 64, 0) == fwd
     assert ws(_lib.OP_HASH_BWD, 2, 3, 200, 100, 64, 64, 0) == bwd
     assert ws(_lib.OP_QK_FWD, 0, 3, 200, 100, 64, 64, 0) == 0
     assert ws(_lib.OP_QK_FWD, 1, 3, 200, 100, 64, 96, 0) == 0
+    assert ws(_lib.OP_BLOCK_META_EXACT, 2, 3, 200, 100, 0, 64, 0) == segs
     assert ws(_lib.OP_LSH_SORT, 1, 1, 5000, 0, 64, 0, 16) > 0
     assert ws(_lib.OP_LSH_SORT, 1, 1, 5000, 0, 64, 0, 15) == 0
     assert ws(99, 1, 1, 5, 5, 64, 64, 0) == 0

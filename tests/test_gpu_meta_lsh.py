@@ -34,12 +34,7 @@ def _compare_meta(out, c, block, exact=False, heads=None):
             qh = c.q_hash[b, h] if hashed else None
             kh = c.k_hash[b, h] if hashed else None
             if exact:
-                qs, ks, qseg, kseg, live, free = Bk.metadata_exact(c.q_idx[b, h], c.k_idx[b, h], qh, kh, block)
-                if hashed:
-                    np.testing.assert_array_equal(got["q_segs"][b, h], qseg)
-                    np.testing.assert_array_equal(got["k_segs"][b, h], kseg)
-                else:
-                    assert "q_segs" not in got and "k_segs" not in got
+                qs, ks, live, free = Bk.metadata_exact(c.q_idx[b, h], c.k_idx[b, h], qh, kh, block)
             else:
                 qs, ks, live, free = Bk.metadata(c.q_idx[b, h], c.k_idx[b, h], qh, kh, block)
             np.testing.assert_array_equal(got["q_stats"][b, h], qs)
@@ -87,6 +82,8 @@ def test_block_meta_bit_exact(kw, block):
         dict(Tq=5000, Tk=5000, mode="hash", nb=16, layout="grouped", shared=True),
         dict(Tq=3000, Tk=2500, mode="hash", nb=150, layout="grouped"),  # many blocks with > 3 buckets
         dict(Tq=1, Tk=130, mode="hash", nb=2, layout="grouped"),
+        dict(Tq=777, Tk=901, mode="hash", nb=40, layout="shuffled"),  # up to a bucket per row, unsorted
+        dict(Tq=1200, Tk=1200, mode="hash", nb=1000, layout="grouped", shared=True),
     ],
 )
 def test_block_meta_exact_bit_exact(kw, block):

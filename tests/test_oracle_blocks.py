@@ -133,35 +133,61 @@ def test_lists_are_ascending_and_consistent():
 
 
 # ---------------------------------------------------------------------------
-# Exact liveness ("2. Hash-Sparse" rule 1 read as: keep a tile iff its
-# buckets can match on a causal pair), pinned against brute force.
+# Exact liveness ("2. Hash-Sparse" rules 1 and 2 read literally: a tile is kept
+# iff a query and a key of it share a bucket in causal order, i.e. iff it holds
+# an admissible pair).  ``tile_has_pair`` reduces the element mask per tile; the
+# pins below check it by explicit per-pair loops, closed forms and a worked case.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("seed,nb,block,sort_by_hash", [(0, 4, 32, True), (1, 6, 32, True), (2, 3, 16, False),
-                                                        (3, 40, 32, True), (4, 2, 64, True)])
-def test_exact_liveness_equals_brute_force(seed, nb, block, sort_by_hash):
-    """Where both blocks hold <= MAX_SEGS buckets: live iff the tile holds an admissible
-    pair; elsewhere the range rule's answer.  Always a subset of the range rule."""
+def _tile_has_pair_loops(qi, ki, qh, kh, block):
+    """Scalar loops over every (query, key) pair, written from the rule directly."""
+    nq, nk = Bk.n_blocks(len(qi), block), Bk.n_blocks(len(ki), block)
+    out = np.zeros((nq, nk), dtype=bool)
+    for r in range(len(qi)):
+        for c in range(len(ki)):
+            same = qh is None or int(qh[r]) == int(kh[c])
+            if same and int(ki[c]) <= int(qi[r]):
+                out[r // block, c // block] = True
+    return out
+
+
+@pytest.mark.parametrize("seed,nb,block,sort_by_hash", [(0, 4, 16, True), (1, 6, 16, True), (2, 3, 8, False),
+                                                        (3, 40, 16, True), (4, 2, 32, True), (5, 70, 16, False)])
+def test_exact_liveness_equals_pair_loops(seed, nb, block, sort_by_hash):
+    """Any number of buckets per block (up to every row its own bucket): the tile is
+    live iff some pair in it is admissible; always a subset of the range rule."""
     rng = np.random.default_rng(100 + seed)
-    Tq, Tk = 333, 301
+    Tq, Tk = 101, 87
     qi, ki, qh, kh = _random_case(rng, True, Tq, Tk, nb=nb, sort_by_hash=sort_by_hash)
-    mask = A.element_mask(qi, ki, qh, kh)
-    _, _, live_range, _ = Bk.metadata(qi, ki, qh, kh, block)
-    _, _, qseg, kseg, live, _ = Bk.metadata_exact(qi, ki, qh, kh, block)
-    n_small = 0
-    for i in range(live.shape[0]):
-        for j in range(live.shape[1]):
-            has_pair = bool(_tile_pairs(mask, i, j, block).any())
-            assert not (live[i, j] and not live_range[i, j])
-            if has_pair:
-                assert live[i, j]
-            if qseg[i, 0] >= 0 and kseg[j, 0] >= 0:
-                n_small += 1
-                assert live[i, j] == has_pair, (i, j)
-            else:
-                assert live[i, j] == live_range[i, j]
-    assert n_small > 0
-    if nb <= 3 and block <= 32:
-        assert n_small == live.size  # every block holds at most 3 buckets
+    _, _, live_range, free = Bk.metadata(qi, ki, qh, kh, block)
+    _, _, live, free_x = Bk.metadata_exact(qi, ki, qh, kh, block)
+    np.testing.assert_array_equal(live, _tile_has_pair_loops(qi, ki, qh, kh, block))
+    assert not (live & ~live_range).any()
+    np.testing.assert_array_equal(free_x, free)
+    assert not (free & ~live).any()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_exact_liveness_without_buckets_is_the_range_rule(seed):
+    """QK-sparse: the pair (query with the largest position, key with the smallest) is
+    admissible whenever max q_idx >= min k_idx, so the block rule is already exact."""
+    rng = np.random.default_rng(50 + seed)
+    qi, ki, _, _ = _random_case(rng, False, 301, 277)
+    if seed == 1:
+        qi, ki = rng.permutation(qi), rng.permutation(ki)
+    _, _, live_range, _ = Bk.metadata(qi, ki, None, None, 32)
+    _, _, live, _ = Bk.metadata_exact(qi, ki, None, None, 32)
+    np.testing.assert_array_equal(live, live_range)
+    np.testing.assert_array_equal(live, _tile_has_pair_loops(qi, ki, None, None, 32))
+
+
+def test_exact_liveness_identity_positions_one_bucket():
+    """Identity positions, one bucket: live iff j <= i (standard causal tiles)."""
+    pos = np.arange(200)
+    h = np.zeros(200, dtype=np.int64)
+    live = Bk.tile_has_pair(pos, pos, h, h, 64)
+    n = Bk.n_blocks(200, 64)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    np.testing.assert_array_equal(live, j <= i)
 
 
 def test_exact_liveness_drops_bucket_matched_acausal_tiles():
@@ -172,27 +198,20 @@ def test_exact_liveness_drops_bucket_matched_acausal_tiles():
     qh = np.array([0, 0, 1, 1])
     ki = np.array([20, 21, 60, 61])
     kh = np.array([0, 0, 1, 1])
-    mask = A.element_mask(qi, ki, qh, kh)
-    assert not mask.any()
+    assert not A.element_mask(qi, ki, qh, kh).any()
     _, _, live_range, _ = Bk.metadata(qi, ki, qh, kh, 4)
-    _, _, qseg, kseg, live, _ = Bk.metadata_exact(qi, ki, qh, kh, 4)
+    _, _, live, _ = Bk.metadata_exact(qi, ki, qh, kh, 4)
     assert live_range[0, 0] and not live[0, 0]
-    np.testing.assert_array_equal(qseg[0], [2, 0, 0, 0, 0, 10, 11, 0, 1, 50, 51, 0, 0, 0, 0, 0])
-    np.testing.assert_array_equal(kseg[0], [2, 0, 0, 0, 0, 20, 21, 0, 1, 60, 61, 0, 0, 0, 0, 0])
     # one key of bucket 1 moved before the last bucket-1 query makes the tile live
     ki2 = np.array([20, 21, 51, 61])
-    _, _, _, _, live2, _ = Bk.metadata_exact(qi, ki2, qh, kh, 4)
+    _, _, live2, _ = Bk.metadata_exact(qi, ki2, qh, kh, 4)
     assert live2[0, 0] and A.element_mask(qi, ki2, qh, kh).any()
-
-
-def test_block_segments_overflow_and_unsorted_rows():
-    idx = np.array([9, 3, 7, 1, 5, 2, 8, 6])
-    hs = np.array([2, 0, 2, 0, 5, 1, 9, 3])
-    seg = Bk.block_segments(idx, hs, 4)
-    # block 0: buckets {0, 2}: (0: min 1, max 3), (2: min 7, max 9)
-    np.testing.assert_array_equal(seg[0], [2, 0, 0, 0, 0, 1, 3, 0, 2, 7, 9, 0, 0, 0, 0, 0])
-    # block 1: four distinct buckets -> overflow marker, records zero
-    np.testing.assert_array_equal(seg[1], [-1] + [0] * 15)
+    # five buckets in one block, one shared bucket (7) in causal order: live
+    qi3, qh3 = np.array([1, 2, 3, 4, 90]), np.array([3, 4, 5, 6, 7])
+    ki3, kh3 = np.array([80, 81, 82, 83, 89]), np.array([8, 9, 10, 11, 7])
+    assert Bk.tile_has_pair(qi3, ki3, qh3, kh3, 8)[0, 0]
+    assert Bk.tile_has_pair(qi3, ki3 + 1, qh3, kh3, 8)[0, 0]  # key 90 <= query 90: a token sees itself
+    assert not Bk.tile_has_pair(qi3, ki3 + 2, qh3, kh3, 8)[0, 0]
 
 
 @pytest.mark.parametrize("seed", [0, 1])
@@ -208,4 +227,4 @@ def test_exact_pruned_evaluation_equals_full_mask(seed):
     np.testing.assert_array_equal(np.isfinite(lse2), finite)
     np.testing.assert_allclose(lse2[finite], lse[finite], atol=1e-12, rtol=0)
     # and it really prunes more than the range rule on bucket-sorted inputs
-    assert Bk.metadata_exact(qi, ki, qh, kh, block)[4].sum() < Bk.metadata(qi, ki, qh, kh, block)[2].sum()
+    assert Bk.metadata_exact(qi, ki, qh, kh, block)[2].sum() < Bk.metadata(qi, ki, qh, kh, block)[2].sum()
