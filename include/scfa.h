@@ -173,6 +173,33 @@ int scfa_hash_sparse_bwd(const void *q, const void *k, const void *v,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Hash-sparse forward that allocates nothing and takes no workspace.  For
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Arguments, results
+ * and errors are those of scfa_hash_sparse_fwd; the caller still passes every
+ * input and output.  Its scratch (block statistics, bucket segments, live-tile
+ * lists) is a static device array of scfa_noalloc_scratch_bytes() bytes (32
+ * MiB), one copy per GPU, held from the first call on that GPU until the
+ * process ends.  A shape whose scratch exceeds it (scfa_workspace_size(
+ * SCFA_OP_HASH_FWD, ...) > scfa_noalloc_scratch_bytes(), e.g. more than about
+ * 40 heads of 16,384 tokens at block 64) is rejected with
+ * SCFA_ERR_WORKSPACE_TOO_SMALL before anything touches the GPU.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (several
+ * streams or host threads) race and give wrong results; calls ordered on one
+ * stream are safe.  The array's previous contents never matter (every value is
+ * written before it is read), so nothing needs clearing between calls.
+ */
+int scfa_hash_sparse_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const int32_t *q_idx, const int32_t *k_idx,
+                                 const int32_t *q_hash, const int32_t *k_hash,
+                                 void *o, float *lse,
+                                 int B, int H, int Tq, int Tk, int d, int block, float scale,
+                                 int dtype, unsigned flags, void *stream);
+
+/* Bytes of the static scratch array scfa_hash_sparse_fwd_noalloc uses per GPU. */
+size_t scfa_noalloc_scratch_bytes(void);
+
+/*
  * LSH bucketing and the (bucket, original position) reordering that feeds
  * Hash-sparse attention ("why dynamic sparsity breaks it": LSH groups similar
  * tokens into buckets; tokens reordered by hash keep their original positions

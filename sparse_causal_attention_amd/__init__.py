@@ -36,6 +36,8 @@ __all__ = [
     "qk_sparse_bwd",
     "hash_sparse_fwd",
     "hash_sparse_bwd",
+    "hash_sparse_fwd_noalloc",
+    "noalloc_scratch_bytes",
     "lsh_bucket_sort",
     "block_meta",
     "attn_fwd_lists",
@@ -167,6 +169,30 @@ def hash_sparse_bwd(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, *, bloc
     """Gradients (dq, dk, dv) for the Hash-sparse forward."""
     return _bwd("scfa_hash_sparse_bwd", _lib.OP_HASH_BWD, q, k, v, o, lse, dout, (q_idx, k_idx, q_hash, k_hash),
                 block, scale, flags, workspace)
+
+
+def hash_sparse_fwd_noalloc(q, k, v, q_idx, k_idx, q_hash, k_hash, *, block=64, scale=None, flags=0, out=None):
+    """hash_sparse_fwd without a workspace: the library uses its static per-GPU scratch
+    (scfa_hash_sparse_fwd_noalloc).  ``out`` optionally supplies preallocated (o, lse)."""
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    for t, n, T in zip((q_idx, k_idx, q_hash, k_hash), ("q_idx", "k_idx", "q_hash", "k_hash"), (Tq, Tk, Tq, Tk)):
+        _need(t, n, torch.int32, (B, H, T))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse = out if out is not None else (torch.empty_like(q),
+                                          torch.empty((B, H, Tq), dtype=torch.float32, device=q.device))
+    rc = _LIB.scfa_hash_sparse_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(q_hash),
+                                           _ptr(k_hash), _ptr(o), _ptr(lse), B, H, Tq, Tk, d, block, float(scale),
+                                           _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_hash_sparse_fwd_noalloc", rc)
+    return o, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static per-GPU scratch of hash_sparse_fwd_noalloc."""
+    return int(_LIB.scfa_noalloc_scratch_bytes())
 
 
 def lsh_bucket_sort(x, R, n_buckets, idx=None, companion=None, *, idx_ascending=False, want_x=True,

@@ -19,6 +19,8 @@ EXPORTED = (
     "scfa_qk_sparse_bwd",
     "scfa_hash_sparse_fwd",
     "scfa_hash_sparse_bwd",
+    "scfa_hash_sparse_fwd_noalloc",
+    "scfa_noalloc_scratch_bytes",
     "scfa_lsh_bucket_sort",
     "scfa_block_meta",
     "scfa_block_meta_exact",
@@ -66,6 +68,8 @@ _SIGNATURES = {
     "scfa_qk_sparse_bwd": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p] + _ATTN_TAIL,
     "scfa_hash_sparse_fwd": [_p, _p, _p, _p, _p, _p, _p, _p, _p] + _ATTN_TAIL,
     "scfa_hash_sparse_bwd": [_p] * 13 + _ATTN_TAIL,
+    "scfa_hash_sparse_fwd_noalloc": [_p] * 9 + _LISTS_TAIL,
+    "scfa_noalloc_scratch_bytes": [],
     "scfa_lsh_bucket_sort": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_block_meta": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p],
     "scfa_block_meta_exact": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
@@ -97,6 +101,7 @@ def load() -> ctypes.CDLL:
         fn.argtypes = argtypes
         fn.restype = _i
     lib.scfa_workspace_size.restype = _sz
+    lib.scfa_noalloc_scratch_bytes.restype = _sz
     lib.scfa_last_error.restype = ctypes.c_char_p
     _LIB = lib
     return lib

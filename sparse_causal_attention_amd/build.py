@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libscfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "meta.hip", "attn_fwd.hip", "attn_bwd.hip", "lsh.hip", "rows.hip"]
+SOURCES = ["api.cpp", "meta.hip", "attn_fwd.hip", "attn_bwd.hip", "lsh.hip", "rows.hip", "noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -372,6 +372,8 @@ int rows_call(bool gather, const void *src, const int32_t *index, void *dst, int
 }
 }  // namespace
 
+int scfa::report_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
 extern "C" {
 
 int scfa_qk_sparse_fwd(const void *q, const void *k, const void *v, const int32_t *q_idx, const int32_t *k_idx,

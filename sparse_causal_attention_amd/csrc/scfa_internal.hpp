@@ -92,6 +92,9 @@ struct LshArgs {
 
 hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s);
 
+// Sets the calling thread's scfa_last_error() message and returns `code`.
+int report_error(int code, const char *msg);
+
 hipError_t launch_gather_rows(const RowArgs &r, hipStream_t s);
 hipError_t launch_scatter_rows(const RowArgs &r, bool zero_fill, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const AttnArgs &a, int mode, hipStream_t s);

@@ -178,6 +178,20 @@ def test_workspace_sizes():
     assert ws(99, 1, 1, 5, 5, 64, 64, 0) == 0
 
 
+def test_noalloc_rejects_oversize_shapes_on_the_host():
+    lib = _lib.load()
+    cap = lib.scfa_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    # 48 heads of 16,384 tokens at block 64 need more scratch than the static array holds
+    assert lib.scfa_workspace_size(_lib.OP_HASH_FWD, 2, 24, 16384, 16384, 64, 64, 0) > cap
+    rc = lib.scfa_hash_sparse_fwd_noalloc(P, P, P, P2, P2, P2, P2, P, P2, 2, 24, 16384, 16384, 64, 64, 0.125, 0, 0,
+                                          None)
+    assert rc == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert b"static scratch" in lib.scfa_last_error()
+    # the benchmark's 24 heads fit
+    assert lib.scfa_workspace_size(_lib.OP_HASH_FWD, 2, 12, 16384, 16384, 64, 64, 0) <= cap
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_LIB", None)
