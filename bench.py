@@ -83,9 +83,10 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(tile_rule, view):
+def measured_traffic(tile_rule, view, backward):
     """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
-    (None too when the summary was taken with the other tile rule or the other view of the rows)."""
+    (None too when the summary was taken with the other tile rule, the other view of the rows or the
+    other backward)."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith((" ", "#")))
@@ -93,7 +94,7 @@ def measured_traffic(tile_rule, view):
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
     if (kv.get("source_digest") != kernel_source_digest() or kv.get("tile_rule") != tile_rule
-            or kv.get("rows") != view):
+            or kv.get("rows") != view or kv.get("backward", "recompute") != backward):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -179,7 +180,7 @@ class Timer:
         return tot[m] if len(tot) % 2 else 0.5 * (tot[m - 1] + tot[m])
 
 
-def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False, qk=None):
+def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False, qk=None, ds=None):
     """One step.  By default the sorts return only bucket ids, positions and the permutations, and
     the attention kernels read Q, dO, K and V through the permutations (row indirection); with
     copy_sorted the sorts also copy the rows into sorted order and attention reads the copies.
@@ -188,7 +189,11 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False,
     the permutations).
 
     With qk (Q and K stacked in one [2B, H, T, d] allocation, q and k its halves) and rows read
-    through the permutations, one LSH + sort call serves both tensors."""
+    through the permutations, one LSH + sort call serves both tensors.
+
+    With ds (a dS buffer, see prepare_ds) the backward stores every live tile's dS in the dK/dV
+    kernel and computes dQ from the stored tiles (tile slots built with the lists, then the
+    preprocess for D, dK/dV, dQ); without it the dQ kernel recomputes S, P and dP."""
     nb, blk, sc = w.n_buckets, w.block, w.scale
     B = q.shape[0]
     if timer:
@@ -214,6 +219,8 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False,
     if timer:
         timer.mark()
     meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=True, exact=exact)
+    if ds is not None:
+        scfa.tile_slots(meta)
     if timer:
         timer.mark()
     meta.update(q_hash=qh, q_idx=qi, k_hash=kh, k_idx=ki, **({"q_perm": rows["q_rows"], "k_perm": rows["k_rows"]}
@@ -221,21 +228,54 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False,
     o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc, **rows)
     if timer:
         timer.mark()
-    dq, delta = scfa.attn_bwd_dq_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, block=blk, scale=sc, **rows)
-    if timer:
-        timer.mark()
-    dk, dv = scfa.attn_bwd_dkdv_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, block=blk, scale=sc,
-                                      **rows)
-    if timer:
-        timer.mark()
+    if ds is None:
+        dq, delta = scfa.attn_bwd_dq_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, block=blk, scale=sc,
+                                           **rows)
+        if timer:
+            timer.mark()
+        dk, dv = scfa.attn_bwd_dkdv_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, block=blk, scale=sc,
+                                          **rows)
+        if timer:
+            timer.mark()
+    else:
+        delta = scfa.attn_bwd_prep(o, lse, dos, q_rows=rows.get("q_rows"))
+        if timer:
+            timer.mark()
+        dk, dv = scfa.attn_bwd_dkdv_ds_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, ds, block=blk,
+                                             scale=sc, **rows)
+        if timer:
+            timer.mark()
+        dq = scfa.attn_bwd_dq_ds_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, ds, delta, block=blk,
+                                       scale=sc, **rows)
+        if timer:
+            timer.mark()
     return meta, (o, lse, dq, dk, dv)
+
+
+def prepare_ds(scfa, torch, w, q, k, R, qk=None, exact=True, copy_sorted=False):
+    """A dS buffer holding every live tile of the step's inputs (sized once, before timing, from one
+    metadata pass, as a caller sizes any workspace)."""
+    B = q.shape[0]
+    if qk is not None and not copy_sorted:
+        hh, ii, _, _, _ = scfa.lsh_bucket_sort(qk, R, w.n_buckets, want_x=False)
+        qh, kh, qi, ki = hh[:B], hh[B:], ii[:B], ii[B:]
+    else:
+        qh, qi, _, _, _ = scfa.lsh_bucket_sort(q, R, w.n_buckets, want_x=False)
+        kh, ki, _, _, _ = scfa.lsh_bucket_sort(k, R, w.n_buckets, want_x=False)
+    meta = scfa.block_meta(qi, ki, qh, kh, block=w.block, with_cols=True, exact=exact)
+    total = int(meta["col_count"].sum().item())
+    return scfa.ds_buffer(total, w.block, device=q.device)
 
 
 STEP_CALLS = ["lsh_sort_qk", "block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
 STEP_CALLS_COPIED = ["lsh_sort_q", "lsh_sort_k", "block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
+STEP_CALLS_DS = ["lsh_sort_qk", "block_meta", "fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
+STEP_CALLS_COPIED_DS = ["lsh_sort_q", "lsh_sort_k", "block_meta", "fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
 
-def step_calls(copy_sorted):
+def step_calls(copy_sorted, stored_ds=False):
+    if stored_ds:
+        return STEP_CALLS_COPIED_DS if copy_sorted else STEP_CALLS_DS
     return STEP_CALLS_COPIED if copy_sorted else STEP_CALLS
 
 
@@ -431,16 +471,19 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, qk, nbs, args):
     for nb in nbs:
         wn = dataclasses.replace(w, n_buckets=nb, name=f"{w.name.rsplit('_nb', 1)[0]}_nb{nb}")
         R = torch.from_numpy(np.stack([lsh_rotation(wn, h) for h in range(w.H)])).to("cuda:0")
-        calls = step_calls(args.copy_sorted)
+        ds = prepare_ds(scfa, torch, wn, q, k, R, qk, not args.range_lists, args.copy_sorted) if args.stored_ds \
+            else None
+        calls = step_calls(args.copy_sorted, ds is not None)
         timer = Timer(torch, calls)
         ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists,
-                                                              args.copy_sorted, qk),
+                                                              args.copy_sorted, qk, ds),
                                     args.steps,
                                     args.warmup, timer)
         timer.collect()
         units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
         per_call = {n: round(timer.median_ms(n), 4) for n in calls}
-        attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
+        attn_ms = sum(t for n, t in per_call.items() if not n.startswith("lsh"))
+        del ds
         nq = (w.T + w.block - 1) // w.block
         print(json.dumps({
             "sweep": "n_buckets", "workload": wn.name, "n_buckets": nb, "executed_tiles": tiles,
@@ -461,6 +504,9 @@ def main():
     ap.add_argument("--copy-sorted", action="store_true",
                     help="copy Q, dO, K, V into sorted order in the sorts (default: attention reads them through "
                          "the sort permutations)")
+    ap.add_argument("--stored-ds", action="store_true",
+                    help="backward with stored dS: the dK/dV kernel keeps each tile's dS and dQ is computed from it "
+                         "(default: the dQ kernel recomputes S, P and dP, which measures faster on this workload)")
     ap.add_argument("--range-lists", action="store_true",
                     help="build the tile lists with the bucket-range rule only (keep tiles that hold no valid pair)")
     ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
@@ -510,20 +556,21 @@ def main():
         _log(f"[bench] calibration copy: {args.copy_calibration} MiB read + {args.copy_calibration} MiB written")
         del src, dst
 
+    ds = prepare_ds(scfa, torch, w, q, k, R, qk, not args.range_lists, args.copy_sorted) if args.stored_ds else None
     _log("[bench] warmup")
     for _ in range(args.warmup):
-        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists, copy_sorted=args.copy_sorted, qk=qk)
+        run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists, copy_sorted=args.copy_sorted, qk=qk, ds=ds)
     torch.cuda.synchronize()
 
     # HIP events between the calls, on the stream the kernels run on, inside the timed region
     _log(f"[bench] timing {args.steps} steps")
-    calls = step_calls(args.copy_sorted)
+    calls = step_calls(args.copy_sorted, ds is not None)
     timer = Timer(torch, calls)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         meta, _ = run_step(scfa, w, q, k, v, do, R, timer, exact=not args.range_lists, copy_sorted=args.copy_sorted,
-                           qk=qk)
+                           qk=qk, ds=ds)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -557,39 +604,58 @@ def main():
         dtimer.collect()
 
     per_call = {n: round(timer.median_ms(n), 4) for n in calls}
-    attn_ms = per_call["block_meta"] + per_call["fwd"] + per_call["bwd_dq"] + per_call["bwd_dkdv"]
-    # executed matrix flops per launch of each attention kernel (tile units x d); all algorithmic except the
-    # dQ kernel's recompute of Q K^T and dO V^T
-    kernel_flops = {"fwd": 4.0 * units * w.d, "bwd_dq": 6.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
+    attn_ms = sum(t for n, t in per_call.items() if not n.startswith("lsh"))
+    rows_flag = "false" if args.copy_sorted else "true"
+    if ds is None:
+        # executed matrix flops per launch (tile units x d); the recomputing dQ kernel executes 6*d per tile unit,
+        # of which 2*d (dS K) is algorithmic: it recomputes Q K^T and dO V^T, which the dK/dV kernel's 8*d counts
+        kernel_flops = {"fwd": 4.0 * units * w.d, "bwd_dq": 6.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
+        names = {"fwd": f"k_fwd_bf16_ks<kHash,64,64,{rows_flag}>", "bwd_dq": f"k_bwd_dq_bf16<kHash,64,64,{rows_flag}>",
+                 "bwd_dkdv": f"k_bwd_dkdv_bf16<kHash,64,64,{rows_flag},false>"}
+    else:
+        # stored dS: dK/dV executes its 8*d per tile unit (all algorithmic) and writes each tile's dS;
+        # dQ is dS K only (2*d per tile unit)
+        kernel_flops = {"fwd": 4.0 * units * w.d, "bwd_dq": 2.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
+        names = {"fwd": f"k_fwd_bf16_ks<kHash,64,64,{rows_flag}>", "bwd_dq": f"k_bwd_dq_ds_bf16<64,64,{rows_flag}>",
+                 "bwd_dkdv": f"k_bwd_dkdv_bf16<kHash,64,64,{rows_flag},true>"}
     # algorithmic flops per launch: the dQ kernel's share is dS K only (2*d per tile unit)
     alg = {"fwd": 4.0 * units * w.d, "bwd_dq": 2.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
     dominant = max(kernel_flops, key=lambda n: per_call[n])
     achieved = alg[dominant] / (per_call[dominant] * 1e-3) / 1e12
     roofline = {
-        "kernel": {"fwd": "k_fwd_bf16_ks<kHash,64,64,%s>", "bwd_dq": "k_bwd_dq_bf16<kHash,64,64,%s>",
-                   "bwd_dkdv": "k_bwd_dkdv_bf16<kHash,64,64,%s>"}[dominant] % (
-                       "false" if args.copy_sorted else "true"),
+        "kernel": names[dominant],
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": (measured_traffic("range" if args.range_lists else "exact", "copied" if args.copy_sorted else
-                                     "permuted") if dominant == "bwd_dkdv" else None),
+                                     "permuted", "stored_ds" if ds is not None else "recompute")
+                    if dominant == "bwd_dkdv" else None),
         "avg_launch_ms": per_call[dominant],
         "algorithmic_flops_per_launch": alg[dominant],
     }
 
     # each attention kernel's executed matrix flops per launch over its event time (context; "roofline" is
-    # the dominant kernel's).  The dQ kernel executes 6*d per tile unit, of which 2*d (dS K) is algorithmic:
-    # it recomputes Q K^T and dO V^T, which the dK/dV kernel's 8*d already counts.
-    names = {"fwd": "k_fwd_bf16_ks", "bwd_dq": "k_bwd_dq_bf16", "bwd_dkdv": "k_bwd_dkdv_bf16"}
+    # the dominant kernel's)
     kernel_rooflines = {
         n: {"kernel": names[n], "executed_tflops": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12, 2),
             "executed_frac": round(kernel_flops[n] / (per_call[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": per_call[n], "executed_flops_per_launch": kernel_flops[n],
             "algorithmic_flops_per_launch": alg[n]}
         for n in kernel_flops}
+    if ds is not None:
+        # HBM-bound pieces of the stored-dS backward: the preprocess reads O and dO and writes D and lse*log2 e;
+        # the dQ kernel reads each tile's dS once (2 bytes per tile unit)
+        prep_bytes = w.B * w.H * w.Tq * (2 * 2 * w.d + 4 + 4 + 8)
+        dq_bytes = 2.0 * units
+        kernel_rooflines["bwd_prep"] = {"kernel": "k_bwd_prep<64>", "bound": "hbm", "avg_launch_ms": per_call["bwd_prep"],
+                                        "algorithmic_bytes_per_launch": prep_bytes,
+                                        "GBps": round(prep_bytes / (per_call["bwd_prep"] * 1e-3) / 1e9, 1),
+                                        "frac_hbm": round(prep_bytes / (per_call["bwd_prep"] * 1e-3) / 1e9 /
+                                                          PEAK_HBM_GBS, 4)}
+        kernel_rooflines["bwd_dq"].update({"ds_bytes_per_launch": dq_bytes,
+                                           "ds_GBps": round(dq_bytes / (per_call["bwd_dq"] * 1e-3) / 1e9, 1)})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -622,6 +688,8 @@ def main():
                      "rows read through the sort permutations"),
             "tile_rule": "range" if args.range_lists else "exact",
             "rows": "copied" if args.copy_sorted else "permuted",
+            "backward": "stored dS (dQ from the dK/dV kernel's dS tiles)" if ds is not None else
+                        "recompute (dQ kernel recomputes S, P, dP)",
         },
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
         "executed_tiles": tiles,

@@ -336,6 +336,74 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
                              int dtype, unsigned flags, void *stream);
 
 /*
+ * Backward with stored dS: the dK/dV kernel keeps every live tile's dS (the
+ * bf16 values its dK product uses) and dQ becomes a plain block-sparse
+ * product dQ = scale * dS K over the row lists, with no exponent, mask or dP
+ * recomputed.  The gradients are the analytic ones of scfa_qk_sparse_bwd /
+ * scfa_hash_sparse_bwd (the page gives no backward; its LM-training results,
+ * "实验与结果" > "Hash-Sparse LM training" and "QK-Sparse LM training", need
+ * one).  bf16 only, pruned modes only (positions required; no
+ * SCFA_FLAG_NO_PRUNE).  Order on one stream:
+ *   scfa_block_meta[_exact] (with columns) -> scfa_tile_slots ->
+ *   forward -> scfa_attn_bwd_prep -> scfa_attn_bwd_dkdv_ds_lists ->
+ *   scfa_attn_bwd_dq_ds_lists.
+ * ds: device buffer of ds_tiles tiles of block x block bf16 (tile = dS^T of
+ *   one live tile, key-major: [key][query]), 16-byte aligned, caller-owned.
+ *   The tiles needed are col_base[B*H*nk] (the live-tile count, on the
+ *   device).  If that exceeds ds_tiles nothing is stored and dQ falls back to
+ *   recomputing S, P and dP (the scfa_attn_bwd_dq_lists kernel): results stay
+ *   correct, only slower.
+ */
+
+/* Slot numbering of the live tiles.  Key block c = (b*H + h)*nk + j owns
+ * slots col_base[c] .. col_base[c] + col_count[c] - 1 in its column-list
+ * order; col_base [B*H*nk + 1] int32 (exclusive scan of the column counts,
+ * the total last).  row_slot [B,H,nq,nk] int32: entry t of query block i's
+ * row list (key block j) is stored in slot row_slot[b,h,i,t] (the first
+ * row_count entries of each row are written).  Lists as from scfa_block_meta. */
+int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list,
+                    const int32_t *col_count, const int32_t *col_list,
+                    int B, int H, int Tq, int Tk, int block,
+                    int32_t *col_base, int32_t *row_slot, void *stream);
+
+/* Backward preprocess: delta [2,B,H,Tq] float32 = (rowsum(dout * o),
+ * lse * log2(e)), as scfa_attn_bwd_dq_lists writes it.  o and lse are the
+ * forward's outputs (view rows), dout [B,H,Tq,d] bf16, read through q_rows
+ * when non-NULL (as in the list entry points). */
+int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows,
+                       float *delta, int B, int H, int Tq, int d, int dtype, void *stream);
+
+/* dK, dV as scfa_attn_bwd_dkdv_lists (reading delta from scfa_attn_bwd_prep),
+ * also writing each live tile's dS into slot col_base[...] + list position of
+ * ds (when every tile fits). */
+int scfa_attn_bwd_dkdv_ds_lists(const void *q, const void *k, const void *v,
+                                const float *lse, const void *dout, const float *delta,
+                                const int32_t *q_idx, const int32_t *k_idx,
+                                const int32_t *q_hash, const int32_t *k_hash,
+                                const int32_t *q_rows, const int32_t *k_rows,
+                                const int32_t *col_count, const int32_t *col_list,
+                                const int32_t *col_base, void *ds, long long ds_tiles,
+                                void *dk, void *dv,
+                                int B, int H, int Tq, int Tk, int d, int block, float scale,
+                                int dtype, unsigned flags, void *stream);
+
+/* dq from the stored dS tiles (enqueue after scfa_attn_bwd_dkdv_ds_lists on
+ * the same stream).  The remaining arguments are those of
+ * scfa_attn_bwd_dq_lists, used only by the recomputing fallback (which also
+ * rewrites delta with the same values). */
+int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v,
+                              const void *o, const float *lse, const void *dout,
+                              const int32_t *q_idx, const int32_t *k_idx,
+                              const int32_t *q_hash, const int32_t *k_hash,
+                              const int32_t *q_rows, const int32_t *k_rows,
+                              const int32_t *row_count, const int32_t *row_list,
+                              const int32_t *row_slot, const int32_t *col_base,
+                              const void *ds, long long ds_tiles,
+                              void *dq, float *delta,
+                              int B, int H, int Tq, int Tk, int d, int block, float scale,
+                              int dtype, unsigned flags, void *stream);
+
+/*
  * Row gather and scatter: the steps either side of the attention path.
  * Dropping tokens compacts Q/K/V to the kept rows, and Hash-sparse attention
  * reorders tokens by bucket; every row keeps its original position ("why

@@ -43,6 +43,11 @@ __all__ = [
     "attn_fwd_lists",
     "attn_bwd_dq_lists",
     "attn_bwd_dkdv_lists",
+    "tile_slots",
+    "ds_buffer",
+    "attn_bwd_prep",
+    "attn_bwd_dkdv_ds_lists",
+    "attn_bwd_dq_ds_lists",
     "workspace_size",
     "gather_rows",
     "scatter_rows",
@@ -247,6 +252,7 @@ def block_meta(q_idx, k_idx, q_hash=None, k_hash=None, *, block=64, with_cols=Tr
     if with_cols:
         out["col_count"] = torch.empty((B, H, nk), dtype=torch.int32, device=dev)
         out["col_list"] = torch.empty((B, H, nk, nq), dtype=torch.int32, device=dev)
+    out["block"] = block
     lists = (_ptr(out["row_count"]), _ptr(out["row_list"]), _ptr(out.get("col_count")), _ptr(out.get("col_list")))
     if exact:
         ws, nws = (None, 0)
@@ -329,6 +335,82 @@ def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash,
                                        float(scale), _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_bwd_dkdv_lists", rc)
     return dk, dv
+
+
+def tile_slots(meta):
+    """Slot numbering of the live tiles for the stored-dS backward (scfa_tile_slots).
+
+    Adds "col_base" (int32 [B*H*nk + 1], the live-tile count last) and "row_slot"
+    (int32 [B,H,nq,nk]) to ``meta`` (which needs column lists) and returns it.
+    """
+    B, H, nq, nk = meta["row_list"].shape
+    Tq_blocks, Tk_blocks = nq, nk
+    dev = meta["row_list"].device
+    meta["col_base"] = torch.empty(B * H * nk + 1, dtype=torch.int32, device=dev)
+    meta["row_slot"] = torch.empty((B, H, nq, nk), dtype=torch.int32, device=dev)
+    block = meta.get("block", 64)
+    # Tq / Tk only size the lists; any lengths with these block counts give the same result
+    rc = _LIB.scfa_tile_slots(_ptr(meta["row_count"]), _ptr(meta["row_list"]), _ptr(meta["col_count"]),
+                              _ptr(meta["col_list"]), B, H, Tq_blocks * block, Tk_blocks * block, block,
+                              _ptr(meta["col_base"]), _ptr(meta["row_slot"]), _stream())
+    _lib.check("scfa_tile_slots", rc)
+    return meta
+
+
+def ds_buffer(n_tiles, block=64, device="cuda"):
+    """A dS buffer of n_tiles tiles (bf16 [n_tiles, block, block]) for the stored-dS backward."""
+    return torch.empty((max(int(n_tiles), 0), block, block), dtype=torch.bfloat16, device=device)
+
+
+def attn_bwd_prep(o, lse, dout, *, q_rows=None, out=None):
+    """delta [2,B,H,Tq] float32 = (rowsum(dout * o), lse * log2 e) (scfa_attn_bwd_prep)."""
+    B, H, Tq, d = o.shape
+    _need(o, "o", torch.bfloat16)
+    _need(dout, "dout", torch.bfloat16, o.shape)
+    _need(lse, "lse", torch.float32, (B, H, Tq))
+    _need(q_rows, "q_rows", torch.int32, (B, H, Tq))
+    delta = out if out is not None else torch.empty((2, B, H, Tq), dtype=torch.float32, device=o.device)
+    rc = _LIB.scfa_attn_bwd_prep(_ptr(o), _ptr(lse), _ptr(dout), _ptr(q_rows), _ptr(delta), B, H, Tq, d,
+                                 _dtype_code(o), _stream())
+    _lib.check("scfa_attn_bwd_prep", rc)
+    return delta
+
+
+def attn_bwd_dkdv_ds_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash, meta, ds, *, block=64,
+                           scale=None, flags=0, out=None, q_rows=None, k_rows=None):
+    """dK, dV over column lists, storing every live tile's dS in ``ds`` (needs tile_slots(meta))."""
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _need(ds, "ds", torch.bfloat16)
+    dk, dv = out if out is not None else (torch.empty_like(k), torch.empty_like(v))
+    rc = _LIB.scfa_attn_bwd_dkdv_ds_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                          _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
+                                          *_rows_args(q_rows, k_rows, q, k), _ptr(meta["col_count"]),
+                                          _ptr(meta["col_list"]), _ptr(meta["col_base"]), _ptr(ds),
+                                          ds.shape[0] if ds.dim() == 3 else 0, _ptr(dk), _ptr(dv), B, H, Tq, Tk, d,
+                                          block, float(scale), _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_attn_bwd_dkdv_ds_lists", rc)
+    return dk, dv
+
+
+def attn_bwd_dq_ds_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta, ds, delta, *, block=64,
+                         scale=None, flags=0, out=None, q_rows=None, k_rows=None):
+    """dQ from the stored dS tiles (after attn_bwd_dkdv_ds_lists); falls back to recomputing when the
+    buffer was too small for every live tile."""
+    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _need(ds, "ds", torch.bfloat16)
+    dq = out if out is not None else torch.empty_like(q)
+    rc = _LIB.scfa_attn_bwd_dq_ds_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_idx),
+                                        _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, q, k),
+                                        _ptr(meta["row_count"]), _ptr(meta["row_list"]), _ptr(meta["row_slot"]),
+                                        _ptr(meta["col_base"]), _ptr(ds), ds.shape[0] if ds.dim() == 3 else 0,
+                                        _ptr(dq), _ptr(delta), B, H, Tq, Tk, d, block, float(scale),
+                                        _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_attn_bwd_dq_ds_lists", rc)
+    return dq
 
 
 def gather_rows(src, index):

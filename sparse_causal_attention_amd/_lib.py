@@ -27,6 +27,10 @@ EXPORTED = (
     "scfa_attn_fwd_lists",
     "scfa_attn_bwd_dq_lists",
     "scfa_attn_bwd_dkdv_lists",
+    "scfa_tile_slots",
+    "scfa_attn_bwd_prep",
+    "scfa_attn_bwd_dkdv_ds_lists",
+    "scfa_attn_bwd_dq_ds_lists",
     "scfa_gather_rows",
     "scfa_scatter_rows",
     "scfa_workspace_size",
@@ -59,6 +63,7 @@ _i = ctypes.c_int
 _u = ctypes.c_uint
 _f = ctypes.c_float
 _sz = ctypes.c_size_t
+_i64 = ctypes.c_longlong
 
 _ATTN_TAIL = [_i, _i, _i, _i, _i, _i, _f, _i, _u, _p, _sz, _p]
 _LISTS_TAIL = [_i, _i, _i, _i, _i, _i, _f, _i, _u, _p]
@@ -76,6 +81,10 @@ _SIGNATURES = {
     "scfa_attn_fwd_lists": [_p] * 13 + _LISTS_TAIL,
     "scfa_attn_bwd_dq_lists": [_p] * 16 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_lists": [_p] * 16 + _LISTS_TAIL,
+    "scfa_tile_slots": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p],
+    "scfa_attn_bwd_prep": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p],
+    "scfa_attn_bwd_dkdv_ds_lists": [_p] * 16 + [_i64] + [_p, _p] + _LISTS_TAIL,
+    "scfa_attn_bwd_dq_ds_lists": [_p] * 17 + [_i64] + [_p, _p] + _LISTS_TAIL,
     "scfa_gather_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p],
     "scfa_scatter_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p],
     "scfa_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],

@@ -111,6 +111,11 @@ struct AttnCall {
   float *out_lse;
   void *dq, *dk, *dv;
   float *delta;  // list entry points only
+  // stored-dS backward (list entry points): the dS buffer and the tile slots
+  bool ds_path;
+  void *ds;
+  long long ds_tiles;
+  const int32_t *row_slot, *col_base;
   Shape s;
   unsigned flags;
   void *ws;
@@ -176,6 +181,16 @@ int attention(const AttnCall &c) {
       return rc;
   }
   const bool no_prune = (c.flags & SCFA_FLAG_NO_PRUNE) != 0;
+  if (c.ds_path) {
+    if (s.dtype != SCFA_DTYPE_BF16) return fail(SCFA_ERR_UNSUPPORTED, "stored-dS backward needs dtype bf16");
+    if (dense) return fail(SCFA_ERR_UNSUPPORTED, "stored-dS backward needs positions (pruned modes; no lists in dense)");
+    if (no_prune) return fail(SCFA_ERR_UNSUPPORTED, "stored-dS backward walks the lists: SCFA_FLAG_NO_PRUNE unsupported");
+    if (c.ds_tiles < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "ds_tiles must be >= 0");
+    if ((rc = check_ptr(c.ds, c.ds_tiles * s.block * s.block, 16, "ds")) ||
+        (rc = check_ptr(c.col_base, BH * nk + 1, 4, "col_base")))
+      return rc;
+    if (c.kind == kBwdDq && (rc = check_ptr(c.row_slot, BH * nq * nk, 4, "row_slot"))) return rc;
+  }
   // lists (list entry points) or workspace (the others)
   if (c.api == kApiLists) {
     if (!dense && !no_prune) {
@@ -222,6 +237,10 @@ int attention(const AttnCall &c) {
   a.scale = s.scale;
   a.no_prune = no_prune ? 1 : 0;
   a.force_mask = (c.flags & SCFA_FLAG_FORCE_MASK) ? 1 : 0;
+  a.ds = c.ds;
+  a.ds_tiles = c.ds_tiles;
+  a.row_slot = c.row_slot;
+  a.col_base = c.col_base;
 
   if (c.api == kApiLists) {
     a.row_cnt = c.row_cnt;
@@ -274,6 +293,8 @@ int attention(const AttnCall &c) {
   hipError_t e;
   if (c.kind == kFwd) {
     e = bf16 ? scfa::launch_attn_fwd_bf16(a, mode, st) : scfa::launch_attn_fwd_f32(a, mode, st);
+  } else if (c.ds_path) {
+    e = scfa::launch_attn_bwd_ds_bf16(a, mode, c.kind == kBwdDq ? 1 : 2, st);
   } else {
     const int part = c.kind == kBwdAll ? 3 : (c.kind == kBwdDq ? 1 : 2);
     e = bf16 ? scfa::launch_attn_bwd_bf16(a, mode, part, st) : scfa::launch_attn_bwd_f32(a, mode, part, st);
@@ -476,6 +497,90 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v, const 
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
   c.q_rows = q_rows, c.k_rows = k_rows;
   c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list, const int32_t *col_count,
+                    const int32_t *col_list, int B, int H, int Tq, int Tk, int block, int32_t *col_base,
+                    int32_t *row_slot, void *stream) {
+  if (B < 1 || H < 1 || Tq < 0 || Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tk >= 0 required");
+  if (block != 64 && block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
+  const long long BH = (long long)B * H;
+  const long long nq = nblocks(Tq, block), nk = nblocks(Tk, block);
+  if (BH * nq * nk >= (1ll << 31)) return fail(SCFA_ERR_INVALID_ARGUMENT, "metadata too large");
+  int rc;
+  if ((rc = check_ptr(row_count, BH * nq, 4, "row_count")) || (rc = check_ptr(row_list, BH * nq * nk, 4, "row_list")) ||
+      (rc = check_ptr(col_count, BH * nk, 4, "col_count")) || (rc = check_ptr(col_list, BH * nk * nq, 4, "col_list")) ||
+      (rc = check_ptr(col_base, BH * nk + 1, 4, "col_base")) || (rc = check_ptr(row_slot, BH * nq * nk, 4, "row_slot")))
+    return rc;
+  const hipError_t e = scfa::launch_tile_slots(row_count, row_list, col_count, col_list, (int)BH, (int)nq, (int)nk,
+                                               col_base, row_slot, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tile slots");
+  return ok();
+}
+
+int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows, float *delta, int B,
+                       int H, int Tq, int d, int dtype, void *stream) {
+  if (B < 1 || H < 1 || Tq < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq >= 0 required");
+  if (d != 64 && d != 128) return fail(SCFA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
+  if (dtype != SCFA_DTYPE_BF16) return fail(SCFA_ERR_UNSUPPORTED, "scfa_attn_bwd_prep needs dtype bf16");
+  const long long BH = (long long)B * H;
+  if (BH * Tq * d >= (1ll << 31)) return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*Tq*d must be < 2^31");
+  int rc;
+  if ((rc = check_ptr(o, BH * Tq * d, 16, "o")) || (rc = check_ptr(lse, BH * Tq, 4, "lse")) ||
+      (rc = check_ptr(dout, BH * Tq * d, 16, "dout")) || (rc = check_ptr(q_rows, q_rows ? BH * Tq : 0, 4, "q_rows")) ||
+      (rc = check_ptr(delta, 2 * BH * Tq, 4, "delta")))
+    return rc;
+  scfa::AttnArgs a{};
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.q_rows = q_rows;
+  a.delta = delta;
+  a.BH = (int)BH;
+  a.Tq = Tq;
+  a.d = d;
+  const hipError_t e = scfa::launch_attn_bwd_prep(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess");
+  return ok();
+}
+
+int scfa_attn_bwd_dkdv_ds_lists(const void *q, const void *k, const void *v, const float *lse, const void *dout,
+                                const float *delta, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                                const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                                const int32_t *col_count, const int32_t *col_list, const int32_t *col_base, void *ds,
+                                long long ds_tiles, void *dk, void *dv, int B, int H, int Tq, int Tk, int d, int block,
+                                float scale, int dtype, unsigned flags, void *stream) {
+  AttnCall c{};
+  c.kind = kBwdDkdv;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.lse = lse, c.dout = dout, c.delta = const_cast<float *>(delta);
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
+  c.ds_path = true, c.ds = ds, c.ds_tiles = ds_tiles, c.col_base = col_base;
+  c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                              const void *dout, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                              const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                              const int32_t *row_count, const int32_t *row_list, const int32_t *row_slot,
+                              const int32_t *col_base, const void *ds, long long ds_tiles, void *dq, float *delta,
+                              int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags,
+                              void *stream) {
+  AttnCall c{};
+  c.kind = kBwdDq;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.row_cnt = row_count, c.row_list = row_list, c.dq = dq, c.delta = delta;
+  c.ds_path = true, c.ds = const_cast<void *>(ds), c.ds_tiles = ds_tiles, c.row_slot = row_slot, c.col_base = col_base;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;
   return attention(c);

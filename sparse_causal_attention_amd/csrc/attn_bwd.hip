@@ -16,6 +16,13 @@
 //  * dK/dV kernel: one work group per key block, walking its column list
 //    (live query blocks).  Lanes own key columns: S = Q K^T, dP = dO V^T,
 //    dV^T += dO^T P, dK^T += Q^T dS.
+//
+// Stored-dS variant (bf16, pruned modes): a preprocess kernel writes D and
+// lse * log2 e; the dK/dV kernel also stores every live tile's bf16 dS^T
+// (key-major, the values its dK product uses) in that tile's slot; the dQ
+// kernel is then a plain block-sparse product dQ^T += K^T dS^T over the row
+// lists, with no exponent, mask or dP.  The recomputing dQ kernel stays as
+// the fallback when the dS buffer is too small.
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
 #include "scfa_pipe.hpp"
@@ -95,10 +102,13 @@ __device__ __forceinline__ void col_tile(const AttnArgs &a, LiveList &cl, int t,
 struct Chunk {
   int t, ch, r0, nvalid;
   bool free;
+  int slot;  // stored-dS slot of the chunk's tile (dQ kernel over stored dS), else -1
 };
 
+// `sl` (nullable): the entries' dS slots, read through a register window like the list.
 template <int MODE, int BS, bool ROWS>
-__device__ __forceinline__ bool next_chunk(const AttnArgs &a, LiveList &ls, int self, int t, int ch, Chunk &out) {
+__device__ __forceinline__ bool next_chunk(const AttnArgs &a, LiveList &ls, int self, int t, int ch, Chunk &out,
+                                           LiveList *sl = nullptr) {
   constexpr int NCH = BS / kChunk;
   const int n_other = ROWS ? a.nk : a.nq;
   const int T_other = ROWS ? a.Tk : a.Tq;
@@ -115,6 +125,7 @@ __device__ __forceinline__ bool next_chunk(const AttnArgs &a, LiveList &ls, int 
     out.r0 = r0;
     out.nvalid = min(kChunk, T_other - r0);
     out.free = free;
+    out.slot = sl ? list_entry(*sl, t) : -1;
     return true;
   }
   return false;
@@ -145,6 +156,8 @@ template <int MODE, int D, int BS, bool KROWS>
 __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_bwd_dq_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) KVBufB<D> sb[2];
+  // As the stored-dS path's fallback, run only when the dS buffer was too small.
+  if (a.dq_fallback && a.col_base[(size_t)a.BH * a.nk] <= a.ds_tiles) return;
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.nq;
@@ -310,13 +323,18 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     }
   }
 
-  if (qvalid) {
-    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + qrow) * D;
+  // Store addresses recomputed from an opaque copy of the thread id (nothing
+  // lane-derived stays live across the chunk loop).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int qrow_e = qb * BS + 32 * (tid >> 6) + (tid & 31), half_e = (tid >> 5) & 1;
+  if (qrow_e < a.Tq) {
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + qrow_e) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * half;
+        const int d0 = 32 * mt + 8 * g + 4 * half_e;
         *reinterpret_cast<uint2 *>(dQ + d0) =
             make_uint2(pack_bf16x2(dqa[mt][4 * g] * a.scale, dqa[mt][4 * g + 1] * a.scale),
                        pack_bf16x2(dqa[mt][4 * g + 2] * a.scale, dqa[mt][4 * g + 3] * a.scale));
@@ -329,7 +347,11 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
 // ---------------------------------------------------------------------------
 // QROWS: Q and dO chunk rows come through a.q_rows (indices loaded one chunk
 // ahead); K and V rows come through a.k_rows when it is set.
-template <int MODE, int D, int BS, bool QROWS>
+// STORE: also write each tile's bf16 dS^T into its slot (col_base[bh*nk + kb]
+// + list position), unless the buffer is too small for all tiles.  A tile is
+// stored as 16-query groups, [BS/16][BS keys][16 queries], so each store
+// instruction writes a contiguous kilobyte.
+template <int MODE, int D, int BS, bool QROWS, bool STORE>
 __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_bwd_dkdv_bf16(AttnArgs a) {
   constexpr int NW = BS / 32;
   __shared__ __attribute__((aligned(16))) QGBuf<D> sb[2];
@@ -359,12 +381,18 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (MODE == kHash) my_hash = a.k_hash[koff + krow];
   }
   LiveList cl = col_list_b<MODE, BS>(a, bh, kb);
+  // STORE: this key block's first dS slot (its tiles take consecutive slots in list order)
+  const int slot0 = STORE ? a.col_base[(size_t)bh * a.nk + kb] : 0;
+  const bool store = STORE && a.col_base[(size_t)a.BH * a.nk] <= a.ds_tiles;
   // Consumed here, where the list window's wait already covers this older load;
   // first used after the chunk copies, its wait would also drain them.
   asm volatile("" : "+v"(ksrc_raw));
   const DmaOffsets<D, NW> dmo = dma_offsets<D, NW>();
   const LaneOffsets<D> lo = lane_offsets<D>();
   const int32_t *qrows = QROWS ? a.q_rows + qoff : nullptr;
+  // STORE on a key block with rows past Tk: every chunk is masked, so those rows
+  // (position kIdxTailK, after every query) get P = 0 and store dS = 0.
+  const bool mask_all = STORE && (kb + 1) * BS > a.Tk;
   DmaRows<D, NW> drn;  // QROWS: source rows of the next chunk to copy
   auto issue = [&](QGBuf<D> &b, const Chunk &c) {
     if constexpr (QROWS) {
@@ -376,7 +404,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     }
     if (w == 0) dma_vec(b.lse2, lse2g, c.r0, c.nvalid);
     if (w == NW - 1) dma_vec(b.del, delg, c.r0, c.nvalid);
-    if (MODE != kDense && !(c.free && c.nvalid == kChunk)) {
+    if (MODE != kDense && (mask_all || !(c.free && c.nvalid == kChunk))) {
       if (w == 0) dma_vec(b.idx, a.q_idx + qoff, c.r0, c.nvalid);
       if (MODE == kHash && w == NW - 1) dma_vec(b.hash, a.q_hash + qoff, c.r0, c.nvalid);
     }
@@ -412,6 +440,21 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
       dva[mt][r] = 0.f;
     }
 
+  // STORE: the dS^T of a chunk's second 32-query half is held in registers and
+  // stored after the next chunk's top-of-loop wait.  Stores count in the same
+  // counter as the chunk copies, so a store issued at the end of a chunk would
+  // be waited for right away by that wait; issued after it, the store has a
+  // whole chunk to complete.
+  uint4 held[2] = {};
+  size_t held_off = 0;  // element offset of the held half's 16-query block in ds (lane part excluded)
+  bool held_valid = false;
+  const size_t lane_ds = (size_t)(32 * w + col) * 16 + 8 * half;  // this lane's key row and query octet
+  auto store_held = [&](size_t lane_off) {
+    uint16_t *p = static_cast<uint16_t *>(a.ds) + held_off + lane_off;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) *reinterpret_cast<uint4 *>(p + (size_t)t2 * BS * 16) = held[t2];
+  };
+
   int buf = 0;
   while (have) {
     Chunk nxt2;
@@ -423,13 +466,17 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (have_next) issue(sb[buf ^ 1], nxt);
     if constexpr (QROWS)
       if (have_next2) dma_rows_load<D, NW>(drn, qrows, nxt2.r0, nxt2.nvalid);
+    if constexpr (STORE) {
+      if (held_valid) store_held(lane_ds);
+      held_valid = false;
+    }
     const QGBuf<D> &b = sb[buf];
     // Key rows past Tk only pollute their own (never stored) columns, so a
     // mask-free tile needs masking only for query rows past Tq.
     // The chunk is processed as two halves of 32 query rows; each half is
     // S, dP (4 independent chains) -> P, dS -> dV^T, dK^T, so the second
     // half's products can overlap the first half's exponent and mask work.
-    const bool tail = cur.nvalid < kChunk, masked = tail || !cur.free;
+    const bool tail = cur.nvalid < kChunk, masked = tail || !cur.free || mask_all;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       bf16x8 qfr[D / 16], gfr[D / 16];
@@ -479,11 +526,35 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const bf16x8 pb = as_bf16x8(c_regs_to_u4(s1[0], t2));
-        const bf16x8 db = as_bf16x8(c_regs_to_u4(dp1[0], t2));
+        const uint4 du = c_regs_to_u4(dp1[0], t2);
+        const bf16x8 db = as_bf16x8(du);
+        uint4 dsw = {};  // STORE: 8 consecutive queries of this lane's key (see below)
+        if constexpr (STORE) {
+          // Lane halves hold the query quads {0-3, 8-11} (half 0) and {4-7, 12-15} (half 1) of this
+          // 16-query group (x, y: first quad; z, w: second).  Half 0 sends its second quad and takes
+          // the partner's first; half 1 the reverse: queries 0-7 end in half 0, 8-15 in half 1.
+          const uint32_t s0 = half ? du.x : du.z, s1 = half ? du.y : du.w;
+          const uint32_t r0 = __shfl_xor(s0, 32, 64), r1 = __shfl_xor(s1, 32, 64);
+          dsw = half ? make_uint4(r0, r1, du.z, du.w) : make_uint4(du.x, du.y, r0, r1);
+        }
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
           dva[mt] = mfma32(gtr[t2][mt], pb, dva[mt]);
           dka[mt] = mfma32(qtr[t2][mt], db, dka[mt]);
+        }
+        if constexpr (STORE) {
+          // Tile layout: 16-query groups [BS/16][BS keys][16 queries]; this (ch, sub, t2) is group
+          // 4 ch + 2 sub + t2, and one wave's store covers 32 keys x 32 bytes, contiguous.
+          if (store) {
+            const size_t off = (size_t)(slot0 + cur.t) * BS * BS + (size_t)(4 * cur.ch + 2 * sub) * BS * 16;
+            if (sub == 0) {
+              *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.ds) + off + (size_t)t2 * BS * 16 + lane_ds) = dsw;
+            } else {
+              held[t2] = dsw;
+              held_off = off;
+              held_valid = true;
+            }
+          }
         }
       }
     }
@@ -495,20 +566,211 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
       have_next = have_next2;
     }
   }
+  if constexpr (STORE) {
+    if (held_valid) {
+      int tid = threadIdx.x;  // lane offset recomputed: nothing lane-derived stays live past the loop
+      asm volatile("" : "+v"(tid));
+      store_held((size_t)(32 * (tid >> 6) + (tid & 31)) * 16 + 8 * ((tid >> 5) & 1));  // as lane_ds
+    }
+  }
 
   if (kvalid_row) {
-    uint16_t *dK = static_cast<uint16_t *>(a.dk) + (koff + krow) * D;
-    uint16_t *dV = static_cast<uint16_t *>(a.dv) + (koff + krow) * D;
+    // The store addresses are recomputed here from an opaque copy of the thread
+    // id, so no address stays live across the chunk loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const size_t krow_e = (size_t)kb * BS + 32 * (tid >> 6) + (tid & 31);
+    const int half_e = (tid >> 5) & 1;
+    uint16_t *dK = static_cast<uint16_t *>(a.dk) + (koff + krow_e) * D;
+    uint16_t *dV = static_cast<uint16_t *>(a.dv) + (koff + krow_e) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * half;
+        const int d0 = 32 * mt + 8 * g + 4 * half_e;
         *reinterpret_cast<uint2 *>(dK + d0) =
             make_uint2(pack_bf16x2(dka[mt][4 * g] * a.scale, dka[mt][4 * g + 1] * a.scale),
                        pack_bf16x2(dka[mt][4 * g + 2] * a.scale, dka[mt][4 * g + 3] * a.scale));
         *reinterpret_cast<uint2 *>(dV + d0) = make_uint2(pack_bf16x2(dva[mt][4 * g], dva[mt][4 * g + 1]),
                                                          pack_bf16x2(dva[mt][4 * g + 2], dva[mt][4 * g + 3]));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward preprocess (stored-dS path): D = rowsum(dO * O) and lse * log2 e,
+// summed exactly as the recomputing dQ kernel sums them (each 64-lane half of
+// a row's 16-column groups sequentially with fused multiply-adds, then the
+// two halves added), so both paths see the same D.  Two lanes per row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_prep(AttnArgs a) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = g >> 1;  // over BH * Tq
+  const int half = (int)(g & 1);
+  const bool valid = row < (long long)a.BH * a.Tq;
+  float dsum = 0.f;
+  float lse = 0.f;
+  if (valid) {
+    const long long bh = row / a.Tq;
+    const int i = (int)(row - bh * a.Tq);
+    const int src = a.q_rows ? min(max(a.q_rows[row], 0), a.Tq - 1) : i;
+    const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + ((size_t)bh * a.Tq + src) * D;
+    const uint16_t *O = static_cast<const uint16_t *>(a.o) + (size_t)row * D;
+    lse = a.lse[row];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const uint4 ud = ld16(dO + 16 * kk + 8 * half), uo = ld16(O + 16 * kk + 8 * half);
+      const uint32_t dw[4] = {ud.x, ud.y, ud.z, ud.w};
+      const uint32_t ow[4] = {uo.x, uo.y, uo.z, uo.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = fmaf(bf16_bits_to_float(dw[e] & 0xffffu), bf16_bits_to_float(ow[e] & 0xffffu), dsum);
+        dsum = fmaf(bf16_bits_to_float(dw[e] >> 16), bf16_bits_to_float(ow[e] >> 16), dsum);
+      }
+    }
+  }
+  const float other = __shfl_xor(dsum, 1, 64);
+  if (valid && half == 0) {
+    a.delta[row] = dsum + other;
+    a.delta[(size_t)a.BH * a.Tq + row] = lse * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ from stored dS: one work group per query block walking its row list;
+// entry t's tile is in slot row_slot[t] (read through a register window like
+// the list).  2*BS/32 waves: wave w owns queries 32*(w % QW)..+31 (QW = BS/32)
+// and half of the head dimension (d-tiles (w / QW)*D/64 ..), so twice the
+// waves share each staged chunk.  Each 64-key chunk stages the K rows (through
+// a.k_rows when KROWS) and the tile's dS^T rows [64 keys][BS queries] in LDS;
+// both operands of dQ^T += K^T dS^T are transposed reads over the same key
+// rows.
+// ---------------------------------------------------------------------------
+template <int D, int BS>
+struct DsBuf {
+  MatChunk<D> k;
+  MatChunk<BS> ds;
+};
+
+// DMA source offsets that gather one 64-key chunk of a stored tile (16-query
+// groups [BS/16][BS keys][16 queries], offsets relative to the chunk's first
+// key row) into the row-major swizzled MatChunk<BS> layout: LDS piece s holds
+// logical piece lp = (s % CPR) ^ swz(r) (queries 8 lp..) of chunk row r = s / CPR.
+template <int BS, int NW>
+__device__ __forceinline__ DmaOffsets<BS, NW> dma_offsets_ds() {
+  using O = DmaOffsets<BS, NW>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  O o;
+#pragma unroll
+  for (int k = 0; k < O::PER_WAVE; ++k) {
+    const int s = (k * NW + w) * 64 + lane;
+    const int r = s / O::CPR, lp = (s % O::CPR) ^ swz(r);
+    o.off[k] = (lp >> 1) * BS * 16 + r * 16 + (lp & 1) * 8;
+  }
+  return o;
+}
+
+template <int D, int BS, bool KROWS>
+__global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
+  constexpr int QW = BS / 32;
+  constexpr int NW = 2 * QW;
+  constexpr int MTW = D / 64;  // d-tiles of 32 per wave
+  __shared__ __attribute__((aligned(16))) DsBuf<D, BS> sb[2];
+  if (a.col_base[(size_t)a.BH * a.nk] > a.ds_tiles) return;  // tiles not stored: the fallback computes dQ
+
+  // Query blocks in reverse order: the dK/dV kernel wrote the tiles in roughly ascending block order, so
+  // the most recently written (still cached) tiles are read first.
+  const int wg = (int)gridDim.x - 1 - xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.nq;
+  const int qb = wg % a.nq;
+  const int w = threadIdx.x >> 6;
+  const int qw = w % QW, mh = w / QW;
+  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
+  const uint16_t *DS = static_cast<const uint16_t *>(a.ds);
+  const size_t row = (size_t)bh * a.nq + qb;
+  LiveList rl{min(a.row_cnt[row], a.nk), 0, a.row_list + row * a.nk, a.nk, 0, 0};
+  LiveList sl{rl.n, 0, a.row_slot + row * a.nk, a.nk, 0, 0};
+  list_window2(rl, sl, 0);
+  const DmaOffsets<D, NW> dmk = dma_offsets<D, NW>();
+  const DmaOffsets<BS, NW> dms = dma_offsets_ds<BS, NW>();
+  int k_off[MTW];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i) k_off[i] = trans_offset<D>(mh * MTW + i);
+  const int ds_off = trans_offset<BS>(qw);  // this wave's 32 query columns
+  const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
+  DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
+  auto issue = [&](DsBuf<D, BS> &b, const Chunk &c) {
+    if constexpr (KROWS) dma_matrix_rows<D, NW>(b.k, K, a.Tk, drn);
+    else dma_matrix<D, NW>(b.k, K, c.r0, c.nvalid, dmk);
+    // (an entry without a slot, which lists from the builder never have, reads tile 0)
+    const size_t slot = (size_t)max(min(c.slot, (int)min(a.ds_tiles - 1, (long long)INT32_MAX)), 0);
+    dma_matrix<BS, NW>(b.ds, DS + slot * BS * BS + (size_t)c.ch * kChunk * 16, 0, kChunk, dms);
+  };
+  Chunk cur;
+  bool have = next_chunk<kQK, BS, true>(a, rl, qb, 0, 0, cur, &sl);
+  if (have) {
+    if constexpr (KROWS) dma_rows_load<D, NW>(drn, krows, cur.r0, cur.nvalid);
+    issue(sb[0], cur);
+  }
+  Chunk nxt;
+  bool have_next = false;
+  if constexpr (KROWS) {
+    have_next = have && next_chunk<kQK, BS, true>(a, rl, qb, cur.t, cur.ch + 1, nxt, &sl);
+    if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.r0, nxt.nvalid);
+  }
+  f32x16 dqa[MTW];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqa[i][r] = 0.f;
+
+  int buf = 0;
+  while (have) {
+    Chunk nxt2;
+    bool have_next2 = false;
+    if constexpr (KROWS)
+      have_next2 = have_next && next_chunk<kQK, BS, true>(a, rl, qb, nxt.t, nxt.ch + 1, nxt2, &sl);
+    else have_next = next_chunk<kQK, BS, true>(a, rl, qb, cur.t, cur.ch + 1, nxt, &sl);
+    wait_vmem();
+    __syncthreads();
+    if (have_next) issue(sb[buf ^ 1], nxt);
+    if constexpr (KROWS)
+      if (have_next2) dma_rows_load<D, NW>(drn, krows, nxt2.r0, nxt2.nvalid);
+    const DsBuf<D, BS> &b = sb[buf];
+    bf16x8 ktr[4][MTW], dsb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dsb[t] = frag_trans_at<BS>(b.ds, ds_off, t);
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) ktr[t][i] = frag_trans_at<D>(b.k, k_off[i], t);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) dqa[i] = mfma32(ktr[t][i], dsb[t], dqa[i]);
+    buf ^= 1;
+    cur = nxt;
+    have = have_next;
+    if constexpr (KROWS) {
+      nxt = nxt2;
+      have_next = have_next2;
+    }
+  }
+
+  int tid = threadIdx.x;  // store addresses recomputed: nothing lane-derived stays live across the loop
+  asm volatile("" : "+v"(tid));
+  const int qrow_e = qb * BS + 32 * ((tid >> 6) % QW) + (tid & 31), half_e = (tid >> 5) & 1;
+  if (qrow_e < a.Tq) {
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + ((size_t)bh * a.Tq + qrow_e) * D;
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * (mh * MTW + i) + 8 * g + 4 * half_e;
+        *reinterpret_cast<uint2 *>(dQ + d0) =
+            make_uint2(pack_bf16x2(dqa[i][4 * g] * a.scale, dqa[i][4 * g + 1] * a.scale),
+                       pack_bf16x2(dqa[i][4 * g + 2] * a.scale, dqa[i][4 * g + 3] * a.scale));
       }
   }
 }
@@ -691,9 +953,11 @@ static hipError_t run_bwd_bf16(const AttnArgs &a, int part, hipStream_t s) {
   }
   if ((part & 2) && a.nk > 0) {
     if (a.q_rows)
-      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0, s, a);
+      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, true, false>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0,
+                         s, a);
     else
-      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0, s, a);
+      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, false, false>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64),
+                         0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -708,6 +972,39 @@ static hipError_t run_bwd_f32(const AttnArgs &a, int part, hipStream_t s) {
   }
   if ((part & 2) && a.nk > 0) {
     hipLaunchKernelGGL((k_bwd_dkdv_f32<MODE, D, BS>), dim3((unsigned)(a.BH * a.nk)), dim3(BS), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// Stored-dS backward.  part 2: dK/dV, storing the dS tiles; part 1: dQ from
+// them, then the recomputing dQ kernel as the guarded fallback (it exits at
+// once unless the buffer was too small).
+template <int MODE, int D, int BS>
+static hipError_t run_bwd_ds_bf16(const AttnArgs &a, int part, hipStream_t s) {
+  if ((part & 2) && a.nk > 0) {
+    if (a.q_rows)
+      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, true, true>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64), 0,
+                         s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_dkdv_bf16<MODE, D, BS, false, true>), dim3((unsigned)(a.BH * a.nk)), dim3(BS / 32 * 64),
+                         0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((part & 1) && a.nq > 0) {
+    if (a.k_rows)
+      hipLaunchKernelGGL((k_bwd_dq_ds_bf16<D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_bwd_dq_ds_bf16<D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AttnArgs f = a;
+    f.dq_fallback = 1;
+    if (a.k_rows)
+      hipLaunchKernelGGL((k_bwd_dq_bf16<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, f);
+    else
+      hipLaunchKernelGGL((k_bwd_dq_bf16<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 32 * 64), 0, s, f);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -741,6 +1038,32 @@ hipError_t launch_attn_bwd_bf16(const AttnArgs &a, int mode, int part, hipStream
 hipError_t launch_attn_bwd_f32(const AttnArgs &a, int mode, int part, hipStream_t s) {
   if (a.BH == 0) return hipSuccess;
   SCFA_DISPATCH_B(run_bwd_f32, a, mode, s);
+}
+
+hipError_t launch_attn_bwd_ds_bf16(const AttnArgs &a, int mode, int part, hipStream_t s) {
+  if (a.BH == 0) return hipSuccess;
+  const int key = (mode == kHash ? 4 : 0) + (a.d == 128 ? 2 : 0) + (a.block == 128 ? 1 : 0);
+  if (mode == kDense) return hipErrorInvalidValue;  // no lists, no slots
+  switch (key) {
+    case 0: return run_bwd_ds_bf16<kQK, 64, 64>(a, part, s);
+    case 1: return run_bwd_ds_bf16<kQK, 64, 128>(a, part, s);
+    case 2: return run_bwd_ds_bf16<kQK, 128, 64>(a, part, s);
+    case 3: return run_bwd_ds_bf16<kQK, 128, 128>(a, part, s);
+    case 4: return run_bwd_ds_bf16<kHash, 64, 64>(a, part, s);
+    case 5: return run_bwd_ds_bf16<kHash, 64, 128>(a, part, s);
+    case 6: return run_bwd_ds_bf16<kHash, 128, 64>(a, part, s);
+    case 7: return run_bwd_ds_bf16<kHash, 128, 128>(a, part, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_bwd_prep(const AttnArgs &a, hipStream_t s) {
+  const long long lanes = 2ll * a.BH * a.Tq;
+  if (lanes == 0) return hipSuccess;
+  const dim3 grid((unsigned)((lanes + 255) / 256));
+  if (a.d == 64) hipLaunchKernelGGL(k_bwd_prep<64>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_bwd_prep<128>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace scfa

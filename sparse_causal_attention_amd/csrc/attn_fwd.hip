@@ -278,11 +278,17 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   // buffers before they are reused for the exchange.  The exchange goes in
   // rounds of QX query waves when all QW do not fit the buffers at once.
   float lt = pair_sum(l);
+  // Lane-derived values of the epilogue are recomputed from an opaque copy of
+  // the thread id, so none of them stays live across the chunk loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane_e = tid & 63, half_e = lane_e >> 5, qw_e = (tid >> 6) % QW;
+  const int qrow_e = qb * BS + 32 * qw_e + (lane_e & 31);
   constexpr int XN = 2 + 16 * (D / 32);  // floats per lane: reference max, sum, accumulator
   constexpr int FIT = (int)(sizeof(sb) / (sizeof(float) * XN * 64));
   constexpr int QX = FIT >= QW ? QW : (FIT >= 2 ? 2 : 1);
   static_assert(FIT >= 1 && QW % QX == 0, "exchange does not fit the chunk buffers");
-  float *xch = reinterpret_cast<float *>(sb) + (size_t)(qw % QX) * XN * 64 + lane;
+  float *xch = reinterpret_cast<float *>(sb) + (size_t)(qw_e % QX) * XN * 64 + lane_e;
   float m = mref;
 #pragma unroll
   for (int round = 0; round < QW / QX; ++round) {
@@ -312,18 +318,18 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   if (kh == 1) return;
 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qvalid) {
-    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + qrow) * D;
+  if (qrow_e < a.Tq) {
+    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + qrow_e) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * half;
+        const int d0 = 32 * mt + 8 * g + 4 * half_e;
         const uint2 val = make_uint2(pack_bf16x2(acc[mt][4 * g] * inv, acc[mt][4 * g + 1] * inv),
                                      pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv));
         *reinterpret_cast<uint2 *>(O + d0) = val;
       }
-    if (half == 0) a.out_lse[(size_t)bh * a.Tq + qrow] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+    if (half_e == 0) a.out_lse[(size_t)bh * a.Tq + qrow_e] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
   }
 }
 

@@ -190,6 +190,99 @@ __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, i
   if (lane == 0) *cnt_out = count;
 }
 
+// ---------------------------------------------------------------------------
+// Tile slots: a numbering of the live tiles for the backward's stored dS.
+// Slots follow the column lists: key block c (over all heads, c = bh*nk + j)
+// owns slots col_base[c] .. col_base[c] + count - 1, in its list order, so the
+// dK/dV kernel writes a key block's tiles to consecutive slots.  The dQ
+// kernel walks row lists; row_slot gives, for each row-list entry, the slot of
+// that tile (col_base of its key block + the rank of query block i in that
+// block's column list).
+// ---------------------------------------------------------------------------
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 16;
+
+__device__ __forceinline__ int clamp_count(int c, int hi) { return min(max(c, 0), hi); }
+
+// Exclusive scan of the (clamped) counts over all heads; base[n] is the total.
+__global__ __launch_bounds__(kScanThreads) void k_count_scan(const int32_t *cnt, int n, int cap, int32_t *base) {
+  __shared__ int wave_tot[kScanThreads / 64];
+  __shared__ int carry_s;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  if (t == 0) carry_s = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < n; b0 += kScanThreads * kScanItems) {
+    const int first = b0 + t * kScanItems;
+    int v[kScanItems];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      v[k] = first + k < n ? clamp_count(cnt[first + k], cap) : 0;
+      sum += v[k];
+    }
+    // inclusive scan of the thread sums within the wave, then across waves
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wave_tot[w] = inc;
+    __syncthreads();
+    int wave_off = 0;
+    for (int k = 0; k < w; ++k) wave_off += wave_tot[k];
+    int run = carry_s + wave_off + inc - sum;  // exclusive prefix of this thread's first item
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      if (first + k < n) base[first + k] = run;
+      run += v[k];
+    }
+    __syncthreads();  // every thread has read carry_s and wave_tot
+    if (t == kScanThreads - 1) carry_s = run;
+    __syncthreads();
+  }
+  if (t == 0) base[n] = carry_s;
+}
+
+// row_slot[bh, i, t] = slot of the tile (i, j) named by row-list entry t
+// (-1 if key block j's column list does not hold i, which lists from the
+// builder never do).
+__global__ __launch_bounds__(64) void k_row_slots(const int32_t *row_cnt, const int32_t *row_list,
+                                                  const int32_t *col_cnt, const int32_t *col_list,
+                                                  const int32_t *col_base, int32_t *row_slot, int nq, int nk) {
+  const int bh = blockIdx.x / nq;
+  const int i = blockIdx.x % nq;
+  const size_t rrow = ((size_t)bh * nq + i) * nk;
+  const int n = clamp_count(row_cnt[(size_t)bh * nq + i], nk);
+  for (int t = threadIdx.x; t < n; t += 64) {
+    const int j = row_list[rrow + t] & 0x7fffffff;
+    int slot = -1;
+    if (j < nk) {
+      const int32_t *cl = col_list + ((size_t)bh * nk + j) * nq;
+      const int m = clamp_count(col_cnt[(size_t)bh * nk + j], nq);
+      int lo = 0, hi = m;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((cl[mid] & 0x7fffffff) < i) lo = mid + 1;
+        else hi = mid;
+      }
+      if (lo < m && (cl[lo] & 0x7fffffff) == i) slot = col_base[(size_t)bh * nk + j] + lo;
+    }
+    row_slot[rrow + t] = slot;
+  }
+}
+
+hipError_t launch_tile_slots(const int32_t *row_cnt, const int32_t *row_list, const int32_t *col_cnt,
+                             const int32_t *col_list, int BH, int nq, int nk, int32_t *col_base, int32_t *row_slot,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_count_scan, dim3(1), dim3(kScanThreads), 0, s, col_cnt, BH * nk, nq, col_base);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || BH * nq == 0) return e;
+  hipLaunchKernelGGL(k_row_slots, dim3((unsigned)(BH * nq)), dim3(64), 0, s, row_cnt, row_list, col_cnt, col_list,
+                     col_base, row_slot, nq, nk);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s) {
   const int hash_mode = a.q_hash != nullptr;
   if (a.nq + a.nk > 0) {

@@ -32,6 +32,16 @@ struct AttnArgs {
   int BH, Tq, Tk, nq, nk, d, block;
   float scale;
   int no_prune, force_mask;
+  // Stored dS (bf16 tiles [block keys][block queries], one per live tile, in the
+  // slots of the tile-slot numbering): the dK/dV kernel writes key block c's
+  // tiles to slots col_base[c] + t, the dQ kernel reads the tiles named by
+  // row_slot.  ds_tiles is the buffer's capacity; when the total tile count
+  // col_base[BH*nk] exceeds it, nothing is stored and the recomputing dQ kernel
+  // (dq_fallback) runs instead of the stored-dS one.
+  void *ds;
+  const int32_t *row_slot, *col_base;
+  long long ds_tiles;
+  int dq_fallback;
 };
 
 // Row gather / scatter: [BH, Ts, row] <-> [BH, Td, row], rows of ppr 16-byte
@@ -91,6 +101,11 @@ struct LshArgs {
 };
 
 hipError_t launch_block_meta(const MetaArgs &a, bool with_cols, hipStream_t s);
+// col_base [BH*nk + 1] (exclusive scan of the column counts, total last) and
+// row_slot [BH, nq, nk] (slot of each row-list entry's tile).
+hipError_t launch_tile_slots(const int32_t *row_cnt, const int32_t *row_list, const int32_t *col_cnt,
+                             const int32_t *col_list, int BH, int nq, int nk, int32_t *col_base, int32_t *row_slot,
+                             hipStream_t s);
 
 // Sets the calling thread's scfa_last_error() message and returns `code`.
 int report_error(int code, const char *msg);
@@ -102,6 +117,11 @@ hipError_t launch_attn_fwd_f32(const AttnArgs &a, int mode, hipStream_t s);
 // part: bit 0 = dQ (+ D = rowsum(dO * O)), bit 1 = dK/dV (reads D).
 hipError_t launch_attn_bwd_bf16(const AttnArgs &a, int mode, int part, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const AttnArgs &a, int mode, int part, hipStream_t s);
+// Backward preprocess: delta[0] = rowsum(dO * O), delta[1] = lse * log2 e (bf16).
+hipError_t launch_attn_bwd_prep(const AttnArgs &a, hipStream_t s);
+// Stored-dS backward (bf16, pruned modes): part 2 = dK/dV writing dS tiles,
+// part 1 = dQ from the dS tiles (+ the guarded recomputing fallback).
+hipError_t launch_attn_bwd_ds_bf16(const AttnArgs &a, int mode, int part, hipStream_t s);
 
 hipError_t launch_lsh_bucket_sort(const LshArgs &a, hipStream_t s);
 

@@ -85,6 +85,15 @@ __device__ __forceinline__ void list_window(LiveList &l, int base) {
   asm volatile("" : "+v"(l.win));
 }
 
+// Two windows loaded together, so their loads share one wait.
+__device__ __forceinline__ void list_window2(LiveList &l, LiveList &m, int base) {
+  l.base = m.base = base;
+  const int i = base + (int)(threadIdx.x & 63);
+  l.win = i < l.lim ? l.p[i] : 0;
+  m.win = i < m.lim ? m.p[i] : 0;
+  asm volatile("" : "+v"(l.win), "+v"(m.win));
+}
+
 // Stored entry t (t >= base; uniform across the wave).
 __device__ __forceinline__ int list_entry(LiveList &l, int t) {
   if (t - l.base >= 64) list_window(l, t & ~63);
@@ -256,6 +265,16 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets() {
   return o;
 }
 
+// LaneOffsets<D>::trans[mt] for a run-time (wave-uniform) mt.
+template <int D>
+__device__ __forceinline__ int trans_offset(int mt) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, a = j & 3, mm = j >> 2, g = lane >> 4, h = g >> 1;
+  const int x = 4 * h + mm;
+  const int c = 4 * mt + 2 * (g & 1) + (a >> 1);
+  return x * D + ((c ^ swz(x)) << 3) + 4 * (a & 1);
+}
+
 template <int D>
 __device__ __forceinline__ bf16x8 frag_rows(const MatChunk<D> &m, const LaneOffsets<D> &o, int sub, int kk) {
   return as_bf16x8(*reinterpret_cast<const uint4 *>(m.v + o.rows[kk] + 32 * sub * D));
@@ -265,6 +284,20 @@ __device__ __forceinline__ bf16x8 frag_rows(const MatChunk<D> &m, const LaneOffs
 template <int D>
 __device__ __forceinline__ bf16x8 frag_trans(const MatChunk<D> &m, const LaneOffsets<D> &o, int mt, int t) {
   const uint16_t *p0 = m.v + o.trans[mt] + 16 * t * D;
+#if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only
+  const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0));
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0 + 8 * D));
+#else
+  const i16x4 x0 = {}, x1 = {};
+#endif
+  const uint2 lo = __builtin_bit_cast(uint2, x0), hi = __builtin_bit_cast(uint2, x1);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// frag_trans with the lane offset given directly (trans_offset<D>(mt)).
+template <int D>
+__device__ __forceinline__ bf16x8 frag_trans_at(const MatChunk<D> &m, int off, int t) {
+  const uint16_t *p0 = m.v + off + 16 * t * D;
 #if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only
   const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0));
   const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0 + 8 * D));

@@ -192,6 +192,23 @@ def test_noalloc_rejects_oversize_shapes_on_the_host():
     assert lib.scfa_workspace_size(_lib.OP_HASH_FWD, 2, 12, 16384, 16384, 64, 64, 0) <= cap
 
 
+def test_stored_ds_validation():
+    lib = _lib.load()
+
+    def dq(qi=P2, dtype=0, flags=0, tiles=10, ds=P):
+        return lib.scfa_attn_bwd_dq_ds_lists(P, P, P, P, P2, P, qi, qi, None, None, None, None, P2, P2, P2, P2, ds,
+                                             tiles, P, P2, 1, 1, 100, 100, 64, 64, 0.125, dtype, flags, None)
+
+    assert dq(qi=None) == _lib.ERR_UNSUPPORTED  # dense: no lists, no slots
+    assert dq(dtype=1) == _lib.ERR_UNSUPPORTED  # bf16 only
+    assert dq(flags=_lib.FLAG_NO_PRUNE) == _lib.ERR_UNSUPPORTED
+    assert dq(tiles=-1) == _lib.ERR_INVALID_ARGUMENT
+    assert dq(ds=P + 8) == _lib.ERR_INVALID_ARGUMENT  # 16-byte alignment
+    assert lib.scfa_tile_slots(P2, P2, P2, P2, 1, 1, 100, 100, 96, P2, P2, None) == _lib.ERR_UNSUPPORTED
+    assert lib.scfa_tile_slots(P2, P2, P2, P2, 1, 1, 100, 100, 64, None, P2, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.scfa_attn_bwd_prep(P, P2, P, None, P2, 1, 1, 100, 64, 1, None) == _lib.ERR_UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_LIB", None)

@@ -26,7 +26,7 @@ def _scfa():
 def _compare_meta(out, c, block, exact=False, heads=None):
     B, H, Tq = c.q_idx.shape
     hashed = c.q_hash is not None
-    got = {k: v.cpu().numpy() for k, v in out.items()}
+    got = {k: v.cpu().numpy() for k, v in out.items() if hasattr(v, "cpu")}
     for b in range(B):
         for h in range(H):
             if heads is not None and (b, h) not in heads:

@@ -3,8 +3,10 @@
 ``bench.run_step`` is called exactly as the benchmark times it on the 16k
 Hash-sparse training workload (2 x 12 heads, 16,384 tokens, d = 64, 32
 buckets): one LSH + sort call over Q and K stacked in one allocation, exact
-block lists, and the attention kernels reading Q, dO, K and V through the sort
-permutations (the ``_lists`` entry points).  The oracle recomputes every bucket
+block lists with tile slots, and the attention kernels reading Q, dO, K and V
+through the sort permutations (the ``_lists`` entry points).  Both backward
+paths run on the same inputs: the recomputing one the benchmark times by
+default, and the stored-dS one (``--stored-ds``).  The oracle recomputes every bucket
 id, permutation and block list bit for bit, O, lse and all gradients densely
 on two full heads, and sampled query rows and key rows of every other head.
 """
@@ -51,11 +53,21 @@ def test_timed_step_matches_oracle():
     q, k, v, do, R, qk = bench.make_inputs(w, torch)
     note("[timed step] run_step (stacked sort, exact lists, permuted rows)")
     meta, outs = bench.run_step(scfa, w, q, k, v, do, R, exact=True, copy_sorted=False, qk=qk)
+    note("[timed step] run_step with the stored-dS backward")
+    ds = bench.prepare_ds(scfa, torch, w, q, k, R, qk, exact=True)
+    meta_ds, outs_ds = bench.run_step(scfa, w, q, k, v, do, R, exact=True, copy_sorted=False, qk=qk, ds=ds)
     torch.cuda.synchronize()
+    assert int(meta_ds["col_base"][-1].item()) <= ds.shape[0]  # every tile stored: dQ came from dS
+    for n in ("row_count", "row_list", "col_count", "col_list"):
+        assert torch.equal(meta_ds[n], meta[n])
+    # same forward; dK, dV bit for bit (same kernel, D from the preprocess equals D from the dQ kernel)
+    for i in (0, 1, 3, 4):  # O, lse, dK, dV
+        assert torch.equal(outs_ds[i], outs[i]), i
+    dq_ds = to_np(outs_ds[2])
     got = {n: meta[n].cpu().numpy() for n in ("row_count", "row_list", "col_count", "col_list", "q_hash", "q_idx",
                                               "q_perm", "k_hash", "k_idx", "k_perm")}
     o, lse, dq, dk, dv = (to_np(t) for t in outs)
-    del q, k, v, do, qk, meta, outs
+    del q, k, v, do, qk, meta, outs, ds, meta_ds, outs_ds
     rng = np.random.default_rng(16384)
     full_heads = {(0, 0), (w.B - 1, w.H - 1)}
     for b in range(w.B):
@@ -82,12 +94,14 @@ def test_timed_step_matches_oracle():
                 check_forward(o[b, h], lse[b, h], o_ref, lse_ref, "bf16", f"step b{b}h{h}")
                 ref = A.backward(qs, ks, vs, dos, iq, ik, hq, hk, w.scale)
                 check_grads([dq[b, h], dk[b, h], dv[b, h]], ref, "bf16", f"step b{b}h{h}")
+                check_grads([dq_ds[b, h], dk[b, h], dv[b, h]], ref, "bf16", f"step stored dS b{b}h{h}")
             else:
                 rows = _rows_sample(rng, w.Tq, 64)
                 o_ref, lse_ref = A.forward_rows(rows, qs, ks, vs, iq, ik, hq, hk, w.scale)
                 check_forward(o[b, h][rows], lse[b, h][rows], o_ref, lse_ref, "bf16", f"step rows b{b}h{h}")
                 dq_ref = A.backward_rows(rows, qs, ks, vs, dos, iq, ik, hq, hk, w.scale)
                 assert rel_fro(dq[b, h][rows], dq_ref) <= 5e-2, (b, h)
+                assert rel_fro(dq_ds[b, h][rows], dq_ref) <= 5e-2, (b, h)
                 keys = _rows_sample(rng, w.Tk, 32)
                 dk_ref, dv_ref = A.backward_key_rows(keys, qs, ks, vs, dos, iq, ik, hq, hk, w.scale)
                 assert rel_fro(dk[b, h][keys], dk_ref) <= 5e-2, (b, h)
