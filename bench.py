@@ -25,9 +25,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 --sweep-drop: QK-sparse training step (B=4, H=12, T=8192, d=64) at each drop
 rate: compaction (gather), forward + backward on the kept tokens,
-un-compaction (scatter), against the naive way of dropping tokens, which
-masks them inside dense causal attention at the full length and so costs
-the dense-causal step whatever the rate.
+un-compaction (scatter), against two naive ways of dropping tokens (the
+compacted tensors with every tile computed and then masked; full-length
+causal attention with the dropped tokens masked by position) and against
+dense causal attention with nothing dropped.
 --sweep-T: Hash-sparse (B=1, H=8, d=64, 32 buckets) at each length: LSH +
 sort of Q and K, forward + backward; up to 32k tokens also the dense-causal
 step and the naive hash attention (every tile computed, then masked:
@@ -356,30 +357,61 @@ def _dense_step(scfa, q, k, v, do):
 
 
 def sweep_drop(scfa, torch, rates, args):
+    """QK-sparse training step against the naive ways of dropping tokens, at each drop rate.
+
+    * scfa: compaction of Q, K, V, dO to the kept tokens, QK-sparse forward + backward (tile pruning on the
+      kept positions), outputs put back at the original positions;
+    * naive_compacted: the same compacted tensors, but every tile computed and then masked
+      (NO_PRUNE + FORCE_MASK): dropping without SCFA's tile rules;
+    * naive_full_masked: full-length causal attention with the dropped tokens masked out (a dropped query
+      carries position -1 and admits no key, a dropped key position 2^31 - 1 and no query admits it): the
+      dropped tokens still occupy the tiles;
+    * dense_causal: full-length causal attention, nothing dropped.
+    """
     B, H, T, d = 4, 12, 8192, 64
     q, k, v, do = (_gpu_normal(torch, (B, H, T, d), 100 + i) for i in range(4))
     dense_ms, _ = _time_steps(torch, lambda _: _dense_step(scfa, q, k, v, do), max(3, args.steps // 2),
                               max(1, args.warmup))
+    naive_flags = scfa.FLAG_NO_PRUNE | scfa.FLAG_FORCE_MASK
+    pos = torch.arange(T, device="cuda:0", dtype=torch.int32).expand(B, H, T)
     for rate in rates:
         n_keep = max(1, int(round((1.0 - rate) * T)))
         g = torch.Generator(device="cuda:0")
         g.manual_seed(7)
         keep = torch.stack([torch.stack([torch.sort(torch.randperm(T, generator=g, device="cuda:0")[:n_keep])[0]
                                          for _ in range(H)]) for _ in range(B)]).to(torch.int32).contiguous()
+        kept = torch.zeros((B, H, T), dtype=torch.bool, device="cuda:0")
+        kept.scatter_(2, keep.long(), True)
+        q_pos = torch.where(kept, pos, torch.full_like(pos, -1)).contiguous()
+        k_pos = torch.where(kept, pos, torch.full_like(pos, 2**31 - 1)).contiguous()
 
-        def step(_):
-            qc, kc, vc, gc = (scfa.gather_rows(x, keep) for x in (q, k, v, do))
-            o, lse = scfa.qk_sparse_fwd(qc, kc, vc, keep, keep)
-            grads = scfa.qk_sparse_bwd(qc, kc, vc, o, lse, gc, keep, keep)
-            for x in (o, *grads):
-                scfa.scatter_rows(x, keep, T)
+        def compacted(flags):
+            def step(_):
+                qc, kc, vc, gc = (scfa.gather_rows(x, keep) for x in (q, k, v, do))
+                o, lse = scfa.qk_sparse_fwd(qc, kc, vc, keep, keep, flags=flags)
+                grads = scfa.qk_sparse_bwd(qc, kc, vc, o, lse, gc, keep, keep, flags=flags)
+                for x in (o, *grads):
+                    scfa.scatter_rows(x, keep, T)
+            return step
 
-        ms, _ = _time_steps(torch, step, args.steps, args.warmup)
+        def full_masked(_):
+            o, lse = scfa.qk_sparse_fwd(q, k, v, q_pos, k_pos)
+            scfa.qk_sparse_bwd(q, k, v, o, lse, do, q_pos, k_pos)
+
+        ms, _ = _time_steps(torch, compacted(0), args.steps, args.warmup)
+        naive_c_ms, _ = _time_steps(torch, compacted(naive_flags), max(3, args.steps // 2), 1)
+        naive_f_ms, _ = _time_steps(torch, full_masked, max(3, args.steps // 2), 1)
         print(json.dumps({"sweep": "qk_drop_rate", "B": B, "H": H, "T": T, "d": d, "drop_rate": rate,
                           "kept": n_keep, "scfa_step_ms": round(ms, 4),
-                          "naive_token_drop_ms": round(dense_ms, 4), "speedup_vs_naive": round(dense_ms / ms, 3),
+                          "naive_compacted_ms": round(naive_c_ms, 4),
+                          "naive_full_masked_ms": round(naive_f_ms, 4), "dense_causal_ms": round(dense_ms, 4),
+                          "speedup_vs_naive_compacted": round(naive_c_ms / ms, 3),
+                          "speedup_vs_naive_full_masked": round(naive_f_ms / ms, 3),
+                          "speedup_vs_dense_causal": round(dense_ms / ms, 3),
+                          "naive_compacted_vs_dense_causal": round(dense_ms / naive_c_ms, 3),
                           "scfa_step": "gather Q,K,V,dO + QK-sparse fwd + bwd + scatter O,dQ,dK,dV",
-                          "naive": "dense causal fwd + bwd at full length (masking does not reduce its work)"}),
+                          "naive_compacted": "same, every tile computed then masked (NO_PRUNE + FORCE_MASK)",
+                          "naive_full_masked": "full-length causal fwd + bwd, dropped tokens masked by position"}),
               flush=True)
 
 
@@ -494,6 +526,238 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, qk, nbs, args):
         }), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# The other workloads (--workload 2, 3, 5): one JSON line each, same metric.
+# ---------------------------------------------------------------------------
+def _median(xs):
+    xs = sorted(xs)
+    m = len(xs) // 2
+    return xs[m] if len(xs) % 2 else 0.5 * (xs[m - 1] + xs[m])
+
+
+def _full_length_inputs(w, torch, names, seed):
+    """Full-length [B,H,T,d] bf16 tensors drawn on the GPU (seeded) and the workload's kept positions
+    [B,H,n_keep] (gen.keep_set, shared by Q and K)."""
+    import numpy as np
+
+    from gen import keep_set
+
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    full = [torch.randn((w.B, w.H, w.T, w.d), generator=g, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+            for _ in names]
+    keep = torch.from_numpy(np.stack([np.stack([keep_set(w, b, h)[0] for h in range(w.H)])
+                                      for b in range(w.B)])).to("cuda:0")
+    return dict(zip(names, full)), keep
+
+
+def _roofline(kernel, flops, ms):
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops}
+
+
+def bench_workload(scfa, torch, wid, args):
+    """One benchmark line for workload 2 (Hash-sparse forward, 8k tokens), 3 (QK-sparse training step with
+    30 % of the tokens dropped, 8k tokens) or 5 (50 % drop, then Hash-sparse forward, 1M tokens).  The step
+    runs every row of the hot path the workload has, from inputs resident in HBM:
+      2: LSH + sort of Q and K (one call over both), block lists, forward over the sorted view;
+      3: compaction of Q, K, V, dO to the kept tokens, block lists, forward, dQ, dK/dV, and the outputs put
+         back at the original positions (zero rows for dropped tokens);
+      5: compaction of Q, K, V, LSH + sort of the kept Q and K (one call), block lists, forward over the
+         sorted view, and O put back at the original positions.
+    The dense-causal comparator is the same library's dense mode on the original [B,H,T,d] tensors."""
+    import numpy as np
+
+    from gen import WORKLOADS, head_inputs, lsh_rotation
+
+    w = WORKLOADS[wid]
+    blk, sc = w.block, w.scale
+    dev = torch.device("cuda:0")
+    _log(f"[bench] workload {w.name}: inputs")
+    R = None
+    if w.n_buckets:
+        R = torch.from_numpy(np.stack([lsh_rotation(w, h) for h in range(w.H)])).to(dev)
+    if wid == 2:
+        heads = [[head_inputs(w, b, h) for h in range(w.H)] for b in range(w.B)]
+        st = lambda f: np.stack([np.stack([f(x) for x in row]) for row in heads])  # noqa: E731
+        to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
+        qk = to(np.concatenate([st(lambda x: x.q), st(lambda x: x.k)]))
+        q, k = qk[: w.B], qk[w.B:]
+        v = to(st(lambda x: x.v))
+        dense_in = (q, k, v, None)
+        calls = ["lsh_sort_qk", "block_meta", "fwd"]
+
+        def step(t):
+            if t:
+                t.begin()
+            hh, ii, pp, _, _ = scfa.lsh_bucket_sort(qk, R, w.n_buckets, want_x=False)
+            B = w.B
+            qh, kh, qi, ki = hh[:B], hh[B:], ii[:B], ii[B:]
+            if t:
+                t.mark()
+            meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=False, exact=True)
+            if t:
+                t.mark()
+            scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=blk, scale=sc, q_rows=pp[:B], k_rows=pp[B:])
+            if t:
+                t.mark()
+            return meta
+    elif wid == 3:
+        full, keep = _full_length_inputs(w, torch, ("q", "k", "v", "do"), 300 + wid)
+        dense_in = (full["q"], full["k"], full["v"], full["do"])
+        calls = ["compact", "block_meta", "fwd", "bwd_dq", "bwd_dkdv", "uncompact"]
+
+        def step(t):
+            if t:
+                t.begin()
+            qc, kc, vc, gc = (scfa.gather_rows(full[n], keep) for n in ("q", "k", "v", "do"))
+            if t:
+                t.mark()
+            meta = scfa.block_meta(keep, keep, block=blk, with_cols=True, exact=True)
+            if t:
+                t.mark()
+            o, lse = scfa.attn_fwd_lists(qc, kc, vc, keep, keep, None, None, meta, block=blk, scale=sc)
+            if t:
+                t.mark()
+            dq, delta = scfa.attn_bwd_dq_lists(qc, kc, vc, o, lse, gc, keep, keep, None, None, meta, block=blk,
+                                               scale=sc)
+            if t:
+                t.mark()
+            dk, dv = scfa.attn_bwd_dkdv_lists(qc, kc, vc, lse, gc, delta, keep, keep, None, None, meta, block=blk,
+                                              scale=sc)
+            if t:
+                t.mark()
+            for x in (o, dq, dk, dv):
+                scfa.scatter_rows(x, keep, w.T)
+            if t:
+                t.mark()
+            return meta
+    elif wid == 5:
+        full, keep = _full_length_inputs(w, torch, ("q", "k", "v"), 300 + wid)
+        dense_in = (full["q"], full["k"], full["v"], None)
+        B, n = w.B, w.n_keep
+        qk = torch.empty((2 * B, w.H, n, w.d), dtype=torch.bfloat16, device=dev)
+        keep2 = torch.cat([keep, keep]).contiguous()
+        calls = ["compact", "lsh_sort_qk", "block_meta", "fwd", "uncompact"]
+
+        def step(t):
+            if t:
+                t.begin()
+            scfa.gather_rows(full["q"], keep, out=qk[:B])
+            scfa.gather_rows(full["k"], keep, out=qk[B:])
+            vc = scfa.gather_rows(full["v"], keep)
+            if t:
+                t.mark()
+            hh, ii, pp, _, _ = scfa.lsh_bucket_sort(qk, R, w.n_buckets, idx=keep2, idx_ascending=True, want_x=False)
+            qh, kh, qi, ki = hh[:B], hh[B:], ii[:B], ii[B:]
+            if t:
+                t.mark()
+            meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=False, exact=True)
+            if t:
+                t.mark()
+            o, _ = scfa.attn_fwd_lists(qk[:B], qk[B:], vc, qi, ki, qh, kh, meta, block=blk, scale=sc,
+                                       q_rows=pp[:B], k_rows=pp[B:])
+            if t:
+                t.mark()
+            scfa.scatter_rows(o, qi, w.T)  # view row i holds the query at original position qi[i]
+            if t:
+                t.mark()
+            return meta
+    else:
+        raise SystemExit(f"--workload {wid}: choose 2, 3, 5 (4 is the default benchmark line)")
+
+    steps = args.steps if wid != 5 else max(3, min(args.steps, 5))
+    warm = args.warmup if wid != 5 else 1
+    for _ in range(warm):
+        step(None)
+    torch.cuda.synchronize()
+    _log(f"[bench] timing {steps} steps")
+    timer = Timer(torch, calls)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        meta = step(timer)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / steps * 1e3
+    timer.collect()
+    per_call = {n: round(timer.median_ms(n), 4) for n in calls}
+    units, tiles = tile_work(meta, w.Tq, w.Tk, blk, torch)
+    per_unit = 14.0 if w.train else 4.0
+    step_flops = per_unit * units * w.d
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    attn_ms = sum(v for n, v in per_call.items() if n in ("block_meta", "fwd", "bwd_dq", "bwd_dkdv"))
+
+    # dense causal at the original shape, same library
+    _log("[bench] dense causal reference")
+    dq_, dk_, dv_, do_ = dense_in
+    nd = 1 if wid == 5 else max(3, steps // 4)
+
+    def dense(t):
+        if t:
+            t.begin()
+        o, lse = scfa.attn_fwd_lists(dq_, dk_, dv_, None, None, None, None, None, block=blk, scale=sc)
+        if t:
+            t.mark()
+        if w.train:
+            g, delta = scfa.attn_bwd_dq_lists(dq_, dk_, dv_, o, lse, do_, None, None, None, None, None, block=blk,
+                                              scale=sc)
+            scfa.attn_bwd_dkdv_lists(dq_, dk_, dv_, lse, do_, delta, None, None, None, None, None, block=blk,
+                                     scale=sc)
+            if t:
+                t.mark()
+
+    dcalls = ["dense_fwd"] + (["dense_bwd"] if w.train else [])
+    dtimer = Timer(torch, dcalls)
+    dense(None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(nd):
+        dense(dtimer)
+    torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - t1) / nd * 1e3
+    dtimer.collect()
+    nblk = (w.T + blk - 1) // blk
+
+    kern = {"fwd": (f"k_fwd_bf16_ks<{'kQK' if w.mode == 'qk' else 'kHash'},{w.d},{blk},"
+                    f"{'false' if wid == 3 else 'true'}>", 4.0 * units * w.d)}
+    if w.train:
+        kern["bwd_dq"] = (f"k_bwd_dq_bf16<kQK,{w.d},{blk},false>", 2.0 * units * w.d)
+        kern["bwd_dkdv"] = (f"k_bwd_dkdv_bf16<kQK,{w.d},{blk},false,false>", 8.0 * units * w.d)
+    dominant = max(kern, key=lambda n: per_call[n])
+    out = {
+        "metric": "effective TFLOP/s (executed tiles, % bf16 MFMA peak) + speedup vs dense causal",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, seeded keep sets and Gaussian LSH rotations)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "kept": w.n_keep, "d": w.d, "block": blk,
+                   "n_buckets": w.n_buckets, "train": w.train, "step_calls": calls, "tile_rule": "exact"},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "executed_tiles": tiles,
+        "dense_causal_tiles": w.B * w.H * nblk * (nblk + 1) // 2,
+        "attention_only_tflops": round(step_flops / (attn_ms * 1e-3) / 1e12, 3),
+        "dense_causal_ms": round(dense_ms, 4),
+        "speedup_vs_dense_causal": round(dense_ms / ms_per_step, 3),
+        "speedup_vs_dense_causal_attention_only": round(dense_ms / attn_ms, 3),
+        "per_call_ms": per_call,
+        "step_median_ms_events": round(timer.step_median_ms(), 4),
+        "per_call_stat": f"median of {steps} HIP-event samples per call",
+        "dense_per_call_ms": {n: round(dtimer.median_ms(n), 4) for n in dcalls},
+        "roofline": _roofline(kern[dominant][0], kern[dominant][1], per_call[dominant]),
+        "kernel_rooflines": {n: _roofline(kn, fl, per_call[n]) for n, (kn, fl) in kern.items()},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -509,6 +773,8 @@ def main():
                          "(default: the dQ kernel recomputes S, P and dP, which measures faster on this workload)")
     ap.add_argument("--range-lists", action="store_true",
                     help="build the tile lists with the bucket-range rule only (keep tiles that hold no valid pair)")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_ID,
+                    help="2, 3 or 5: that workload's line instead of the default (4) benchmark line")
     ap.add_argument("--sweep-nb", type=str, default="", metavar="LIST",
                     help="comma-separated bucket counts: one JSON line per count instead of the benchmark line")
     ap.add_argument("--sweep-drop", type=str, default="", metavar="LIST", help="comma-separated drop rates")
@@ -533,6 +799,9 @@ def main():
         return
     if args.sweep_T:
         sweep_length(scfa, torch, [int(x) for x in args.sweep_T.split(",")], args)
+        return
+    if args.workload != WORKLOAD_ID:
+        bench_workload(scfa, torch, args.workload, args)
         return
 
     w = WORKLOADS[WORKLOAD_ID]

@@ -413,17 +413,20 @@ def attn_bwd_dq_ds_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, me
     return dq
 
 
-def gather_rows(src, index):
+def gather_rows(src, index, *, out=None):
     """dst[b, h, i] = src[b, h, index[b, h, i]] (zero rows for out-of-range indices).
 
     Compaction of kept tokens (index = their positions) or reordering (index =
-    a sort permutation).  src [B,H,T_src,d]; index [B,H,T_dst] int32.
+    a sort permutation).  src [B,H,T_src,d]; index [B,H,T_dst] int32.  ``out``
+    optionally supplies dst (contiguous [B,H,T_dst,d], e.g. a slice of a larger
+    allocation along B).
     """
     B, H, Ts, d = src.shape
     _need(src, "src")
     Td = index.shape[2]
     _need(index, "index", torch.int32, (B, H, Td))
-    dst = torch.empty((B, H, Td, d), dtype=src.dtype, device=src.device)
+    _need(out, "out", src.dtype, (B, H, Td, d))
+    dst = out if out is not None else torch.empty((B, H, Td, d), dtype=src.dtype, device=src.device)
     rc = _LIB.scfa_gather_rows(_ptr(src), _ptr(index), _ptr(dst), B, H, Ts, Td, d, _dtype_code(src), _stream())
     _lib.check("scfa_gather_rows", rc)
     return dst
