@@ -181,7 +181,8 @@ class Timer:
         return tot[m] if len(tot) % 2 else 0.5 * (tot[m - 1] + tot[m])
 
 
-def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False, qk=None, ds=None):
+def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False, qk=None, ds=None,
+             orig_rows=True):
     """One step.  By default the sorts return only bucket ids, positions and the permutations, and
     the attention kernels read Q, dO, K and V through the permutations (row indirection); with
     copy_sorted the sorts also copy the rows into sorted order and attention reads the copies.
@@ -194,7 +195,10 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False,
 
     With ds (a dS buffer, see prepare_ds) the backward stores every live tile's dS in the dK/dV
     kernel and computes dQ from the stored tiles (tile slots built with the lists, then the
-    preprocess for D, dK/dV, dQ); without it the dQ kernel recomputes S, P and dP."""
+    preprocess for D, dK/dV, dQ); without it the dQ kernel recomputes S, P and dP.
+
+    With orig_rows (the default) and rows read through the permutations, the kernels write O, lse,
+    dQ, dK and dV at the caller's rows (token order) directly: no separate un-sort."""
     nb, blk, sc = w.n_buckets, w.block, w.scale
     B = q.shape[0]
     if timer:
@@ -226,28 +230,30 @@ def run_step(scfa, w, q, k, v, do, R, timer=None, exact=True, copy_sorted=False,
         timer.mark()
     meta.update(q_hash=qh, q_idx=qi, k_hash=kh, k_idx=ki, **({"q_perm": rows["q_rows"], "k_perm": rows["k_rows"]}
                                                              if rows else {}))
-    o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc, **rows)
+    fl = scfa.FLAG_ORIG_ROWS if (orig_rows and rows) else 0
+    meta["outputs"] = "caller rows" if fl else "view rows"
+    o, lse = scfa.attn_fwd_lists(qs, ks, vs, qi, ki, qh, kh, meta, block=blk, scale=sc, flags=fl, **rows)
     if timer:
         timer.mark()
     if ds is None:
         dq, delta = scfa.attn_bwd_dq_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, block=blk, scale=sc,
-                                           **rows)
+                                           flags=fl, **rows)
         if timer:
             timer.mark()
         dk, dv = scfa.attn_bwd_dkdv_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, block=blk, scale=sc,
-                                          **rows)
+                                          flags=fl, **rows)
         if timer:
             timer.mark()
     else:
-        delta = scfa.attn_bwd_prep(o, lse, dos, q_rows=rows.get("q_rows"))
+        delta = scfa.attn_bwd_prep(o, lse, dos, q_rows=rows.get("q_rows"), flags=fl)
         if timer:
             timer.mark()
         dk, dv = scfa.attn_bwd_dkdv_ds_lists(qs, ks, vs, lse, dos, delta, qi, ki, qh, kh, meta, ds, block=blk,
-                                             scale=sc, **rows)
+                                             scale=sc, flags=fl, **rows)
         if timer:
             timer.mark()
         dq = scfa.attn_bwd_dq_ds_lists(qs, ks, vs, o, lse, dos, qi, ki, qh, kh, meta, ds, delta, block=blk,
-                                       scale=sc, **rows)
+                                       scale=sc, flags=fl, **rows)
         if timer:
             timer.mark()
     return meta, (o, lse, dq, dk, dv)
@@ -954,9 +960,10 @@ def main():
             "n_buckets": w.n_buckets,
             "step": ("lsh+sort(Q,dO) + lsh+sort(K,V) + block lists + fwd + bwd" if args.copy_sorted else
                      "lsh+sort of Q and K (one call over the stacked [2B,H,T,d] tensor) + block lists + fwd + bwd, "
-                     "rows read through the sort permutations"),
+                     "rows read through the sort permutations, outputs written at the caller's rows"),
             "tile_rule": "range" if args.range_lists else "exact",
             "rows": "copied" if args.copy_sorted else "permuted",
+            "outputs": meta["outputs"],
             "backward": "stored dS (dQ from the dK/dV kernel's dS tiles)" if ds is not None else
                         "recompute (dQ kernel recomputes S, P, dP)",
         },

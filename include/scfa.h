@@ -96,6 +96,11 @@ extern "C" {
 #define SCFA_FLAG_IDX_ASCENDING (1u << 2) /* scfa_lsh_bucket_sort: the caller guarantees idx is
                                              strictly ascending within each (b, h), which lets the
                                              sort run one pass instead of five */
+#define SCFA_FLAG_ORIG_ROWS (1u << 4)     /* list entry points with q_rows and k_rows: outputs (o,
+                                             lse, dq, dk, dv) and the backward's o / lse inputs are
+                                             indexed by the caller's rows (q_rows[i], k_rows[j]),
+                                             not by the view's rows; the results equal the view-
+                                             ordered ones put back with scfa_scatter_rows */
 
 /* Operation ids for scfa_workspace_size. */
 #define SCFA_OP_QK_FWD 0
@@ -368,10 +373,11 @@ int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list,
 
 /* Backward preprocess: delta [2,B,H,Tq] float32 = (rowsum(dout * o),
  * lse * log2(e)), as scfa_attn_bwd_dq_lists writes it.  o and lse are the
- * forward's outputs (view rows), dout [B,H,Tq,d] bf16, read through q_rows
- * when non-NULL (as in the list entry points). */
+ * forward's outputs (view rows; the caller's rows with SCFA_FLAG_ORIG_ROWS,
+ * the only flag), dout [B,H,Tq,d] bf16, read through q_rows when non-NULL
+ * (as in the list entry points). */
 int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows,
-                       float *delta, int B, int H, int Tq, int d, int dtype, void *stream);
+                       float *delta, int B, int H, int Tq, int d, int dtype, unsigned flags, void *stream);
 
 /* dK, dV as scfa_attn_bwd_dkdv_lists (reading delta from scfa_attn_bwd_prep),
  * also writing each live tile's dS into slot col_base[...] + list position of

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     FLAG_FORCE_MASK,
     FLAG_IDX_ASCENDING,
     FLAG_NO_PRUNE,
+    FLAG_ORIG_ROWS,
     ScfaError,
 )
 
@@ -55,6 +56,7 @@ __all__ = [
     "FLAG_NO_PRUNE",
     "FLAG_FORCE_MASK",
     "FLAG_IDX_ASCENDING",
+    "FLAG_ORIG_ROWS",
 ]
 
 
@@ -362,8 +364,9 @@ def ds_buffer(n_tiles, block=64, device="cuda"):
     return torch.empty((max(int(n_tiles), 0), block, block), dtype=torch.bfloat16, device=device)
 
 
-def attn_bwd_prep(o, lse, dout, *, q_rows=None, out=None):
-    """delta [2,B,H,Tq] float32 = (rowsum(dout * o), lse * log2 e) (scfa_attn_bwd_prep)."""
+def attn_bwd_prep(o, lse, dout, *, q_rows=None, out=None, flags=0):
+    """delta [2,B,H,Tq] float32 = (rowsum(dout * o), lse * log2 e) (scfa_attn_bwd_prep); flags may hold
+    FLAG_ORIG_ROWS (o and lse at the caller's rows)."""
     B, H, Tq, d = o.shape
     _need(o, "o", torch.bfloat16)
     _need(dout, "dout", torch.bfloat16, o.shape)
@@ -371,7 +374,7 @@ def attn_bwd_prep(o, lse, dout, *, q_rows=None, out=None):
     _need(q_rows, "q_rows", torch.int32, (B, H, Tq))
     delta = out if out is not None else torch.empty((2, B, H, Tq), dtype=torch.float32, device=o.device)
     rc = _LIB.scfa_attn_bwd_prep(_ptr(o), _ptr(lse), _ptr(dout), _ptr(q_rows), _ptr(delta), B, H, Tq, d,
-                                 _dtype_code(o), _stream())
+                                 _dtype_code(o), int(flags), _stream())
     _lib.check("scfa_attn_bwd_prep", rc)
     return delta
 

@@ -50,6 +50,7 @@ FLAG_NO_PRUNE = 1 << 0
 FLAG_FORCE_MASK = 1 << 1
 FLAG_IDX_ASCENDING = 1 << 2
 FLAG_ZERO_FILL = 1 << 3
+FLAG_ORIG_ROWS = 1 << 4
 
 OP_QK_FWD = 0
 OP_QK_BWD = 1
@@ -82,7 +83,7 @@ _SIGNATURES = {
     "scfa_attn_bwd_dq_lists": [_p] * 16 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_lists": [_p] * 16 + _LISTS_TAIL,
     "scfa_tile_slots": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p],
-    "scfa_attn_bwd_prep": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p],
+    "scfa_attn_bwd_prep": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _u, _p],
     "scfa_attn_bwd_dkdv_ds_lists": [_p] * 16 + [_i64] + [_p, _p] + _LISTS_TAIL,
     "scfa_attn_bwd_dq_ds_lists": [_p] * 17 + [_i64] + [_p, _p] + _LISTS_TAIL,
     "scfa_gather_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p],

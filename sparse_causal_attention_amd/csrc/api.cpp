@@ -128,8 +128,8 @@ int attention(const AttnCall &c) {
   const Shape &s = c.s;
   int rc = check_shape(s);
   if (rc) return rc;
-  if (c.flags & ~(SCFA_FLAG_NO_PRUNE | SCFA_FLAG_FORCE_MASK))
-    return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", c.flags);
+  const unsigned known = SCFA_FLAG_NO_PRUNE | SCFA_FLAG_FORCE_MASK | (c.api == kApiLists ? SCFA_FLAG_ORIG_ROWS : 0u);
+  if (c.flags & ~known) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", c.flags);
   const long long BH = (long long)s.B * s.H;
   const long long nQ = BH * s.Tq * s.d, nK = BH * s.Tk * s.d;
   const long long nQi = BH * s.Tq, nKi = BH * s.Tk;
@@ -181,6 +181,9 @@ int attention(const AttnCall &c) {
       return rc;
   }
   const bool no_prune = (c.flags & SCFA_FLAG_NO_PRUNE) != 0;
+  const bool orig_rows = (c.flags & SCFA_FLAG_ORIG_ROWS) != 0;
+  if (orig_rows && (c.q_rows == nullptr || c.k_rows == nullptr) && (nQi > 0 || nKi > 0))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "SCFA_FLAG_ORIG_ROWS needs both q_rows and k_rows");
   if (c.ds_path) {
     if (s.dtype != SCFA_DTYPE_BF16) return fail(SCFA_ERR_UNSUPPORTED, "stored-dS backward needs dtype bf16");
     if (dense) return fail(SCFA_ERR_UNSUPPORTED, "stored-dS backward needs positions (pruned modes; no lists in dense)");
@@ -237,6 +240,7 @@ int attention(const AttnCall &c) {
   a.scale = s.scale;
   a.no_prune = no_prune ? 1 : 0;
   a.force_mask = (c.flags & SCFA_FLAG_FORCE_MASK) ? 1 : 0;
+  a.orig_rows = orig_rows ? 1 : 0;
   a.ds = c.ds;
   a.ds_tiles = c.ds_tiles;
   a.row_slot = c.row_slot;
@@ -522,10 +526,13 @@ int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list, const int
 }
 
 int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows, float *delta, int B,
-                       int H, int Tq, int d, int dtype, void *stream) {
+                       int H, int Tq, int d, int dtype, unsigned flags, void *stream) {
   if (B < 1 || H < 1 || Tq < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq >= 0 required");
   if (d != 64 && d != 128) return fail(SCFA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
   if (dtype != SCFA_DTYPE_BF16) return fail(SCFA_ERR_UNSUPPORTED, "scfa_attn_bwd_prep needs dtype bf16");
+  if (flags & ~SCFA_FLAG_ORIG_ROWS) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
+  if ((flags & SCFA_FLAG_ORIG_ROWS) && q_rows == nullptr && B * H * (long long)Tq > 0)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "SCFA_FLAG_ORIG_ROWS needs q_rows");
   const long long BH = (long long)B * H;
   if (BH * Tq * d >= (1ll << 31)) return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*Tq*d must be < 2^31");
   int rc;
@@ -542,6 +549,7 @@ int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const 
   a.BH = (int)BH;
   a.Tq = Tq;
   a.d = d;
+  a.orig_rows = (flags & SCFA_FLAG_ORIG_ROWS) ? 1 : 0;
   const hipError_t e = scfa::launch_attn_bwd_prep(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward preprocess");
   return ok();

@@ -176,7 +176,9 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   // Loads that depend only on this lane's own row go first: issued after the
   // list and chunk copies, a wait for them would also wait for those copies.
   int qsrc_raw = a.q_rows && qvalid ? a.q_rows[qoff + qrow] : qrow;  // clamped where used
-  float lse_raw = qvalid ? a.lse[qoff + qrow] : 0.f;
+  // lse (and O below) are read at the caller's row when outputs live there
+  const int lrow = a.orig_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
+  float lse_raw = qvalid ? a.lse[qoff + lrow] : 0.f;
   int my_idx = kIdxTailQ, my_hash = 0;
   if (qvalid) {
     my_idx = MODE == kDense ? qrow : a.q_idx[qoff + qrow];
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   float dsum = 0.f;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const size_t off = (size_t)qrow * D + 16 * kk + 8 * half;
+    const size_t off = (size_t)(a.orig_rows ? qsrc : qrow) * D + 16 * kk + 8 * half;
     const size_t soff = (size_t)qsrc * D + 16 * kk + 8 * half;
     const uint4 z = make_uint4(0, 0, 0, 0);
     const uint4 uq = qvalid ? ld16(Q + soff) : z;
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   asm volatile("" : "+v"(tid));
   const int qrow_e = qb * BS + 32 * (tid >> 6) + (tid & 31), half_e = (tid >> 5) & 1;
   if (qrow_e < a.Tq) {
-    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + qrow_e) * D;
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + out_row_q(a, bh, qrow_e)) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -579,10 +581,11 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     // id, so no address stays live across the chunk loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const size_t krow_e = (size_t)kb * BS + 32 * (tid >> 6) + (tid & 31);
+    const int krow_e = kb * BS + 32 * (tid >> 6) + (tid & 31);
     const int half_e = (tid >> 5) & 1;
-    uint16_t *dK = static_cast<uint16_t *>(a.dk) + (koff + krow_e) * D;
-    uint16_t *dV = static_cast<uint16_t *>(a.dv) + (koff + krow_e) * D;
+    const size_t orow = (size_t)out_row_k(a, bh, krow_e);
+    uint16_t *dK = static_cast<uint16_t *>(a.dk) + (koff + orow) * D;
+    uint16_t *dV = static_cast<uint16_t *>(a.dv) + (koff + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -616,8 +619,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(AttnArgs a) {
     const int i = (int)(row - bh * a.Tq);
     const int src = a.q_rows ? min(max(a.q_rows[row], 0), a.Tq - 1) : i;
     const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + ((size_t)bh * a.Tq + src) * D;
-    const uint16_t *O = static_cast<const uint16_t *>(a.o) + (size_t)row * D;
-    lse = a.lse[row];
+    const size_t orow = a.orig_rows ? (size_t)bh * a.Tq + src : (size_t)row;  // o and lse at the caller's rows
+    const uint16_t *O = static_cast<const uint16_t *>(a.o) + orow * D;
+    lse = a.lse[orow];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const uint4 ud = ld16(dO + 16 * kk + 8 * half), uo = ld16(O + 16 * kk + 8 * half);
@@ -762,7 +766,7 @@ __global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
   asm volatile("" : "+v"(tid));
   const int qrow_e = qb * BS + 32 * ((tid >> 6) % QW) + (tid & 31), half_e = (tid >> 5) & 1;
   if (qrow_e < a.Tq) {
-    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + ((size_t)bh * a.Tq + qrow_e) * D;
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + ((size_t)bh * a.Tq + out_row_q(a, bh, qrow_e)) * D;
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll

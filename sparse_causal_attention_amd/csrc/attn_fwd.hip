@@ -319,7 +319,8 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow_e < a.Tq) {
-    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + qrow_e) * D;
+    const int orow = out_row_q(a, bh, qrow_e);
+    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
                                      pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv));
         *reinterpret_cast<uint2 *>(O + d0) = val;
       }
-    if (half_e == 0) a.out_lse[(size_t)bh * a.Tq + qrow_e] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+    if (half_e == 0) a.out_lse[(size_t)bh * a.Tq + orow] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
   }
 }
 

@@ -42,7 +42,20 @@ struct AttnArgs {
   const int32_t *row_slot, *col_base;
   long long ds_tiles;
   int dq_fallback;
+  // With row indirection: outputs (O, lse, dQ, dK, dV) and the backward's o / lse
+  // inputs are indexed by the caller's rows (q_rows[i], k_rows[j]) instead of the
+  // view's rows i, j; delta stays indexed by the view.
+  int orig_rows;
 };
+
+// Caller row of view query row i (view key row j): through the permutation when
+// outputs go to the caller's rows, clamped into the head.
+__device__ __forceinline__ int out_row_q(const AttnArgs &a, size_t bh, int i) {
+  return a.orig_rows ? min(max(a.q_rows[bh * a.Tq + i], 0), a.Tq - 1) : i;
+}
+__device__ __forceinline__ int out_row_k(const AttnArgs &a, size_t bh, int j) {
+  return a.orig_rows ? min(max(a.k_rows[bh * a.Tk + j], 0), a.Tk - 1) : j;
+}
 
 // Row gather / scatter: [BH, Ts, row] <-> [BH, Td, row], rows of ppr 16-byte
 // pieces, index [BH, Td] (gather) or [BH, Ts] (scatter).

@@ -206,7 +206,23 @@ def test_stored_ds_validation():
     assert dq(ds=P + 8) == _lib.ERR_INVALID_ARGUMENT  # 16-byte alignment
     assert lib.scfa_tile_slots(P2, P2, P2, P2, 1, 1, 100, 100, 96, P2, P2, None) == _lib.ERR_UNSUPPORTED
     assert lib.scfa_tile_slots(P2, P2, P2, P2, 1, 1, 100, 100, 64, None, P2, None) == _lib.ERR_INVALID_ARGUMENT
-    assert lib.scfa_attn_bwd_prep(P, P2, P, None, P2, 1, 1, 100, 64, 1, None) == _lib.ERR_UNSUPPORTED
+    assert lib.scfa_attn_bwd_prep(P, P2, P, None, P2, 1, 1, 100, 64, 1, 0, None) == _lib.ERR_UNSUPPORTED
+    assert lib.scfa_attn_bwd_prep(P, P2, P, None, P2, 1, 1, 100, 64, 0, _lib.FLAG_ORIG_ROWS, None) == \
+        _lib.ERR_INVALID_ARGUMENT  # caller rows need q_rows
+
+
+def test_orig_rows_flag_validation():
+    lib = _lib.load()
+
+    def fwd(q_rows=None, k_rows=None, flags=_lib.FLAG_ORIG_ROWS):
+        return lib.scfa_attn_fwd_lists(P, P, P, P2, P2, None, None, q_rows, k_rows, P2, P2, P, P2, 1, 1, 100, 100,
+                                       64, 64, 0.125, 0, flags, None)
+
+    assert fwd() == _lib.ERR_INVALID_ARGUMENT  # no row indirection
+    assert fwd(q_rows=P2) == _lib.ERR_INVALID_ARGUMENT  # both needed
+    # not a flag of the one-call entry points
+    assert lib.scfa_qk_sparse_fwd(P, P, P, P2, P2, P, P2, 1, 2, 100, 100, 64, 64, 0.125, 0, _lib.FLAG_ORIG_ROWS,
+                                  P, 1 << 30, None) == _lib.ERR_INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

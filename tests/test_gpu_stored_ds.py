@@ -130,3 +130,54 @@ def test_stored_ds_falls_back_when_the_buffer_is_small():
         torch.cuda.synchronize()
         for a_, b_ in zip(ref, got):
             assert torch.equal(a_, b_), f"capacity {cap}"
+
+
+@pytest.mark.parametrize("mode,d,block,Tq,Tk", [("hash", 64, 64, 1500, 1400), ("qk", 64, 64, 777, 1000),
+                                                ("hash", 128, 128, 900, 1100), ("hash", 64, 128, 500, 450)])
+def test_outputs_at_caller_rows(mode, d, block, Tq, Tk):
+    """SCFA_FLAG_ORIG_ROWS: the forward, both backward paths and the preprocess read and write at the
+    caller's rows; every result equals the view-ordered one put back with scatter_rows, bit for bit."""
+    scfa = _lib()
+    B, H = 2, 2
+    c = synthetic_case(64, B=B, H=H, Tq=Tq, Tk=Tk, d=d, dtype="bf16", mode=mode, nb=5, layout="grouped")
+    note(f"[caller rows] {mode} d={d} block={block} Tq={Tq} Tk={Tk}")
+    q, k, v, do = (dev(x).to(torch.bfloat16) for x in (c.q, c.k, c.v, c.do))
+    qi, ki = dev(c.q_idx), dev(c.k_idx)
+    qh, kh = (dev(c.q_hash), dev(c.k_hash)) if mode == "hash" else (None, None)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(11)
+    qr = torch.stack([torch.stack([torch.randperm(Tq, generator=g, device="cuda:0") for _ in range(H)])
+                      for _ in range(B)]).to(torch.int32)
+    kr = torch.stack([torch.stack([torch.randperm(Tk, generator=g, device="cuda:0") for _ in range(H)])
+                      for _ in range(B)]).to(torch.int32)
+    rows = {"q_rows": qr, "k_rows": kr}
+    F = scfa.FLAG_ORIG_ROWS
+    meta = scfa.tile_slots(scfa.block_meta(qi, ki, qh, kh, block=block, with_cols=True, exact=True))
+    torch.cuda.synchronize()
+    ds = scfa.ds_buffer(int(meta["col_base"][-1].item()), block)
+    # view order
+    o, lse = scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=block, **rows)
+    dq, delta = scfa.attn_bwd_dq_lists(q, k, v, o, lse, do, qi, ki, qh, kh, meta, block=block, **rows)
+    dk, dv = scfa.attn_bwd_dkdv_lists(q, k, v, lse, do, delta, qi, ki, qh, kh, meta, block=block, **rows)
+    # caller order
+    o2, lse2 = scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=block, flags=F, **rows)
+    dq2, delta2 = scfa.attn_bwd_dq_lists(q, k, v, o2, lse2, do, qi, ki, qh, kh, meta, block=block, flags=F, **rows)
+    dk2, dv2 = scfa.attn_bwd_dkdv_lists(q, k, v, lse2, do, delta2, qi, ki, qh, kh, meta, block=block, flags=F,
+                                        **rows)
+    delta3 = scfa.attn_bwd_prep(o2, lse2, do, q_rows=qr, flags=F)
+    dk3, dv3 = scfa.attn_bwd_dkdv_ds_lists(q, k, v, lse2, do, delta3, qi, ki, qh, kh, meta, ds, block=block, flags=F,
+                                           **rows)
+    dq3 = scfa.attn_bwd_dq_ds_lists(q, k, v, o2, lse2, do, qi, ki, qh, kh, meta, ds, delta3, block=block, flags=F,
+                                    **rows)
+    dq_v = scfa.attn_bwd_dq_ds_lists(q, k, v, o, lse, do, qi, ki, qh, kh, meta, ds, delta, block=block, **rows)
+    torch.cuda.synchronize()
+    un = lambda x, r, T: scfa.scatter_rows(x, r, T, zero_fill=False)  # noqa: E731
+    assert torch.equal(o2, un(o, qr, Tq))
+    lse_back = torch.empty_like(lse)
+    lse_back.scatter_(2, qr.long(), lse)
+    assert torch.equal(lse2, lse_back)
+    assert torch.equal(delta2, delta) and torch.equal(delta3, delta)  # delta stays in view order
+    assert torch.equal(dq2, un(dq, qr, Tq))
+    assert torch.equal(dk2, un(dk, kr, Tk)) and torch.equal(dv2, un(dv, kr, Tk))
+    assert torch.equal(dk3, dk2) and torch.equal(dv3, dv2)
+    assert torch.equal(dq3, un(dq_v, qr, Tq))

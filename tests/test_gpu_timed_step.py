@@ -4,7 +4,8 @@
 Hash-sparse training workload (2 x 12 heads, 16,384 tokens, d = 64, 32
 buckets): one LSH + sort call over Q and K stacked in one allocation, exact
 block lists with tile slots, and the attention kernels reading Q, dO, K and V
-through the sort permutations (the ``_lists`` entry points).  Both backward
+through the sort permutations (the ``_lists`` entry points) and writing O, lse
+and the gradients at the caller's rows (token order).  Both backward
 paths run on the same inputs: the recomputing one the benchmark times by
 default, and the stored-dS one (``--stored-ds``).  The oracle recomputes every bucket
 id, permutation and block list bit for bit, O, lse and all gradients densely
@@ -58,15 +59,18 @@ def test_timed_step_matches_oracle():
     meta_ds, outs_ds = bench.run_step(scfa, w, q, k, v, do, R, exact=True, copy_sorted=False, qk=qk, ds=ds)
     torch.cuda.synchronize()
     assert int(meta_ds["col_base"][-1].item()) <= ds.shape[0]  # every tile stored: dQ came from dS
-    for n in ("row_count", "row_list", "col_count", "col_list"):
-        assert torch.equal(meta_ds[n], meta[n])
+    for cnt, lst in (("row_count", "row_list"), ("col_count", "col_list")):  # entries past a count are unspecified
+        assert torch.equal(meta_ds[cnt], meta[cnt])
+        valid = torch.arange(meta[lst].shape[-1], device=meta[lst].device) < meta[cnt][..., None]
+        assert torch.equal(meta_ds[lst][valid], meta[lst][valid])
     # same forward; dK, dV bit for bit (same kernel, D from the preprocess equals D from the dQ kernel)
     for i in (0, 1, 3, 4):  # O, lse, dK, dV
         assert torch.equal(outs_ds[i], outs[i]), i
     dq_ds = to_np(outs_ds[2])
     got = {n: meta[n].cpu().numpy() for n in ("row_count", "row_list", "col_count", "col_list", "q_hash", "q_idx",
                                               "q_perm", "k_hash", "k_idx", "k_perm")}
-    o, lse, dq, dk, dv = (to_np(t) for t in outs)
+    assert meta["outputs"] == "caller rows"
+    o, lse, dq, dk, dv = (to_np(t) for t in outs)  # caller (token) order
     del q, k, v, do, qk, meta, outs, ds, meta_ds, outs_ds
     rng = np.random.default_rng(16384)
     full_heads = {(0, 0), (w.B - 1, w.H - 1)}
@@ -83,6 +87,9 @@ def test_timed_step_matches_oracle():
                 np.testing.assert_array_equal(got[which + "_idx"][b, h], i_ref)
                 res[which] = (p_ref, h_ref, i_ref)
             (pq, hq, iq), (pk, hk, ik) = res["q"], res["k"]
+            # caller-order outputs seen in the sorted view: view row i is caller row pq[i] (pk for keys)
+            o_v, lse_v, dq_v, dqds_v = o[b, h][pq], lse[b, h][pq], dq[b, h][pq], dq_ds[b, h][pq]
+            dk_v, dv_v = dk[b, h][pk], dv[b, h][pk]
             # exact block lists, bit for bit
             _, _, live, free = Bk.metadata_exact(iq, ik, hq, hk, w.block)
             _check_lists(got, b, h, live, free)
@@ -91,19 +98,19 @@ def test_timed_step_matches_oracle():
             if (b, h) in full_heads:
                 note(f"[timed step] full oracle b{b}h{h}")
                 o_ref, lse_ref = A.forward(qs, ks, vs, iq, ik, hq, hk, w.scale)
-                check_forward(o[b, h], lse[b, h], o_ref, lse_ref, "bf16", f"step b{b}h{h}")
+                check_forward(o_v, lse_v, o_ref, lse_ref, "bf16", f"step b{b}h{h}")
                 ref = A.backward(qs, ks, vs, dos, iq, ik, hq, hk, w.scale)
-                check_grads([dq[b, h], dk[b, h], dv[b, h]], ref, "bf16", f"step b{b}h{h}")
-                check_grads([dq_ds[b, h], dk[b, h], dv[b, h]], ref, "bf16", f"step stored dS b{b}h{h}")
+                check_grads([dq_v, dk_v, dv_v], ref, "bf16", f"step b{b}h{h}")
+                check_grads([dqds_v, dk_v, dv_v], ref, "bf16", f"step stored dS b{b}h{h}")
             else:
                 rows = _rows_sample(rng, w.Tq, 64)
                 o_ref, lse_ref = A.forward_rows(rows, qs, ks, vs, iq, ik, hq, hk, w.scale)
-                check_forward(o[b, h][rows], lse[b, h][rows], o_ref, lse_ref, "bf16", f"step rows b{b}h{h}")
+                check_forward(o_v[rows], lse_v[rows], o_ref, lse_ref, "bf16", f"step rows b{b}h{h}")
                 dq_ref = A.backward_rows(rows, qs, ks, vs, dos, iq, ik, hq, hk, w.scale)
-                assert rel_fro(dq[b, h][rows], dq_ref) <= 5e-2, (b, h)
-                assert rel_fro(dq_ds[b, h][rows], dq_ref) <= 5e-2, (b, h)
+                assert rel_fro(dq_v[rows], dq_ref) <= 5e-2, (b, h)
+                assert rel_fro(dqds_v[rows], dq_ref) <= 5e-2, (b, h)
                 keys = _rows_sample(rng, w.Tk, 32)
                 dk_ref, dv_ref = A.backward_key_rows(keys, qs, ks, vs, dos, iq, ik, hq, hk, w.scale)
-                assert rel_fro(dk[b, h][keys], dk_ref) <= 5e-2, (b, h)
-                assert rel_fro(dv[b, h][keys], dv_ref) <= 5e-2, (b, h)
+                assert rel_fro(dk_v[keys], dk_ref) <= 5e-2, (b, h)
+                assert rel_fro(dv_v[keys], dv_ref) <= 5e-2, (b, h)
             note(f"[timed step] b{b}h{h} ok")
