@@ -462,6 +462,80 @@ def sweep_length(scfa, torch, lengths, args):
         torch.cuda.empty_cache()
 
 
+def sweep_ragged(scfa, torch, args):
+    """QK-sparse training over heads with their own kept counts: packed heads against the padded layout.
+
+    Each of the B*H heads drops its own share of tokens (drop rate drawn per head), so kept counts differ.
+    * packed: the heads back to back with no padding, per-head offsets (block_meta_varlen + the varlen
+      forward, dQ and dK/dV calls);
+    * padded: every head padded to the longest kept count, padding queries at position -1 and padding keys at
+      2^31 - 1 (block_meta + the list forward, dQ and dK/dV calls).
+    Both time metadata + forward + backward with the compacted tensors already resident; the outputs agree
+    bit for bit on the real rows.
+    """
+    import numpy as np
+
+    B, H, T, d, block = 4, 12, 8192, 64, 64
+    for name, lo, hi in (("uniform drop 10-90%", 0.1, 0.9), ("skewed: drop 90% except one head per batch", 0.9, 0.9)):
+        rng = np.random.default_rng(11)
+        rates = rng.uniform(lo, hi, B * H)
+        if lo == hi:
+            rates[::H] = 0.0
+        kept = [max(1, int(round((1.0 - r) * T))) for r in rates]
+        pos = [np.sort(rng.choice(T, n, replace=False)).astype(np.int32) for n in kept]
+        off = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+        total, mx = int(off[-1]), max(kept)
+        q, k, v, do = (_gpu_normal(torch, (total, d), 300 + i) for i in range(4))
+        idx = torch.from_numpy(np.concatenate(pos)).cuda()
+        offs = torch.from_numpy(off).cuda()
+        pq = np.full((B * H, mx), -1, np.int32)
+        pk = np.full((B * H, mx), 2**31 - 1, np.int32)
+        rows = np.full((B * H, mx), -1, np.int64)
+        for i, p in enumerate(pos):
+            pq[i, :len(p)] = p
+            pk[i, :len(p)] = p
+            rows[i, :len(p)] = np.arange(off[i], off[i + 1])
+        pqi, pki = (torch.from_numpy(a.reshape(B, H, mx)).cuda() for a in (pq, pk))
+        sel = torch.from_numpy(rows.reshape(-1)).cuda()
+        have = sel >= 0
+
+        def padded_of(x):
+            y = torch.zeros((B * H * mx, d), dtype=x.dtype, device=x.device)
+            y[have] = x[sel[have]]
+            return y.view(B, H, mx, d)
+
+        Pq, Pk, Pv, Pdo = (padded_of(x) for x in (q, k, v, do))
+        mt = dict(H=H, max_Tq=mx, max_Tk=mx, block=block)
+
+        def packed(_):
+            meta = scfa.block_meta_varlen(offs, offs, idx, idx, **mt)
+            o, lse = scfa.attn_fwd_varlen(q, k, v, offs, offs, idx, idx, None, None, meta, **mt)
+            dq, delta = scfa.attn_bwd_dq_varlen(q, k, v, o, lse, do, offs, offs, idx, idx, None, None, meta, **mt)
+            scfa.attn_bwd_dkdv_varlen(q, k, v, lse, do, delta, offs, offs, idx, idx, None, None, meta, **mt)
+            return o
+
+        def padded(_):
+            meta = scfa.block_meta(pqi, pki, block=block, with_cols=True, exact=True)
+            o, lse = scfa.attn_fwd_lists(Pq, Pk, Pv, pqi, pki, None, None, meta, block=block)
+            dq, delta = scfa.attn_bwd_dq_lists(Pq, Pk, Pv, o, lse, Pdo, pqi, pki, None, None, meta, block=block)
+            scfa.attn_bwd_dkdv_lists(Pq, Pk, Pv, lse, Pdo, delta, pqi, pki, None, None, meta, block=block)
+            return o
+
+        ms_packed, o1 = _time_steps(torch, packed, args.steps, args.warmup)
+        ms_padded, o2 = _time_steps(torch, padded, args.steps, args.warmup)
+        same = bool(torch.equal(o1[sel[have]], o2.reshape(-1, d)[have]))
+        print(json.dumps({"sweep": "ragged_heads", "heads": name, "B": B, "H": H, "T": T, "d": d, "block": block,
+                          "kept_min": min(kept), "kept_max": mx, "rows_packed": total, "rows_padded": B * H * mx,
+                          "packed_ms": round(ms_packed, 4), "padded_ms": round(ms_padded, 4),
+                          "speedup_packed_vs_padded": round(ms_padded / ms_packed, 3),
+                          "qkvdo_bytes_packed": 4 * total * d * 2, "qkvdo_bytes_padded": 4 * B * H * mx * d * 2,
+                          "outputs_equal": same,
+                          "step": "block lists + QK-sparse fwd + dQ + dK/dV (compacted tensors resident)"}),
+              flush=True)
+        del q, k, v, do, Pq, Pk, Pv, Pdo
+        torch.cuda.empty_cache()
+
+
 def measure_rows(scfa, torch, w, q, k, v, do, R, args):
     """HBM throughput of gather_rows / scatter_rows at the step's shape."""
     import numpy as np
@@ -785,6 +859,8 @@ def main():
                     help="comma-separated bucket counts: one JSON line per count instead of the benchmark line")
     ap.add_argument("--sweep-drop", type=str, default="", metavar="LIST", help="comma-separated drop rates")
     ap.add_argument("--sweep-T", type=str, default="", metavar="LIST", help="comma-separated sequence lengths")
+    ap.add_argument("--sweep-ragged", action="store_true",
+                    help="QK-sparse heads with their own kept counts: packed heads against the padded layout")
     ap.add_argument("--measure-rows", action="store_true",
                     help="time the row gather / scatter calls instead of the step (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -802,6 +878,9 @@ def main():
 
     if args.sweep_drop:
         sweep_drop(scfa, torch, [float(x) for x in args.sweep_drop.split(",")], args)
+        return
+    if args.sweep_ragged:
+        sweep_ragged(scfa, torch, args)
         return
     if args.sweep_T:
         sweep_length(scfa, torch, [int(x) for x in args.sweep_T.split(",")], args)

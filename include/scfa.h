@@ -341,6 +341,66 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
                              int dtype, unsigned flags, void *stream);
 
 /*
+ * Packed ragged heads ("varlen").  Dropping tokens per head leaves each head
+ * its own kept count ("SCFA solution > 1. QK-Sparse": compact tensors; the
+ * counts differ per head under dynamic pruning).  These calls take the heads
+ * packed back to back, with no padding:
+ *   q_offsets, k_offsets: [B*H + 1] int32 DEVICE arrays, non-decreasing, with
+ *   offsets[0] = 0: head bh = b*H + h owns packed query rows q_offsets[bh] ..
+ *   q_offsets[bh+1] - 1 (keys: k_offsets), at most max_Tq (max_Tk) of them.
+ *   total_q = q_offsets[B*H], total_k = k_offsets[B*H] (passed so the host can
+ *   check sizes).  Tensors: q, o, dout, dq [total_q, d]; k, v, dk, dv
+ *   [total_k, d]; q_idx, q_hash, lse [total_q]; k_idx, k_hash [total_k];
+ *   delta [2, total_q].  Positions and buckets are per head, as elsewhere.
+ *   Lists keep the fixed-stride layout of scfa_block_meta sized by the maximum
+ *   lengths: row_count [B,H,nq], row_list [B,H,nq,nk] with nq = ceil(max_Tq /
+ *   block), nk = ceil(max_Tk / block); blocks past a head's length have no
+ *   live tiles.  Work follows each head's own length: work groups past it exit
+ *   at once.  Row indirection and the stored-dS backward are not available
+ *   here (SCFA_ERR_UNSUPPORTED).  Offsets that break these rules (descending,
+ *   or beyond the tensors) are not detected on the host; per-head lengths are
+ *   clamped into [0, max_T] on the device.
+ *   The meta call applies the exact tile rule (scfa_block_meta_exact) and takes
+ *   its workspace (scfa_workspace_size(SCFA_OP_BLOCK_META_EXACT, B, H, max_Tq,
+ *   max_Tk, 0, block, 0) bytes; NULL in QK-sparse mode).  Everything else is as
+ *   in the fixed-length list entry points.
+ */
+int scfa_block_meta_varlen(const int32_t *q_offsets, const int32_t *k_offsets, int total_q, int total_k,
+                           const int32_t *q_idx, const int32_t *k_idx,
+                           const int32_t *q_hash, const int32_t *k_hash,
+                           int B, int H, int max_Tq, int max_Tk, int block,
+                           int32_t *q_stats, int32_t *k_stats,
+                           int32_t *row_count, int32_t *row_list,
+                           int32_t *col_count, int32_t *col_list,
+                           void *workspace, size_t workspace_bytes, void *stream);
+int scfa_attn_fwd_varlen(const void *q, const void *k, const void *v,
+                         const int32_t *q_offsets, const int32_t *k_offsets, int total_q, int total_k,
+                         const int32_t *q_idx, const int32_t *k_idx,
+                         const int32_t *q_hash, const int32_t *k_hash,
+                         const int32_t *row_count, const int32_t *row_list,
+                         void *o, float *lse,
+                         int B, int H, int max_Tq, int max_Tk, int d, int block, float scale,
+                         int dtype, unsigned flags, void *stream);
+int scfa_attn_bwd_dq_varlen(const void *q, const void *k, const void *v,
+                            const void *o, const float *lse, const void *dout,
+                            const int32_t *q_offsets, const int32_t *k_offsets, int total_q, int total_k,
+                            const int32_t *q_idx, const int32_t *k_idx,
+                            const int32_t *q_hash, const int32_t *k_hash,
+                            const int32_t *row_count, const int32_t *row_list,
+                            void *dq, float *delta,
+                            int B, int H, int max_Tq, int max_Tk, int d, int block, float scale,
+                            int dtype, unsigned flags, void *stream);
+int scfa_attn_bwd_dkdv_varlen(const void *q, const void *k, const void *v,
+                              const float *lse, const void *dout, const float *delta,
+                              const int32_t *q_offsets, const int32_t *k_offsets, int total_q, int total_k,
+                              const int32_t *q_idx, const int32_t *k_idx,
+                              const int32_t *q_hash, const int32_t *k_hash,
+                              const int32_t *col_count, const int32_t *col_list,
+                              void *dk, void *dv,
+                              int B, int H, int max_Tq, int max_Tk, int d, int block, float scale,
+                              int dtype, unsigned flags, void *stream);
+
+/*
  * Backward with stored dS: the dK/dV kernel keeps every live tile's dS (the
  * bf16 values its dK product uses) and dQ becomes a plain block-sparse
  * product dQ = scale * dS K over the row lists, with no exponent, mask or dP

@@ -44,6 +44,10 @@ __all__ = [
     "attn_fwd_lists",
     "attn_bwd_dq_lists",
     "attn_bwd_dkdv_lists",
+    "block_meta_varlen",
+    "attn_fwd_varlen",
+    "attn_bwd_dq_varlen",
+    "attn_bwd_dkdv_varlen",
     "tile_slots",
     "ds_buffer",
     "attn_bwd_prep",
@@ -336,6 +340,106 @@ def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash,
                                        _ptr(cc_), _ptr(cl_), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, block,
                                        float(scale), _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_bwd_dkdv_lists", rc)
+    return dk, dv
+
+
+def _varlen_check(q_off, k_off, H):
+    _need(q_off, "q_offsets", torch.int32)
+    _need(k_off, "k_offsets", torch.int32, q_off.shape)
+    if q_off.dim() != 1 or (q_off.numel() - 1) % H:
+        raise ValueError("offsets must be [B*H + 1]")
+    return (q_off.numel() - 1) // H
+
+
+def block_meta_varlen(q_off, k_off, q_idx, k_idx, q_hash=None, k_hash=None, *, H, max_Tq, max_Tk, block=64,
+                      with_cols=True):
+    """Exact block lists for packed ragged heads (scfa_block_meta_varlen).
+
+    q_off, k_off: int32 [B*H + 1] offsets of each head's rows in the packed q_idx [total_q] / k_idx
+    [total_k] (and buckets); lists are sized by max_Tq, max_Tk.
+    """
+    B = _varlen_check(q_off, k_off, H)
+    tq, tk = q_idx.numel(), k_idx.numel()
+    _need(q_idx, "q_idx", torch.int32, (tq,))
+    _need(k_idx, "k_idx", torch.int32, (tk,))
+    _need(q_hash, "q_hash", torch.int32, (tq,))
+    _need(k_hash, "k_hash", torch.int32, (tk,))
+    nq, nk = -(-max_Tq // block), -(-max_Tk // block)
+    dev = q_idx.device
+    out = {
+        "q_stats": torch.empty((B, H, nq, 4), dtype=torch.int32, device=dev),
+        "k_stats": torch.empty((B, H, nk, 4), dtype=torch.int32, device=dev),
+        "row_count": torch.empty((B, H, nq), dtype=torch.int32, device=dev),
+        "row_list": torch.empty((B, H, nq, nk), dtype=torch.int32, device=dev),
+        "block": block,
+    }
+    if with_cols:
+        out["col_count"] = torch.empty((B, H, nk), dtype=torch.int32, device=dev)
+        out["col_list"] = torch.empty((B, H, nk, nq), dtype=torch.int32, device=dev)
+    ws, nws = (None, 0)
+    if q_hash is not None:
+        ws, nws = _workspace(_lib.OP_BLOCK_META_EXACT, B, H, max_Tq, max_Tk, 0, block, dev)
+    rc = _LIB.scfa_block_meta_varlen(_ptr(q_off), _ptr(k_off), tq, tk, _ptr(q_idx), _ptr(k_idx), _ptr(q_hash),
+                                     _ptr(k_hash), B, H, max_Tq, max_Tk, block, _ptr(out["q_stats"]),
+                                     _ptr(out["k_stats"]), _ptr(out["row_count"]), _ptr(out["row_list"]),
+                                     _ptr(out.get("col_count")), _ptr(out.get("col_list")), _ptr(ws), nws, _stream())
+    _lib.check("scfa_block_meta_varlen", rc)
+    return out
+
+
+def _varlen_shapes(q, k, v, q_off, k_off, H):
+    B = _varlen_check(q_off, k_off, H)
+    if q.dim() != 2 or k.dim() != 2 or v.shape != k.shape or k.shape[1] != q.shape[1]:
+        raise ValueError("packed q [total_q, d], k and v [total_k, d]")
+    return B, q.shape[0], k.shape[0], q.shape[1]
+
+
+def attn_fwd_varlen(q, k, v, q_off, k_off, q_idx, k_idx, q_hash, k_hash, meta, *, H, max_Tq, max_Tk, block=64,
+                    scale=None, flags=0):
+    """Forward over packed ragged heads (scfa_attn_fwd_varlen); positions None = dense causal per head."""
+    B, tq, tk, d = _varlen_shapes(q, k, v, q_off, k_off, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((tq,), dtype=torch.float32, device=q.device)
+    rc_, rl_ = _list_args(meta, "row_count", "row_list")
+    rc = _LIB.scfa_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(q_off), _ptr(k_off), tq, tk, _ptr(q_idx),
+                                   _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), _ptr(rc_), _ptr(rl_), _ptr(o), _ptr(lse),
+                                   B, H, max_Tq, max_Tk, d, block, float(scale), _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_attn_fwd_varlen", rc)
+    return o, lse
+
+
+def attn_bwd_dq_varlen(q, k, v, o, lse, dout, q_off, k_off, q_idx, k_idx, q_hash, k_hash, meta, *, H, max_Tq,
+                       max_Tk, block=64, scale=None, flags=0):
+    """dQ (and delta [2, total_q]) over packed ragged heads (scfa_attn_bwd_dq_varlen)."""
+    B, tq, tk, d = _varlen_shapes(q, k, v, q_off, k_off, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    delta = torch.empty((2, tq), dtype=torch.float32, device=q.device)
+    rc_, rl_ = _list_args(meta, "row_count", "row_list")
+    rc = _LIB.scfa_attn_bwd_dq_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_off),
+                                      _ptr(k_off), tq, tk, _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
+                                      _ptr(rc_), _ptr(rl_), _ptr(dq), _ptr(delta), B, H, max_Tq, max_Tk, d, block,
+                                      float(scale), _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_attn_bwd_dq_varlen", rc)
+    return dq, delta
+
+
+def attn_bwd_dkdv_varlen(q, k, v, lse, dout, delta, q_off, k_off, q_idx, k_idx, q_hash, k_hash, meta, *, H,
+                         max_Tq, max_Tk, block=64, scale=None, flags=0):
+    """dK, dV over packed ragged heads (scfa_attn_bwd_dkdv_varlen), reading delta from attn_bwd_dq_varlen."""
+    B, tq, tk, d = _varlen_shapes(q, k, v, q_off, k_off, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    cc_, cl_ = _list_args(meta, "col_count", "col_list")
+    rc = _LIB.scfa_attn_bwd_dkdv_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta), _ptr(q_off),
+                                        _ptr(k_off), tq, tk, _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
+                                        _ptr(cc_), _ptr(cl_), _ptr(dk), _ptr(dv), B, H, max_Tq, max_Tk, d, block,
+                                        float(scale), _dtype_code(q), int(flags), _stream())
+    _lib.check("scfa_attn_bwd_dkdv_varlen", rc)
     return dk, dv
 
 

@@ -27,6 +27,10 @@ EXPORTED = (
     "scfa_attn_fwd_lists",
     "scfa_attn_bwd_dq_lists",
     "scfa_attn_bwd_dkdv_lists",
+    "scfa_block_meta_varlen",
+    "scfa_attn_fwd_varlen",
+    "scfa_attn_bwd_dq_varlen",
+    "scfa_attn_bwd_dkdv_varlen",
     "scfa_tile_slots",
     "scfa_attn_bwd_prep",
     "scfa_attn_bwd_dkdv_ds_lists",
@@ -82,6 +86,10 @@ _SIGNATURES = {
     "scfa_attn_fwd_lists": [_p] * 13 + _LISTS_TAIL,
     "scfa_attn_bwd_dq_lists": [_p] * 16 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_lists": [_p] * 16 + _LISTS_TAIL,
+    "scfa_block_meta_varlen": [_p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    "scfa_attn_fwd_varlen": [_p, _p, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p] + _LISTS_TAIL,
+    "scfa_attn_bwd_dq_varlen": [_p] * 8 + [_i, _i] + [_p] * 8 + _LISTS_TAIL,
+    "scfa_attn_bwd_dkdv_varlen": [_p] * 8 + [_i, _i] + [_p] * 8 + _LISTS_TAIL,
     "scfa_tile_slots": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p],
     "scfa_attn_bwd_prep": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _u, _p],
     "scfa_attn_bwd_dkdv_ds_lists": [_p] * 16 + [_i64] + [_p, _p] + _LISTS_TAIL,

@@ -116,6 +116,10 @@ struct AttnCall {
   void *ds;
   long long ds_tiles;
   const int32_t *row_slot, *col_base;
+  // packed ragged heads (varlen entry points): offsets [BH+1] and packed row counts; Shape's Tq, Tk
+  // are then the maximum head lengths
+  const int32_t *q_off, *k_off;
+  long long total_q, total_k;
   Shape s;
   unsigned flags;
   void *ws;
@@ -131,8 +135,18 @@ int attention(const AttnCall &c) {
   const unsigned known = SCFA_FLAG_NO_PRUNE | SCFA_FLAG_FORCE_MASK | (c.api == kApiLists ? SCFA_FLAG_ORIG_ROWS : 0u);
   if (c.flags & ~known) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", c.flags);
   const long long BH = (long long)s.B * s.H;
-  const long long nQ = BH * s.Tq * s.d, nK = BH * s.Tk * s.d;
-  const long long nQi = BH * s.Tq, nKi = BH * s.Tk;
+  const bool varlen = c.q_off != nullptr || c.k_off != nullptr;
+  if (varlen) {
+    if (c.q_off == nullptr || c.k_off == nullptr)
+      return fail(SCFA_ERR_INVALID_ARGUMENT, "q_offsets and k_offsets must both be set");
+    if (!aligned(c.q_off, 4) || !aligned(c.k_off, 4)) return fail(SCFA_ERR_INVALID_ARGUMENT, "offsets not 4-byte aligned");
+    if (c.total_q < 0 || c.total_k < 0 || c.total_q * s.d >= (1ll << 31) || c.total_k * s.d >= (1ll << 31))
+      return fail(SCFA_ERR_INVALID_ARGUMENT, "packed row counts must be >= 0 and rows*d < 2^31");
+    if (c.q_rows || c.k_rows || c.ds_path) return fail(SCFA_ERR_UNSUPPORTED, "ragged heads: no row indirection or stored dS");
+  }
+  const long long rowsQ = varlen ? c.total_q : BH * s.Tq, rowsK = varlen ? c.total_k : BH * s.Tk;
+  const long long nQ = rowsQ * s.d, nK = rowsK * s.d;
+  const long long nQi = rowsQ, nKi = rowsK;
   const int nq = nblocks(s.Tq, s.block), nk = nblocks(s.Tk, s.block);
   if ((rc = check_ptr(c.q, nQ, 16, "q")) || (rc = check_ptr(c.k, nK, 16, "k")) || (rc = check_ptr(c.v, nK, 16, "v")))
     return rc;
@@ -241,6 +255,9 @@ int attention(const AttnCall &c) {
   a.no_prune = no_prune ? 1 : 0;
   a.force_mask = (c.flags & SCFA_FLAG_FORCE_MASK) ? 1 : 0;
   a.orig_rows = orig_rows ? 1 : 0;
+  a.q_off = c.q_off;
+  a.k_off = c.k_off;
+  a.delta_half = rowsQ;
   a.ds = c.ds;
   a.ds_tiles = c.ds_tiles;
   a.row_slot = c.row_slot;
@@ -317,7 +334,9 @@ size_t lsh_ws(int B, int H, int T, int d, int nb) {
 
 int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, int B, int H,
               int Tq, int Tk, int block, int32_t *q_stats, int32_t *k_stats, bool exact, int32_t *row_count,
-              int32_t *row_list, int32_t *col_count, int32_t *col_list, void *ws, size_t ws_bytes, void *stream) {
+              int32_t *row_list, int32_t *col_count, int32_t *col_list, void *ws, size_t ws_bytes, void *stream,
+              const int32_t *q_off = nullptr, const int32_t *k_off = nullptr, long long total_q = 0,
+              long long total_k = 0) {
   if (B < 1 || H < 1 || Tq < 0 || Tk < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tk >= 0 required");
   if (block != 64 && block != 128) return fail(SCFA_ERR_UNSUPPORTED, "block=%d unsupported (64 or 128)", block);
   if ((q_hash == nullptr) != (k_hash == nullptr))
@@ -328,10 +347,15 @@ int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
   const long long nq = nblocks(Tq, block), nk = nblocks(Tk, block);
   if (BH * nq * nk >= (1ll << 31) || BH * (Tq > Tk ? Tq : Tk) >= (1ll << 31))
     return fail(SCFA_ERR_INVALID_ARGUMENT, "metadata too large");
+  const bool varlen = q_off != nullptr || k_off != nullptr;
+  if (varlen && (q_off == nullptr || k_off == nullptr || total_q < 0 || total_k < 0 || !aligned(q_off, 4) ||
+                 !aligned(k_off, 4)))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "ragged heads need both 4-byte aligned offsets and packed row counts >= 0");
+  const long long rowsQ = varlen ? total_q : BH * Tq, rowsK = varlen ? total_k : BH * Tk;
   int rc;
-  if ((rc = check_ptr(q_idx, BH * Tq, 4, "q_idx")) || (rc = check_ptr(k_idx, BH * Tk, 4, "k_idx")) ||
-      (rc = check_ptr(q_hash, q_hash ? BH * Tq : 0, 4, "q_hash")) ||
-      (rc = check_ptr(k_hash, k_hash ? BH * Tk : 0, 4, "k_hash")) ||
+  if ((rc = check_ptr(q_idx, rowsQ, 4, "q_idx")) || (rc = check_ptr(k_idx, rowsK, 4, "k_idx")) ||
+      (rc = check_ptr(q_hash, q_hash ? rowsQ : 0, 4, "q_hash")) ||
+      (rc = check_ptr(k_hash, k_hash ? rowsK : 0, 4, "k_hash")) ||
       (rc = check_ptr(q_stats, BH * nq * 4, 16, "q_stats")) || (rc = check_ptr(k_stats, BH * nk * 4, 16, "k_stats")) ||
       (rc = check_ptr(row_count, BH * nq, 4, "row_count")) || (rc = check_ptr(row_list, BH * nq * nk, 4, "row_list")))
     return rc;
@@ -345,6 +369,8 @@ int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
   m.k_idx = k_idx;
   m.q_hash = q_hash;
   m.k_hash = k_hash;
+  m.q_off = q_off;
+  m.k_off = k_off;
   m.q_stats = q_stats;
   m.k_stats = k_stats;
   if (use_segs) {
@@ -506,6 +532,76 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v, const 
   return attention(c);
 }
 
+int scfa_block_meta_varlen(const int32_t *q_offsets, const int32_t *k_offsets, int total_q, int total_k,
+                           const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash,
+                           int B, int H, int max_Tq, int max_Tk, int block, int32_t *q_stats, int32_t *k_stats,
+                           int32_t *row_count, int32_t *row_list, int32_t *col_count, int32_t *col_list,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (q_offsets == nullptr || k_offsets == nullptr)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_offsets and k_offsets are required");
+  return meta_call(q_idx, k_idx, q_hash, k_hash, B, H, max_Tq, max_Tk, block, q_stats, k_stats, true, row_count,
+                   row_list, col_count, col_list, workspace, workspace_bytes, stream, q_offsets, k_offsets, total_q,
+                   total_k);
+}
+
+int scfa_attn_fwd_varlen(const void *q, const void *k, const void *v, const int32_t *q_offsets,
+                         const int32_t *k_offsets, int total_q, int total_k, const int32_t *q_idx,
+                         const int32_t *k_idx, const int32_t *q_hash, const int32_t *k_hash, const int32_t *row_count,
+                         const int32_t *row_list, void *o, float *lse, int B, int H, int max_Tq, int max_Tk, int d,
+                         int block, float scale, int dtype, unsigned flags, void *stream) {
+  if (q_offsets == nullptr || k_offsets == nullptr)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_offsets and k_offsets are required");
+  AttnCall c{};
+  c.kind = kFwd;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.row_cnt = row_count, c.row_list = row_list, c.out_o = o, c.out_lse = lse;
+  c.q_off = q_offsets, c.k_off = k_offsets, c.total_q = total_q, c.total_k = total_k;
+  c.s = Shape{B, H, max_Tq, max_Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_attn_bwd_dq_varlen(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                            const void *dout, const int32_t *q_offsets, const int32_t *k_offsets, int total_q,
+                            int total_k, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                            const int32_t *k_hash, const int32_t *row_count, const int32_t *row_list, void *dq,
+                            float *delta, int B, int H, int max_Tq, int max_Tk, int d, int block, float scale,
+                            int dtype, unsigned flags, void *stream) {
+  if (q_offsets == nullptr || k_offsets == nullptr)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_offsets and k_offsets are required");
+  AttnCall c{};
+  c.kind = kBwdDq;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.row_cnt = row_count, c.row_list = row_list, c.dq = dq, c.delta = delta;
+  c.q_off = q_offsets, c.k_off = k_offsets, c.total_q = total_q, c.total_k = total_k;
+  c.s = Shape{B, H, max_Tq, max_Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
+int scfa_attn_bwd_dkdv_varlen(const void *q, const void *k, const void *v, const float *lse, const void *dout,
+                              const float *delta, const int32_t *q_offsets, const int32_t *k_offsets, int total_q,
+                              int total_k, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
+                              const int32_t *k_hash, const int32_t *col_count, const int32_t *col_list, void *dk,
+                              void *dv, int B, int H, int max_Tq, int max_Tk, int d, int block, float scale,
+                              int dtype, unsigned flags, void *stream) {
+  if (q_offsets == nullptr || k_offsets == nullptr)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "q_offsets and k_offsets are required");
+  AttnCall c{};
+  c.kind = kBwdDkdv;
+  c.api = kApiLists;
+  c.q = q, c.k = k, c.v = v, c.lse = lse, c.dout = dout, c.delta = const_cast<float *>(delta);
+  c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
+  c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
+  c.q_off = q_offsets, c.k_off = k_offsets, c.total_q = total_q, c.total_k = total_k;
+  c.s = Shape{B, H, max_Tq, max_Tk, d, block, dtype, scale};
+  c.flags = flags, c.stream = stream;
+  return attention(c);
+}
+
 int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list, const int32_t *col_count,
                     const int32_t *col_list, int B, int H, int Tq, int Tk, int block, int32_t *col_base,
                     int32_t *row_slot, void *stream) {
@@ -549,6 +645,7 @@ int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const 
   a.BH = (int)BH;
   a.Tq = Tq;
   a.d = d;
+  a.delta_half = BH * Tq;
   a.orig_rows = (flags & SCFA_FLAG_ORIG_ROWS) ? 1 : 0;
   const hipError_t e = scfa::launch_attn_bwd_prep(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward preprocess");

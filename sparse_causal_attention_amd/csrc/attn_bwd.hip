@@ -162,6 +162,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.nq;
   const int qb = wg % a.nq;
+  if (varlen_head(a, bh, 2) && qb * BS >= a.Tq) return;  // past this ragged head's queries
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qb * BS + 32 * w + col;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const float lse2 = qvalid ? lse_raw * kLog2e : INFINITY;
   if (qvalid && half == 0) {
     a.delta[qoff + qrow] = dsum;
-    a.delta[(size_t)a.BH * a.Tq + qoff + qrow] = lse2;
+    a.delta[a.delta_half + qoff + qrow] = lse2;
   }
   const float c = a.scale * kLog2e;
   f32x16 dqa[D / 32];
@@ -361,6 +362,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.nk;
   const int kb = wg % a.nk;
+  if (varlen_head(a, bh, 2) && kb * BS >= a.Tk) return;  // past this ragged head's keys
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int krow = kb * BS + 32 * w + col;
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + qoff * D;
   const uint16_t *K = static_cast<const uint16_t *>(a.k) + koff * D;
   const uint16_t *V = static_cast<const uint16_t *>(a.v) + koff * D;
-  const float *lse2g = a.delta + (size_t)a.BH * a.Tq + qoff;
+  const float *lse2g = a.delta + a.delta_half + qoff;
   const float *delg = a.delta + qoff;
 
   // Loads that depend only on this lane's own row go first: issued after the
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(AttnArgs a) {
   const float other = __shfl_xor(dsum, 1, 64);
   if (valid && half == 0) {
     a.delta[row] = dsum + other;
-    a.delta[(size_t)a.BH * a.Tq + row] = lse * kLog2e;
+    a.delta[a.delta_half + row] = lse * kLog2e;
   }
 }
 
@@ -792,6 +794,7 @@ __global__ __launch_bounds__(BS) void k_bwd_dq_f32(AttnArgs a) {
   __shared__ int sKhash[kF32Chunk];
   const int bh = blockIdx.x / a.nq;
   const int qb = blockIdx.x % a.nq;
+  if (varlen_head(a, bh, 4) && qb * BS >= a.Tq) return;  // past this ragged head's queries
   const int qrow = qb * BS + threadIdx.x;
   const bool qvalid = qrow < a.Tq;
   const size_t qoff = (size_t)bh * a.Tq;
@@ -869,6 +872,7 @@ __global__ __launch_bounds__(BS) void k_bwd_dkdv_f32(AttnArgs a) {
   __shared__ int sQhash[kF32Chunk];
   const int bh = blockIdx.x / a.nk;
   const int kb = blockIdx.x % a.nk;
+  if (varlen_head(a, bh, 4) && kb * BS >= a.Tk) return;  // past this ragged head's keys
   const int krow = kb * BS + threadIdx.x;
   const bool kvalid_row = krow < a.Tk;
   const size_t koff = (size_t)bh * a.Tk;

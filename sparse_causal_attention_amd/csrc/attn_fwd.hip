@@ -147,6 +147,7 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.nq;
   const int qb = wg % a.nq;
+  if (varlen_head(a, bh, 2) && qb * BS >= a.Tq) return;  // past this ragged head's queries
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qw = w % QW, kh = w / QW;
   const int col = lane & 31, half = lane >> 5;
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(BS) void k_fwd_f32(AttnArgs a) {
   __shared__ int sKhash[kF32Chunk];
   const int bh = blockIdx.x / a.nq;
   const int qb = blockIdx.x % a.nq;
+  if (varlen_head(a, bh, 4) && qb * BS >= a.Tq) return;  // past this ragged head's queries
   const int qrow = qb * BS + threadIdx.x;
   const bool qvalid = qrow < a.Tq;
   const float *Q = static_cast<const float *>(a.q) + (size_t)bh * a.Tq * D;

@@ -42,9 +42,16 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
   const int b = blockIdx.x % nblk;
   const bool isq = b < a.nq;
   const int blk = isq ? b : b - a.nq;
-  const int T = isq ? a.Tq : a.Tk;
-  const int32_t *idx = (isq ? a.q_idx : a.k_idx) + (size_t)bh * T;
+  int T = isq ? a.Tq : a.Tk;
+  size_t base = (size_t)bh * T;
+  const int32_t *off = isq ? a.q_off : a.k_off;
+  if (off) {  // packed ragged heads: this head's rows and length (blocks past it stay empty)
+    base = (size_t)off[bh];
+    T = (int)min(max((long long)off[bh + 1] - off[bh], 0ll), (long long)T);
+  }
+  const int32_t *idx = (isq ? a.q_idx : a.k_idx) + base;
   const int32_t *hs = isq ? a.q_hash : a.k_hash;
+  if (hs) hs += base;
   const int r0 = blk * a.block;
   const int r1 = min(r0 + a.block, T);
   int mn = INT32_MAX, mx = INT32_MIN, hmn = INT32_MAX, hmx = INT32_MIN;
@@ -53,7 +60,7 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
     mn = min(mn, v);
     mx = max(mx, v);
     if (hs) {
-      const int h = hs[(size_t)bh * T + r];
+      const int h = hs[r];
       hmn = min(hmn, h);
       hmx = max(hmx, h);
     }
@@ -78,8 +85,8 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
   const int lane = threadIdx.x;
   bool rem0 = r0 + lane < r1, rem1 = r0 + 64 + lane < r1;
   int h0 = 0, i0 = 0, h1 = 0, i1 = 0;
-  if (rem0) h0 = hs[(size_t)bh * T + r0 + lane], i0 = idx[r0 + lane];
-  if (rem1) h1 = hs[(size_t)bh * T + r0 + 64 + lane], i1 = idx[r0 + 64 + lane];
+  if (rem0) h0 = hs[r0 + lane], i0 = idx[r0 + lane];
+  if (rem1) h1 = hs[r0 + 64 + lane], i1 = idx[r0 + 64 + lane];
   const int nblk_side = isq ? a.nq : a.nk;
   int4 *out = reinterpret_cast<int4 *>(segs) + ((size_t)bh * nblk_side + blk) * a.block;
   int nseg = 0;

@@ -46,7 +46,49 @@ struct AttnArgs {
   // inputs are indexed by the caller's rows (q_rows[i], k_rows[j]) instead of the
   // view's rows i, j; delta stays indexed by the view.
   int orig_rows;
+  // Packed ragged heads: head bh's query rows are q_off[bh] .. q_off[bh+1]-1 of
+  // the packed tensors (k_off for keys), at most Tq (Tk) of them; NULL = every
+  // head has Tq (Tk) rows at bh*Tq.  delta_half is the offset of delta's second
+  // half (lse * log2 e): BH*Tq, or the packed query row count.
+  const int32_t *q_off, *k_off;
+  long long delta_half;
 };
+
+// Packed ragged heads: rebase every per-head pointer of head bh so that the
+// kernels' usual addressing (row bh*Tq + i) lands on packed row q_off[bh] + i,
+// and set Tq, Tk to this head's lengths (clamped into [0, max]).  esize is the
+// element size of the [rows, d] tensors.  Returns whether the head is ragged.
+__device__ __forceinline__ bool varlen_head(AttnArgs &a, int bh, int esize) {
+  if (a.q_off == nullptr) return false;
+  const long long q0 = a.q_off[bh], k0 = a.k_off[bh];
+  const int Tq = (int)min(max((long long)a.q_off[bh + 1] - q0, 0ll), (long long)a.Tq);
+  const int Tk = (int)min(max((long long)a.k_off[bh + 1] - k0, 0ll), (long long)a.Tk);
+  const long long sq = q0 - (long long)bh * Tq, sk = k0 - (long long)bh * Tk;  // row shifts
+  const long long bq = sq * a.d * esize, bk = sk * a.d * esize;                   // byte shifts of [rows, d]
+  auto mv = [](const void *p, long long bytes) { return p ? static_cast<const char *>(p) + bytes : nullptr; };
+  auto mvw = [](void *p, long long bytes) { return p ? static_cast<char *>(p) + bytes : nullptr; };
+  a.q = mv(a.q, bq);
+  a.o = mv(a.o, bq);
+  a.dout = mv(a.dout, bq);
+  a.out_o = mvw(a.out_o, bq);
+  a.dq = mvw(a.dq, bq);
+  a.k = mv(a.k, bk);
+  a.v = mv(a.v, bk);
+  a.dk = mvw(a.dk, bk);
+  a.dv = mvw(a.dv, bk);
+  if (a.lse) a.lse += sq;
+  if (a.out_lse) a.out_lse += sq;
+  if (a.delta) a.delta += sq;
+  if (a.q_idx) a.q_idx += sq;
+  if (a.q_hash) a.q_hash += sq;
+  if (a.q_rows) a.q_rows += sq;
+  if (a.k_idx) a.k_idx += sk;
+  if (a.k_hash) a.k_hash += sk;
+  if (a.k_rows) a.k_rows += sk;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  return true;
+}
 
 // Caller row of view query row i (view key row j): through the permutation when
 // outputs go to the caller's rows, clamped into the head.
@@ -72,6 +114,7 @@ struct RowArgs {
 // records is in the block's count entry.
 struct MetaArgs {
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
+  const int32_t *q_off, *k_off;  // packed ragged heads (NULL = fixed Tq, Tk per head), as in AttnArgs
   int32_t *q_stats, *k_stats;  // [BH, nq, 4], [BH, nk, 4]
   int32_t *q_segs, *k_segs;    // [BH, nq, block, 4], [BH, nk, block, 4]; NULL = range rule only
   int32_t *q_nseg, *k_nseg;    // [BH, nq], [BH, nk] record counts (with the segments)

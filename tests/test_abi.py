@@ -225,6 +225,21 @@ def test_orig_rows_flag_validation():
                                   P, 1 << 30, None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_varlen_validation():
+    lib = _lib.load()
+
+    def fwd(qo=P2, ko=P2, tq=1000, tk=900, q_rows_fn=None, d=64):
+        return lib.scfa_attn_fwd_varlen(P, P, P, qo, ko, tq, tk, P2, P2, None, None, P2, P2, P, P2, 2, 3, 300, 300,
+                                        d, 64, 0.125, 0, 0, None)
+
+    assert fwd(qo=None) == _lib.ERR_INVALID_ARGUMENT
+    assert fwd(ko=P2 + 2) == _lib.ERR_INVALID_ARGUMENT  # alignment
+    assert fwd(tq=-1) == _lib.ERR_INVALID_ARGUMENT
+    assert fwd(d=80) == _lib.ERR_UNSUPPORTED
+    assert lib.scfa_block_meta_varlen(None, P2, 10, 10, P2, P2, None, None, 1, 1, 64, 64, 64, P, P, P2, P2, None, None,
+                                      None, 0, None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_LIB", None)
