@@ -487,8 +487,10 @@ int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v,
  *     SCFA_FLAG_ZERO_FILL zeroes dst first (un-compaction: dropped rows 0).
  *     Un-sorting: index = perm, T_dst = T_src; un-compaction: index = q_idx.
  *   dtype as above (bf16 or fp32); d >= 1 with d * sizeof(dtype) a multiple
- *   of 16 bytes; src/dst 16-byte aligned, index 4-byte aligned; src and dst
- *   must not overlap.  Device pointers owned by the caller; no workspace.
+ *   of 16 bytes and at most 4096 bytes; B*H <= 65535; src/dst 16-byte
+ *   aligned, index 4-byte aligned; src and dst must not overlap (other
+ *   shapes: SCFA_ERR_UNSUPPORTED or SCFA_ERR_INVALID_ARGUMENT).  Device
+ *   pointers owned by the caller; no workspace.
  */
 int scfa_gather_rows(const void *src, const int32_t *index, void *dst,
                      int B, int H, int T_src, int T_dst, int d, int dtype, void *stream);

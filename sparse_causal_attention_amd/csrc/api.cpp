@@ -402,6 +402,8 @@ int rows_call(bool gather, const void *src, const int32_t *index, void *dst, int
   if (dtype != SCFA_DTYPE_BF16 && dtype != SCFA_DTYPE_FP32) return fail(SCFA_ERR_UNSUPPORTED, "dtype=%d unsupported", dtype);
   const int esize = dtype == SCFA_DTYPE_BF16 ? 2 : 4;
   if ((d * esize) % 16 != 0) return fail(SCFA_ERR_UNSUPPORTED, "row of %d bytes is not a multiple of 16", d * esize);
+  if (d * esize > 4096) return fail(SCFA_ERR_UNSUPPORTED, "row of %d bytes exceeds 4096", d * esize);
+  if ((long long)B * H > 65535) return fail(SCFA_ERR_UNSUPPORTED, "B*H = %lld exceeds 65535", (long long)B * H);
   if (flags & ~(gather ? 0u : SCFA_FLAG_ZERO_FILL)) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
   const long long BH = (long long)B * H;
   const long long T = Ts > Td ? Ts : Td;

@@ -271,4 +271,6 @@ def test_row_gather_scatter_validation():
     assert g(dst=P + 1024) == _lib.ERR_INVALID_ARGUMENT  # overlaps src
     assert s(flags=1) == _lib.ERR_INVALID_ARGUMENT  # not a scatter flag
     assert s(flags=_lib.FLAG_ZERO_FILL, dst=None) == _lib.ERR_INVALID_ARGUMENT
+    assert g(d=4096) == _lib.ERR_UNSUPPORTED  # 8 KiB rows: more than 256 pieces per row
+    assert s(B=256, H=256) == _lib.ERR_UNSUPPORTED  # B*H beyond the grid's second dimension
     assert lib.scfa_last_error().decode()
