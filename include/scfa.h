@@ -358,8 +358,10 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
  *   live tiles.  Work follows each head's own length: work groups past it exit
  *   at once.  Row indirection and the stored-dS backward are not available
  *   here (SCFA_ERR_UNSUPPORTED).  Offsets that break these rules (descending,
- *   or beyond the tensors) are not detected on the host; per-head lengths are
- *   clamped into [0, max_T] on the device.
+ *   or beyond the tensors) are not detected on the host (they live on the
+ *   device); the device clamps each head's first row into [0, total] and its
+ *   length into [0, min(max_T, total - first row)], so malformed offsets give
+ *   wrong results but no access leaves the packed tensors.
  *   The meta call applies the exact tile rule (scfa_block_meta_exact) and takes
  *   its workspace (scfa_workspace_size(SCFA_OP_BLOCK_META_EXACT, B, H, max_Tq,
  *   max_Tk, 0, block, 0) bytes; NULL in QK-sparse mode).  Everything else is as

@@ -257,6 +257,8 @@ int attention(const AttnCall &c) {
   a.orig_rows = orig_rows ? 1 : 0;
   a.q_off = c.q_off;
   a.k_off = c.k_off;
+  a.q_total = c.total_q;
+  a.k_total = c.total_k;
   a.delta_half = rowsQ;
   a.ds = c.ds;
   a.ds_tiles = c.ds_tiles;
@@ -371,6 +373,8 @@ int meta_call(const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
   m.k_hash = k_hash;
   m.q_off = q_off;
   m.k_off = k_off;
+  m.q_total = total_q;
+  m.k_total = total_k;
   m.q_stats = q_stats;
   m.k_stats = k_stats;
   if (use_segs) {

@@ -45,9 +45,11 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
   int T = isq ? a.Tq : a.Tk;
   size_t base = (size_t)bh * T;
   const int32_t *off = isq ? a.q_off : a.k_off;
-  if (off) {  // packed ragged heads: this head's rows and length (blocks past it stay empty)
-    base = (size_t)off[bh];
-    T = (int)min(max((long long)off[bh + 1] - off[bh], 0ll), (long long)T);
+  if (off) {  // packed ragged heads: this head's rows and length (blocks past it stay empty), clamped
+    const long long tot = isq ? a.q_total : a.k_total;  // into the packed rows as in varlen_head
+    const long long b0 = min(max((long long)off[bh], 0ll), tot);
+    base = (size_t)b0;
+    T = (int)min(max((long long)off[bh + 1] - b0, 0ll), min((long long)T, tot - b0));
   }
   const int32_t *idx = (isq ? a.q_idx : a.k_idx) + base;
   const int32_t *hs = isq ? a.q_hash : a.k_hash;

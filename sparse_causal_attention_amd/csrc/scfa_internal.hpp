@@ -52,6 +52,7 @@ struct AttnArgs {
   // half (lse * log2 e): BH*Tq, or the packed query row count.
   const int32_t *q_off, *k_off;
   long long delta_half;
+  long long q_total, k_total;  // packed rows of the ragged-head tensors (bounds for the offsets)
 };
 
 // Packed ragged heads: rebase every per-head pointer of head bh so that the
@@ -60,9 +61,12 @@ struct AttnArgs {
 // element size of the [rows, d] tensors.  Returns whether the head is ragged.
 __device__ __forceinline__ bool varlen_head(AttnArgs &a, int bh, int esize) {
   if (a.q_off == nullptr) return false;
-  const long long q0 = a.q_off[bh], k0 = a.k_off[bh];
-  const int Tq = (int)min(max((long long)a.q_off[bh + 1] - q0, 0ll), (long long)a.Tq);
-  const int Tk = (int)min(max((long long)a.k_off[bh + 1] - k0, 0ll), (long long)a.Tk);
+  // first row clamped into [0, total], length into [0, min(max, total - first)]: malformed offsets
+  // give wrong results, but every access stays inside the packed tensors
+  const long long q0 = min(max((long long)a.q_off[bh], 0ll), a.q_total);
+  const long long k0 = min(max((long long)a.k_off[bh], 0ll), a.k_total);
+  const int Tq = (int)min(max((long long)a.q_off[bh + 1] - q0, 0ll), min((long long)a.Tq, a.q_total - q0));
+  const int Tk = (int)min(max((long long)a.k_off[bh + 1] - k0, 0ll), min((long long)a.Tk, a.k_total - k0));
   const long long sq = q0 - (long long)bh * Tq, sk = k0 - (long long)bh * Tk;  // row shifts
   const long long bq = sq * a.d * esize, bk = sk * a.d * esize;                   // byte shifts of [rows, d]
   auto mv = [](const void *p, long long bytes) { return p ? static_cast<const char *>(p) + bytes : nullptr; };
@@ -115,6 +119,7 @@ struct RowArgs {
 struct MetaArgs {
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
   const int32_t *q_off, *k_off;  // packed ragged heads (NULL = fixed Tq, Tk per head), as in AttnArgs
+  long long q_total, k_total;    // their packed row counts
   int32_t *q_stats, *k_stats;  // [BH, nq, 4], [BH, nk, 4]
   int32_t *q_segs, *k_segs;    // [BH, nq, block, 4], [BH, nk, block, 4]; NULL = range rule only
   int32_t *q_nseg, *k_nseg;    // [BH, nq], [BH, nk] record counts (with the segments)
