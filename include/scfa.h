@@ -419,7 +419,9 @@ int scfa_attn_bwd_dkdv_varlen(const void *q, const void *k, const void *v,
  *   The tiles needed are col_base[B*H*nk] (the live-tile count, on the
  *   device).  If that exceeds ds_tiles nothing is stored and dQ falls back to
  *   recomputing S, P and dP (the scfa_attn_bwd_dq_lists kernel): results stay
- *   correct, only slower.
+ *   correct, only slower.  col_base and row_slot must be scfa_tile_slots'
+ *   output for the same lists; with other values the gradients are wrong, but
+ *   no tile is written or read outside [0, ds_tiles).
  */
 
 /* Slot numbering of the live tiles.  Key block c = (b*H + h)*nk + j owns

@@ -549,8 +549,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
         if constexpr (STORE) {
           // Tile layout: 16-query groups [BS/16][BS keys][16 queries]; this (ch, sub, t2) is group
           // 4 ch + 2 sub + t2, and one wave's store covers 32 keys x 32 bytes, contiguous.
-          if (store) {
-            const size_t off = (size_t)(slot0 + cur.t) * BS * BS + (size_t)(4 * cur.ch + 2 * sub) * BS * 16;
+          // (a slot outside the buffer, from inconsistent caller slots, is not stored)
+          const long long slot = (long long)slot0 + cur.t;
+          if (store && slot >= 0 && slot < a.ds_tiles) {
+            const size_t off = (size_t)slot * BS * BS + (size_t)(4 * cur.ch + 2 * sub) * BS * 16;
             if (sub == 0) {
               *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.ds) + off + (size_t)t2 * BS * 16 + lane_ds) = dsw;
             } else {
