@@ -250,7 +250,7 @@ def test_exact_lists_are_bit_identical(dtype):
 
 @pytest.mark.parametrize("mode,d,block,Tq,Tk", [("hash", 64, 64, 1500, 1400), ("qk", 64, 64, 777, 1000),
                                                 ("dense", 64, 64, 650, 650), ("hash", 128, 128, 1300, 1300),
-                                                ("hash", 128, 64, 500, 450)])
+                                                ("hash", 128, 64, 500, 450), ("hash", 64, 128, 1300, 1250)])
 def test_row_indirection_bit_identical(mode, d, block, Tq, Tk):
     """Attention over a permuted view (q_rows / k_rows) equals attention over the gathered copies bit
     for bit, for the forward and both backward kernels; indices out of range behave as clamped."""
