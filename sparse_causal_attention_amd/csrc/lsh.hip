@@ -22,6 +22,7 @@
 
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
+#include "scfa_pipe.hpp"
 
 namespace scfa {
 
@@ -353,7 +354,7 @@ __device__ __forceinline__ void top2_merge_pair(Top2 &t) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint4 *Rf, const float *colnorm,
+__global__ __launch_bounds__(kHashThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_lsh_mfma(LshArgs a, const uint4 *Rf, const float *colnorm,
                                                            int32_t *hist, int nchunks) {
   constexpr int KK = D / 16;
   constexpr int NF = 3 * KK * 64;  // uint4 fragments of one 32-column tile of R
@@ -380,9 +381,11 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint
     for (int kk = 0; kk < KK; ++kk)
       xf[n][kk] = as_bf16x8(tv ? ld16(X + (size_t)tok[n] * D + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0));
   }
+  // R tiles go straight from global memory to LDS (no registers held for them);
+  // each wave copies 64 consecutive fragments per piece, lane l to slot 64 w + l.
   const uint4 *Rh = Rf + (size_t)h * nct * NF;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) rt[0][tid + kHashThreads * i] = Rh[tid + kHashThreads * i];
+  for (int i = 0; i < NP; ++i) lds_copy16(Rh + tid + kHashThreads * i, &rt[0][64 * w + kHashThreads * i]);
   if (hist)
     for (int i = tid; i < a.nb; i += kHashThreads) sh[i] = 0;
   float rm = 0.f;
@@ -406,6 +409,7 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint
     }
     xn[n] = sqrtf(pair_sum(ss)) * 1.0001f;  // rounded up past the float32 sum and sqrt
   }
+  wait_vmem();  // the first R tile has landed in LDS
   __syncthreads();
 
   Top2 t2[2];
@@ -414,11 +418,11 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint
   for (int ct = 0; ct < nct; ++ct) {
     const int cb = ct & 1;
     const bool more = ct + 1 < nct;  // wave-uniform
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 pf[NP];  // next tile (the current one again on the last: always in range, never stored)
-    const u32x4 *nsrc = reinterpret_cast<const u32x4 *>(Rh) + (size_t)(more ? ct + 1 : ct) * NF;
+    if (more) {  // the next tile into the other buffer, while this one is multiplied
+      const uint4 *nsrc = Rh + (size_t)(ct + 1) * NF;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) pf[i] = nsrc[tid + kHashThreads * i];
+      for (int i = 0; i < NP; ++i) lds_copy16(nsrc + tid + kHashThreads * i, &rt[cb ^ 1][64 * w + kHashThreads * i]);
+    }
     f32x16 acc0 = kZero16, acc1 = kZero16;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -443,9 +447,7 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_mfma(LshArgs a, const uint
         top2_add(t2[1], acc1[r], c < half ? fabsf(acc1[r]) : -INFINITY, c);
       }
     }
-    if (more)
-#pragma unroll
-      for (int i = 0; i < NP; ++i) rt[cb ^ 1][tid + kHashThreads * i] = __builtin_bit_cast(uint4, pf[i]);
+    if (more) wait_vmem();  // the next tile has landed before any wave reads it
     __syncthreads();
   }
 

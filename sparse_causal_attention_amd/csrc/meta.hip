@@ -56,26 +56,27 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
   if (hs) hs += base;
   const int r0 = blk * a.block;
   const int r1 = min(r0 + a.block, T);
-  int mn = INT32_MAX, mx = INT32_MIN, hmn = INT32_MAX, hmx = INT32_MIN;
-  for (int r = r0 + (int)threadIdx.x; r < r1; r += 64) {
-    const int v = idx[r];
-    mn = min(mn, v);
-    mx = max(mx, v);
-    if (hs) {
-      const int h = hs[r];
-      hmn = min(hmn, h);
-      hmx = max(hmx, h);
-    }
+  // A block holds at most 128 rows: two per lane, loaded once for both the
+  // statistics and the bucket records.
+  const int lane = threadIdx.x;
+  bool rem0 = r0 + lane < r1, rem1 = r0 + 64 + lane < r1;
+  int h0 = 0, i0 = 0, h1 = 0, i1 = 0;
+  if (rem0) {
+    i0 = idx[r0 + lane];
+    if (hs) h0 = hs[r0 + lane];
   }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
+  if (rem1) {
+    i1 = idx[r0 + 64 + lane];
+    if (hs) h1 = hs[r0 + 64 + lane];
+  }
+  const int mn = wave_min(min(rem0 ? i0 : INT32_MAX, rem1 ? i1 : INT32_MAX));
+  const int mx = wave_max(max(rem0 ? i0 : INT32_MIN, rem1 ? i1 : INT32_MIN));
+  int hmn = 0, hmx = 0;
   if (hs) {
-    hmn = wave_min(hmn);
-    hmx = wave_max(hmx);
-  } else {
-    hmn = hmx = 0;
+    hmn = wave_min(min(rem0 ? h0 : INT32_MAX, rem1 ? h1 : INT32_MAX));
+    hmx = wave_max(max(rem0 ? h0 : INT32_MIN, rem1 ? h1 : INT32_MIN));
   }
-  if (threadIdx.x == 0) {
+  if (lane == 0) {
     int32_t *out = (isq ? a.q_stats + ((size_t)bh * a.nq + blk) * 4 : a.k_stats + ((size_t)bh * a.nk + blk) * 4);
     *reinterpret_cast<int4 *>(out) = make_int4(mn, mx, hmn, hmx);
   }
@@ -83,17 +84,18 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
   if (segs == nullptr || hs == nullptr) return;
   // Bucket segments: the smallest remaining bucket id, then the min and max
   // position of its rows, until every row is taken (one record per distinct
-  // bucket, at most `block`).  A block holds at most 128 rows: two per lane.
-  const int lane = threadIdx.x;
-  bool rem0 = r0 + lane < r1, rem1 = r0 + 64 + lane < r1;
-  int h0 = 0, i0 = 0, h1 = 0, i1 = 0;
-  if (rem0) h0 = hs[r0 + lane], i0 = idx[r0 + lane];
-  if (rem1) h1 = hs[r0 + 64 + lane], i1 = idx[r0 + 64 + lane];
+  // bucket, at most `block`).
   const int nblk_side = isq ? a.nq : a.nk;
   int4 *out = reinterpret_cast<int4 *>(segs) + ((size_t)bh * nblk_side + blk) * a.block;
   int nseg = 0;
+  if (hmn == hmx) {  // one bucket (or no rows): its record is the block's statistics
+    nseg = r0 < r1 ? 1 : 0;
+    if (lane == 0 && nseg) out[0] = make_int4(hmn, mn, mx, 0);
+    rem0 = rem1 = false;
+  }
+  int h = hmn;  // the smallest remaining bucket id (the first is the block's minimum)
   while (__ballot(rem0 || rem1) != 0ull) {  // wave-uniform; each pass takes at least one row
-    const int h = wave_min(min(rem0 ? h0 : INT32_MAX, rem1 ? h1 : INT32_MAX));
+    if (nseg > 0) h = wave_min(min(rem0 ? h0 : INT32_MAX, rem1 ? h1 : INT32_MAX));
     const bool in0 = rem0 && h0 == h, in1 = rem1 && h1 == h;
     const int mn2 = wave_min(min(in0 ? i0 : INT32_MAX, in1 ? i1 : INT32_MAX));
     const int mx2 = wave_max(max(in0 ? i0 : INT32_MIN, in1 ? i1 : INT32_MIN));
@@ -109,12 +111,13 @@ __global__ __launch_bounds__(64) void k_block_stats(MetaArgs a) {
 // two blocks has a key at or before one of its queries.  Both record lists are
 // in ascending bucket order, so one merge pass finds the common buckets.
 // `mine` (in LDS) belongs to the list's own block, `other` to the partner;
-// mine_is_q says which side holds the queries.
-__device__ __forceinline__ bool segs_admit(const int4 *mine, int n_mine, const int4 *other, int n_other,
-                                           bool mine_is_q) {
+// mine_is_q says which side holds the queries.  o0 and o1 are other[0] and
+// other[1], already loaded (most blocks hold one or two buckets).
+__device__ __forceinline__ bool segs_admit(const int4 *mine, int n_mine, const int4 *other, int n_other, int4 o0,
+                                           int4 o1, bool mine_is_q) {
   int a = 0, b = 0;
   while (a < n_mine && b < n_other) {
-    const int4 m = mine[a], o = other[b];
+    const int4 m = mine[a], o = b == 0 ? o0 : (b == 1 ? o1 : other[b]);
     if (m.x < o.x) {
       ++a;
     } else if (m.x > o.x) {
@@ -138,12 +141,30 @@ __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, i
   const int4 *qst = reinterpret_cast<const int4 *>(a.q_stats) + (size_t)bh * a.nq;
   const int4 *kst = reinterpret_cast<const int4 *>(a.k_stats) + (size_t)bh * a.nk;
   const bool exact = hash_mode && a.q_segs != nullptr;
+  // Partner statistics are read kPass x 64 at a time, all loads issued before
+  // any is used; the first batch goes out before this block's own records, so
+  // a list of up to kPass x 64 partners costs one round trip.
+  constexpr int kPass = 4;
+  const int n_part = is_row ? a.nk : a.nq;
+  const int4 *ost = is_row ? kst : qst;
+  const int32_t *onseg = is_row ? a.k_nseg : a.q_nseg;  // partners' record counts (exact rule)
+  if (exact) onseg += (size_t)bh * n_part;
+  int4 st[kPass];
+  int on[kPass];
+  auto load_pass = [&](int base0) {
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int o = base0 + 64 * u + lane;
+      st[u] = o < n_part ? ost[o] : make_int4(0, 0, 0, 0);
+      on[u] = exact && o < n_part ? onseg[o] : 0;
+    }
+  };
+  load_pass(0);
   int n_other;
   int32_t *list;
   int32_t *cnt_out;
   int4 mine;
   const int4 *other_seg = nullptr;  // partner blocks' records, `block` slots each
-  const int32_t *other_n = nullptr;
   int n_mine = 0;
   if (is_row) {
     n_other = a.nk;
@@ -152,10 +173,9 @@ __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, i
     cnt_out = a.row_cnt + (size_t)bh * a.nq + r;
     if (exact) {
       const int4 *src = reinterpret_cast<const int4 *>(a.q_segs) + ((size_t)bh * a.nq + r) * a.block;
-      n_mine = a.q_nseg[(size_t)bh * a.nq + r];
-      for (int t = lane; t < n_mine; t += 64) mine_seg[t] = src[t];
+      n_mine = min(a.q_nseg[(size_t)bh * a.nq + r], a.block);
+      for (int t = lane; t < a.block; t += 64) mine_seg[t] = src[t];  // every slot (no wait for the count)
       other_seg = reinterpret_cast<const int4 *>(a.k_segs) + (size_t)bh * a.nk * a.block;
-      other_n = a.k_nseg + (size_t)bh * a.nk;
     }
   } else {
     const int j = r - a.nq;
@@ -165,36 +185,59 @@ __global__ __launch_bounds__(64) void k_build_lists(MetaArgs a, int hash_mode, i
     cnt_out = a.col_cnt + (size_t)bh * a.nk + j;
     if (exact) {
       const int4 *src = reinterpret_cast<const int4 *>(a.k_segs) + ((size_t)bh * a.nk + j) * a.block;
-      n_mine = a.k_nseg[(size_t)bh * a.nk + j];
-      for (int t = lane; t < n_mine; t += 64) mine_seg[t] = src[t];
+      n_mine = min(a.k_nseg[(size_t)bh * a.nk + j], a.block);
+      for (int t = lane; t < a.block; t += 64) mine_seg[t] = src[t];  // every slot (no wait for the count)
       other_seg = reinterpret_cast<const int4 *>(a.q_segs) + (size_t)bh * a.nq * a.block;
-      other_n = a.q_nseg + (size_t)bh * a.nq;
     }
   }
   __syncthreads();  // mine_seg written by the wave's lanes, read by all
   int count = 0;
-  for (int base = 0; base < n_other; base += 64) {
-    const int o = base + lane;
-    bool live = false, free = false;
-    if (o < n_other) {
-      const int4 qs = is_row ? mine : qst[o];
-      const int4 ks = is_row ? kst[o] : mine;
-      live = qs.y >= ks.x;
-      free = ks.y <= qs.x;
-      if (hash_mode) {
-        live = live && qs.w >= ks.z && qs.z <= ks.w;
-        free = free && qs.z == qs.w && ks.z == ks.w && qs.z == ks.z;
+  for (int base0 = 0; base0 < n_other; base0 += kPass * 64) {
+    if (base0 > 0) load_pass(base0);
+    // The range test for every pass first; the first two records of each
+    // partner that needs the exact test are then loaded together.
+    bool live[kPass], free[kPass], need[kPass];
+    int4 rec0[kPass], rec1[kPass];
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int o = base0 + 64 * u + lane;
+      live[u] = free[u] = need[u] = false;
+      if (o < n_other) {
+        const int4 qs = is_row ? mine : st[u];
+        const int4 ks = is_row ? st[u] : mine;
+        live[u] = qs.y >= ks.x;
+        free[u] = ks.y <= qs.x;
+        if (hash_mode) {
+          live[u] = live[u] && qs.w >= ks.z && qs.z <= ks.w;
+          free[u] = free[u] && qs.z == qs.w && ks.z == ks.w && qs.z == ks.z;
+        }
+        // With one bucket on each side the range test is already exact.
+        need[u] = exact && live[u] && !(qs.z == qs.w && ks.z == ks.w);
       }
-      // With one bucket on each side the range test is already exact.
-      if (exact && live && !(qs.z == qs.w && ks.z == ks.w))
-        live = segs_admit(mine_seg, n_mine, other_seg + (size_t)o * a.block, other_n[o], is_row);
+      rec0[u] = rec1[u] = make_int4(0, 0, 0, 0);
+      if (need[u]) {
+        const int4 *os = other_seg + (size_t)o * a.block;
+        const int no = min(on[u], a.block);
+        if (no > 0) rec0[u] = os[0];
+        if (no > 1) rec1[u] = os[1];
+      }
     }
-    const unsigned long long m = __ballot(live);
-    if (live) {
-      const int pos = count + __popcll(m & ((1ull << lane) - 1ull));
-      list[pos] = o | (free ? (int)0x80000000u : 0);
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int base = base0 + 64 * u;
+      if (base >= n_other) break;  // wave-uniform
+      const int o = base + lane;
+      bool lv = live[u];
+      if (need[u])
+        lv = segs_admit(mine_seg, n_mine, other_seg + (size_t)o * a.block, min(on[u], a.block), rec0[u], rec1[u],
+                        is_row);
+      const unsigned long long m = __ballot(lv);
+      if (lv) {
+        const int pos = count + __popcll(m & ((1ull << lane) - 1ull));
+        list[pos] = o | (free[u] ? (int)0x80000000u : 0);
+      }
+      count += __popcll(m);
     }
-    count += __popcll(m);
   }
   if (lane == 0) *cnt_out = count;
 }
