@@ -332,7 +332,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   asm volatile("" : "+v"(tid));
   const int qrow_e = qb * BS + 32 * (tid >> 6) + (tid & 31), half_e = (tid >> 5) & 1;
   if (qrow_e < a.Tq) {
-    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + out_row_q(a, bh, qrow_e)) * D;
+    // The output row: lrow from the prologue (the caller's row with orig_rows)
+    // where one more live register costs no spill, else loaded again here.
+    const int orow = MODE != kDense ? lrow : out_row_q(a, bh, qrow_e);
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -587,7 +590,10 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     asm volatile("" : "+v"(tid));
     const int krow_e = kb * BS + 32 * (tid >> 6) + (tid & 31);
     const int half_e = (tid >> 5) & 1;
-    const size_t orow = (size_t)out_row_k(a, bh, krow_e);
+    // With orig_rows the output row is the row the K and V loads read (the
+    // clamped k_rows entry, kept from the prologue where one more live
+    // register costs no spill, else loaded again here).
+    const size_t orow = STORE ? (size_t)out_row_k(a, bh, krow_e) : a.orig_rows ? (size_t)ksrc : (size_t)krow_e;
     uint16_t *dK = static_cast<uint16_t *>(a.dk) + (koff + orow) * D;
     uint16_t *dV = static_cast<uint16_t *>(a.dv) + (koff + orow) * D;
 #pragma unroll

@@ -285,6 +285,9 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   asm volatile("" : "+v"(tid));
   const int lane_e = tid & 63, half_e = lane_e >> 5, qw_e = (tid >> 6) % QW;
   const int qrow_e = qb * BS + 32 * qw_e + (lane_e & 31);
+  // The output row's index is loaded before the exchange below, whose barriers
+  // wait only for LDS, so its latency overlaps the merge.
+  int orow_raw = a.orig_rows && kh == 0 && qrow_e < a.Tq ? a.q_rows[(size_t)bh * a.Tq + qrow_e] : qrow_e;
   constexpr int XN = 2 + 16 * (D / 32);  // floats per lane: reference max, sum, accumulator
   constexpr int FIT = (int)(sizeof(sb) / (sizeof(float) * XN * 64));
   constexpr int QX = FIT >= QW ? QW : (FIT >= 2 ? 2 : 1);
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow_e < a.Tq) {
-    const int orow = out_row_q(a, bh, qrow_e);
+    const int orow = a.orig_rows ? min(max(orow_raw, 0), a.Tq - 1) : qrow_e;  // as out_row_q
     uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
