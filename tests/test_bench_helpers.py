@@ -1,0 +1,54 @@
+"""Host-side helpers of bench.py: the warm-up loop and the choice of the dense-causal comparator's
+block (the faster one is kept).  No GPU: torch's synchronize is replaced by a stand-in."""
+import os
+import sys
+import time
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+
+
+class _Cuda:
+    def __init__(self):
+        self.syncs = 0
+
+    def synchronize(self):
+        self.syncs += 1
+
+
+class _Torch:
+    def __init__(self):
+        self.cuda = _Cuda()
+
+
+def test_warm_runs_at_least_n_calls():
+    calls = []
+    n = bench._warm(_Torch(), lambda t: calls.append(t), 5)
+    assert n == 5 and calls == [None] * 5
+
+
+def test_warm_keeps_going_until_the_time_floor():
+    calls = []
+
+    def fn(t):
+        calls.append(t)
+        time.sleep(0.002)
+
+    n = bench._warm(_Torch(), fn, 1, min_ms=20.0)
+    assert n == len(calls) and n >= 5  # at least 20 ms of 2 ms calls
+
+
+def test_time_dense_keeps_the_fastest_block():
+    cost = {64: 0.004, 128: 0.001}
+    seen = []
+
+    def run(block, timer):
+        seen.append((block, timer))
+        time.sleep(cost[block])
+
+    ms, best, by_block, timer = bench.time_dense(_Torch(), run, (64, 128), steps=3, warmup=1)
+    assert best == 128 and timer is None
+    assert set(by_block) == {64, 128} and by_block[128] < by_block[64]
+    assert abs(ms - by_block[128]) < 1e-3
+    assert [b for b, _ in seen].count(64) == 4 and [b for b, _ in seen].count(128) == 4
