@@ -115,10 +115,32 @@ __device__ __forceinline__ void lds_copy16(const void *src, void *dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(dst));  // dst is wave-uniform
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
 }
-__device__ __forceinline__ void lds_copy4(const void *src, void *dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(dst));  // dst is wave-uniform
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
+
+// The same copies from a wave-uniform base (held in SGPRs) plus a per-lane
+// 32-bit byte offset: the address needs no 64-bit vector arithmetic, and
+// copies from two matrices at the same rows share one offset register.
+// (readfirstlane returns a signed int: each half goes through uint32_t before
+// widening, or a low word with bit 31 set would fill the high word with ones.)
+__device__ __forceinline__ uint64_t uniform_base(const void *p) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
+__device__ __forceinline__ void lds_copy16_at(uint64_t base, uint32_t off, void *dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(dst));  // dst is wave-uniform
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void lds_copy4_at(uint64_t base, uint32_t off, void *dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(dst));  // dst is wave-uniform
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory");
+}
+
+// The wave's index in its group, known to the compiler as wave-uniform, so the
+// LDS destinations of the copies are computed with scalar instructions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // Hardware dispatches work group i to XCD i % 8.  Give each XCD a contiguous
 // range of logical ids so the blocks of one head share that XCD's L2.
@@ -166,14 +188,14 @@ template <int D, int NW>
 __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, int row0, int nvalid,
                                            const DmaOffsets<D, NW> &o) {
   using O = DmaOffsets<D, NW>;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint16_t *base = g + (size_t)row0 * D;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const uint64_t base = uniform_base(g + (size_t)row0 * D);
   if (nvalid == kChunk) {  // wave-uniform: one branch for the whole chunk
 #pragma unroll
     for (int k = 0; k < O::PER_WAVE; ++k) {
       const int i = k * NW + w;
       if (O::NINST % NW == 0 || i < O::NINST) {
-        lds_copy16(base + o.off[k], dst.v + i * 512);
+        lds_copy16_at(base, (uint32_t)o.off[k] * 2u, dst.v + i * 512);
       }
     }
   } else {
@@ -184,7 +206,7 @@ __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, 
         const int s = i * 64 + lane;
         const int r = s / O::CPR, p = s % O::CPR;
         const int rr = r < nvalid ? r : nvalid - 1;
-        lds_copy16(base + rr * D + ((p ^ swz(r)) << 3), dst.v + i * 512);
+        lds_copy16_at(base, (uint32_t)(rr * D + ((p ^ swz(r)) << 3)) * 2u, dst.v + i * 512);
       }
     }
   }
@@ -212,20 +234,30 @@ __device__ __forceinline__ void dma_rows_load(DmaRows<D, NW> &dr, const int32_t 
   }
 }
 
-// dma_matrix through the row indirection: g is the head's matrix base.
+// dma_matrix through the row indirection: g is the head's matrix base.  The
+// byte offset of a row is 32-bit: the host accepts B * H * T * D < 2^31
+// elements, so a head's bf16 matrix spans less than 4 GiB.
+template <int D, int NW>
+__device__ __forceinline__ uint32_t dma_row_offset(const DmaRows<D, NW> &dr, int k, int T) {
+  // The piece part depends on the thread only (unsigned, from threadIdx), so it
+  // is computed once outside the chunk loop; per chunk: a clamp and a shift-add.
+  constexpr unsigned CPR = DmaOffsets<D, NW>::CPR;
+  const unsigned s = ((unsigned)k * NW + (threadIdx.x >> 6)) * 64u + (threadIdx.x & 63u);
+  const unsigned r = s / CPR, p = s % CPR;
+  const unsigned piece = (p ^ (unsigned)swz((int)r)) << 4;
+  const int src = min(max(dr.row[k], 0), T - 1);
+  return (uint32_t)src * (uint32_t)(D * 2) + piece;
+}
+
 template <int D, int NW>
 __device__ __forceinline__ void dma_matrix_rows(MatChunk<D> &dst, const uint16_t *g, int T, const DmaRows<D, NW> &dr) {
   using O = DmaOffsets<D, NW>;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int w = wave_id();
+  const uint64_t base = uniform_base(g);
 #pragma unroll
   for (int k = 0; k < O::PER_WAVE; ++k) {
     const int i = k * NW + w;
-    if (O::NINST % NW == 0 || i < O::NINST) {
-      const int s = i * 64 + lane;
-      const int r = s / O::CPR, p = s % O::CPR;
-      const int src = min(max(dr.row[k], 0), T - 1);
-      lds_copy16(g + (size_t)src * D + ((p ^ swz(r)) << 3), dst.v + i * 512);
-    }
+    if (O::NINST % NW == 0 || i < O::NINST) lds_copy16_at(base, dma_row_offset<D, NW>(dr, k, T), dst.v + i * 512);
   }
 }
 
@@ -233,7 +265,7 @@ __device__ __forceinline__ void dma_matrix_rows(MatChunk<D> &dst, const uint16_t
 __device__ __forceinline__ void dma_vec(void *dst, const void *g, int row0, int nvalid) {
   const int lane = threadIdx.x & 63;
   const int rr = lane < nvalid ? lane : nvalid - 1;
-  lds_copy4(static_cast<const uint32_t *>(g) + row0 + rr, dst);
+  lds_copy4_at(uniform_base(static_cast<const uint32_t *>(g) + row0), (uint32_t)rr * 4u, dst);
 }
 
 // Per-lane element offsets of the fragment reads inside a MatChunk<D>, computed
