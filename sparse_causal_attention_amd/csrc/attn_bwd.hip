@@ -670,7 +670,7 @@ struct DsBuf {
 // DMA source offsets that gather one 64-key chunk of a stored tile (16-query
 // groups [BS/16][BS keys][16 queries], offsets relative to the chunk's first
 // key row) into the row-major swizzled MatChunk<BS> layout: LDS piece s holds
-// logical piece lp = (s % CPR) ^ swz(r) (queries 8 lp..) of chunk row r = s / CPR.
+// logical piece lp = (s % CPR) ^ swz<BS>(r) (queries 8 lp..) of chunk row r = s / CPR.
 template <int BS, int NW>
 __device__ __forceinline__ DmaOffsets<BS, NW> dma_offsets_ds() {
   using O = DmaOffsets<BS, NW>;
@@ -679,7 +679,7 @@ __device__ __forceinline__ DmaOffsets<BS, NW> dma_offsets_ds() {
 #pragma unroll
   for (int k = 0; k < O::PER_WAVE; ++k) {
     const int s = (k * NW + w) * 64 + lane;
-    const int r = s / O::CPR, lp = (s % O::CPR) ^ swz(r);
+    const int r = s / O::CPR, lp = (s % O::CPR) ^ swz<BS>(r);
     o.off[k] = (lp >> 1) * BS * 16 + r * 16 + (lp & 1) * 8;
   }
   return o;
@@ -708,10 +708,13 @@ __global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
   list_window2(rl, sl, 0);
   const DmaOffsets<D, NW> dmk = dma_offsets<D, NW>();
   const DmaOffsets<BS, NW> dms = dma_offsets_ds<BS, NW>();
-  int k_off[MTW];
+  int k_off[MTW], k_off2[MTW];
 #pragma unroll
-  for (int i = 0; i < MTW; ++i) k_off[i] = trans_offset<D>(mh * MTW + i);
-  const int ds_off = trans_offset<BS>(qw);  // this wave's 32 query columns
+  for (int i = 0; i < MTW; ++i) {
+    k_off[i] = trans_offset<D>(mh * MTW + i, 0);
+    k_off2[i] = trans_offset<D>(mh * MTW + i, 1);
+  }
+  const int ds_off = trans_offset<BS>(qw, 0), ds_off2 = trans_offset<BS>(qw, 1);  // this wave's 32 query columns
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
   auto issue = [&](DsBuf<D, BS> &b, const Chunk &c) {
@@ -755,9 +758,9 @@ __global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
     bf16x8 ktr[4][MTW], dsb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      dsb[t] = frag_trans_at<BS>(b.ds, ds_off, t);
+      dsb[t] = frag_trans_at<BS>(b.ds, ds_off, ds_off2, t);
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) ktr[t][i] = frag_trans_at<D>(b.k, k_off[i], t);
+      for (int i = 0; i < MTW; ++i) ktr[t][i] = frag_trans_at<D>(b.k, k_off[i], k_off2[i], t);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)

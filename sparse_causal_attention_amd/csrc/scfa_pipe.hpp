@@ -8,12 +8,23 @@
 // ds_write instructions are spent on staging.
 //
 // LDS layout of a matrix: row-major, 16-byte pieces XOR-swizzled inside each
-// row: logical piece c of row r sits at physical piece c ^ swz(r), where
-// swz(r) = 2*(r & 3) + ((r >> 2) & 1) takes the eight values 0..7 over r & 7.
-// The row-fragment reads (eight consecutive rows, one logical piece) then hit
-// eight different pieces, and the transposed reads (four rows 4h..4h+3 at a
-// logical piece pair) hit four different piece pairs, so neither conflicts on
-// the LDS banks.  The swizzle is applied through the DMA source addresses.
+// row: logical piece c of row r sits at physical piece c ^ swz<D>(r).  The LDS
+// serves 256 bytes per pass: 16 lanes of a 16-byte row-fragment read, 32 lanes
+// of an 8-byte transposed read.
+//  * D = 64 (128-byte rows, 8 pieces): row bits 1, 2, 3 flip piece bits 2, 0,
+//    1.  A row-fragment read (rows r..r+15, one logical piece) then reaches 16
+//    different bank groups, and so does each pass of a transposed read (rows
+//    4h..4h+3 or the same + 8, at logical piece pairs): neither conflicts.  (A
+//    swizzle over r & 7 alone, which rows r and r + 8 share, cost every
+//    row-fragment read four cycles of conflicts.)
+//  * D = 128 (256-byte rows, 16 pieces): the swizzle is r & 15 with its four
+//    bits reversed; every row starts on the same bank, so the 16 rows of a
+//    row-fragment pass need 16 different pieces, and the transposed reads'
+//    passes stay conflict-free as well.  (A 3-bit swizzle over r & 7 left
+//    four cycles of conflicts on every row-fragment read and two on every
+//    transposed one.)
+// Either way rows r and r + 16 share the swizzle and rows r and r + 8 do not.
+// The swizzle is applied through the DMA source addresses.
 // Rows past the end of the sequence are filled with copies of the last real
 // row (finite values); the kernels mask them explicitly.
 //
@@ -35,8 +46,12 @@
 
 namespace scfa {
 
-// Piece swizzle of row r (depends on r & 7 only).
-__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Piece swizzle of row r for rows of D bf16 values.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
+  else return ((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -175,7 +190,7 @@ __device__ __forceinline__ DmaOffsets<D, NW> dma_offsets() {
     const int i = k * NW + w;
     const int s = i * 64 + lane;
     const int r = s / O::CPR, p = s % O::CPR;
-    o.off[k] = r * D + ((p ^ swz(r)) << 3);
+    o.off[k] = r * D + ((p ^ swz<D>(r)) << 3);
   }
   return o;
 }
@@ -206,7 +221,7 @@ __device__ __forceinline__ void dma_matrix(MatChunk<D> &dst, const uint16_t *g, 
         const int s = i * 64 + lane;
         const int r = s / O::CPR, p = s % O::CPR;
         const int rr = r < nvalid ? r : nvalid - 1;
-        lds_copy16_at(base, (uint32_t)(rr * D + ((p ^ swz(r)) << 3)) * 2u, dst.v + i * 512);
+        lds_copy16_at(base, (uint32_t)(rr * D + ((p ^ swz<D>(r)) << 3)) * 2u, dst.v + i * 512);
       }
     }
   }
@@ -244,7 +259,7 @@ __device__ __forceinline__ uint32_t dma_row_offset(const DmaRows<D, NW> &dr, int
   constexpr unsigned CPR = DmaOffsets<D, NW>::CPR;
   const unsigned s = ((unsigned)k * NW + (threadIdx.x >> 6)) * 64u + (threadIdx.x & 63u);
   const unsigned r = s / CPR, p = s % CPR;
-  const unsigned piece = (p ^ (unsigned)swz((int)r)) << 4;
+  const unsigned piece = (p ^ (unsigned)swz<D>((int)r)) << 4;
   const int src = min(max(dr.row[k], 0), T - 1);
   return (uint32_t)src * (uint32_t)(D * 2) + piece;
 }
@@ -268,16 +283,29 @@ __device__ __forceinline__ void dma_vec(void *dst, const void *g, int row0, int 
   lds_copy4_at(uniform_base(static_cast<const uint32_t *>(g) + row0), (uint32_t)rr * 4u, dst);
 }
 
+// Lane offset of frag_trans(mt, t = 0): its first read (second = 0, rows
+// 4h..4h+3) or its second (second = 1, the same rows + 8).
+template <int D>
+__device__ __forceinline__ int trans_offset(int mt, int second) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, a = j & 3, mm = j >> 2, g = lane >> 4, h = g >> 1;
+  const int r = 4 * h + mm + 8 * second;
+  const int c = 4 * mt + 2 * (g & 1) + (a >> 1);
+  return r * D + ((c ^ swz<D>(r)) << 3) + 4 * (a & 1);
+}
+
 // Per-lane element offsets of the fragment reads inside a MatChunk<D>, computed
 // once per kernel so every read in the main loop is base + lane offset +
 // compile-time constant (an LDS instruction immediate).
 //  rows[kk]: frag_rows(row = col, kk); add 32*sub*D for sub-tile sub.
-//  trans[mt]: first read of frag_trans(mt, t = 0); add 16*t*D for k-step t and
-//             8*D for the second read (rows r and r + 8 share swz(r)).
+//  trans[mt]: first read of frag_trans(mt, t = 0); add 16*t*D for k-step t
+//             (rows r and r + 16 share the swizzle).
+//  trans2[mt]: its second read (row r + 8, whose swizzle differs).
 template <int D>
 struct LaneOffsets {
   int rows[D / 16];
   int trans[D / 32];
+  int trans2[D / 32];
 };
 
 template <int D>
@@ -286,25 +314,13 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets() {
   const int col = lane & 31, half = lane >> 5;
   LaneOffsets<D> o;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) o.rows[kk] = col * D + (((2 * kk + half) ^ swz(col)) << 3);
-  const int j = lane & 15, a = j & 3, mm = j >> 2, g = lane >> 4, h = g >> 1;
-  const int x = 4 * h + mm;  // == r & 7 for both rows a lane reads (r and r + 8)
+  for (int kk = 0; kk < D / 16; ++kk) o.rows[kk] = col * D + (((2 * kk + half) ^ swz<D>(col)) << 3);
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
-    const int c = 4 * mt + 2 * (g & 1) + (a >> 1);
-    o.trans[mt] = x * D + ((c ^ swz(x)) << 3) + 4 * (a & 1);
+    o.trans[mt] = trans_offset<D>(mt, 0);
+    o.trans2[mt] = trans_offset<D>(mt, 1);
   }
   return o;
-}
-
-// LaneOffsets<D>::trans[mt] for a run-time (wave-uniform) mt.
-template <int D>
-__device__ __forceinline__ int trans_offset(int mt) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, a = j & 3, mm = j >> 2, g = lane >> 4, h = g >> 1;
-  const int x = 4 * h + mm;
-  const int c = 4 * mt + 2 * (g & 1) + (a >> 1);
-  return x * D + ((c ^ swz(x)) << 3) + 4 * (a & 1);
 }
 
 template <int D>
@@ -316,9 +332,10 @@ __device__ __forceinline__ bf16x8 frag_rows(const MatChunk<D> &m, const LaneOffs
 template <int D>
 __device__ __forceinline__ bf16x8 frag_trans(const MatChunk<D> &m, const LaneOffsets<D> &o, int mt, int t) {
   const uint16_t *p0 = m.v + o.trans[mt] + 16 * t * D;
+  const uint16_t *p1 = m.v + o.trans2[mt] + 16 * t * D;
 #if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only
   const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0));
-  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0 + 8 * D));
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p1));
 #else
   const i16x4 x0 = {}, x1 = {};
 #endif
@@ -326,13 +343,14 @@ __device__ __forceinline__ bf16x8 frag_trans(const MatChunk<D> &m, const LaneOff
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// frag_trans with the lane offset given directly (trans_offset<D>(mt)).
+// frag_trans with the lane offsets given directly (trans_offset<D>(mt, 0 / 1)).
 template <int D>
-__device__ __forceinline__ bf16x8 frag_trans_at(const MatChunk<D> &m, int off, int t) {
+__device__ __forceinline__ bf16x8 frag_trans_at(const MatChunk<D> &m, int off, int off2, int t) {
   const uint16_t *p0 = m.v + off + 16 * t * D;
+  const uint16_t *p1 = m.v + off2 + 16 * t * D;
 #if defined(__HIP_DEVICE_COMPILE__)  // target builtin: device pass only
   const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0));
-  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p0 + 8 * D));
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)to_lds(p1));
 #else
   const i16x4 x0 = {}, x1 = {};
 #endif
