@@ -309,8 +309,13 @@ def run_dense(scfa, w, q, k, v, do, timer=None):
 DENSE_CALLS = ["dense_fwd", "dense_bwd_dq", "dense_bwd_dkdv"]
 
 
+CPU_SAMPLE_S = 10.0  # the CPU oracle runs heads until at least this much work has been timed
+
+
 def cpu_baseline(w, tile_units_per_head):
-    """The fp64 oracle on one head of the workload (LSH, sort, masked attention fwd + bwd)."""
+    """The fp64 oracle on heads (b=0, h=0, 1, ...) of the workload (LSH, sort, masked attention fwd + bwd),
+    until at least CPU_SAMPLE_S seconds of work; each head is credited with the workload's average
+    executed-tile flops per head."""
     import numpy as np
 
     from gen import head_inputs, lsh_rotation
@@ -323,24 +328,29 @@ def cpu_baseline(w, tile_units_per_head):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    hi = head_inputs(w, 0, 0)
-    R = lsh_rotation(w, 0)
-    t0 = time.perf_counter()
-    bq, bk = lsh.buckets(hi.q, R), lsh.buckets(hi.k, R)
-    pq, hq, iq = lsh.bucket_sort(bq, hi.q_pos)
-    pk, hk, ik = lsh.bucket_sort(bk, hi.k_pos)
-    A.forward(hi.q[pq], hi.k[pk], hi.v[pk], iq, ik, hq, hk, w.scale)
-    A.backward(hi.q[pq], hi.k[pk], hi.v[pk], hi.do[pq], iq, ik, hq, hk, w.scale)
-    dt = time.perf_counter() - t0
-    flops = 14.0 * tile_units_per_head * w.d
+    dt, heads = 0.0, 0
+    while heads < w.H and (heads == 0 or dt < CPU_SAMPLE_S):
+        hi = head_inputs(w, 0, heads)  # inputs are drawn outside the timed work
+        R = lsh_rotation(w, heads)
+        t0 = time.perf_counter()
+        bq, bk = lsh.buckets(hi.q, R), lsh.buckets(hi.k, R)
+        pq, hq, iq = lsh.bucket_sort(bq, hi.q_pos)
+        pk, hk, ik = lsh.bucket_sort(bk, hi.k_pos)
+        A.forward(hi.q[pq], hi.k[pk], hi.v[pk], iq, ik, hq, hk, w.scale)
+        A.backward(hi.q[pq], hi.k[pk], hi.v[pk], hi.do[pq], iq, ik, hq, hk, w.scale)
+        dt += time.perf_counter() - t0
+        heads += 1
+    flops = 14.0 * tile_units_per_head * w.d * heads
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"one head (b=0, h=0) of the workload: LSH + sort of Q and K, dense masked fp64 forward "
-                  f"and backward over {w.T} tokens; {dt:.2f} s, credited with that head's executed-tile flops",
+        "sample": f"{heads} heads (b=0, h=0..{heads - 1}) of the workload, run until at least {CPU_SAMPLE_S:.0f} s of "
+                  f"work: LSH + sort of Q and K, dense masked fp64 forward and backward over {w.T} tokens each; "
+                  f"{dt:.2f} s, credited with the workload's average executed-tile flops per head",
         "seconds": dt,
+        "heads": heads,
     }
 
 
@@ -1053,7 +1063,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        _log("[bench] cpu oracle baseline (one head)")
+        _log("[bench] cpu oracle baseline (fp64, heads until the sample is long enough)")
         cpu = cpu_baseline(w, units / (w.B * w.H))
 
     out = {
