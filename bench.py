@@ -695,6 +695,15 @@ def _full_length_inputs(w, torch, names, seed):
     return dict(zip(names, full)), keep
 
 
+def _dropped(keep, T, torch):
+    """The positions [B,H,T - n] (ascending) that the kept set [B,H,n] leaves out, per head."""
+    B, H, n = keep.shape
+    mask = torch.ones((B, H, T), dtype=torch.bool, device=keep.device)
+    mask.scatter_(2, keep.long(), False)
+    pos = torch.arange(T, dtype=torch.int32, device=keep.device).expand(B, H, T)
+    return pos[mask].view(B, H, T - n).contiguous()
+
+
 def _roofline(kernel, flops, ms):
     achieved = flops / (ms * 1e-3) / 1e12
     return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -702,16 +711,12 @@ def _roofline(kernel, flops, ms):
             "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops}
 
 
-def bench_workload(scfa, torch, wid, args):
-    """One benchmark line for workload 2 (Hash-sparse forward, 8k tokens), 3 (QK-sparse training step with
-    30 % of the tokens dropped, 8k tokens) or 5 (50 % drop, then Hash-sparse forward, 1M tokens).  The step
-    runs every row of the hot path the workload has, from inputs resident in HBM:
-      2: LSH + sort of Q and K (one call over both), block lists, forward over the sorted view;
-      3: compaction of Q, K, V, dO to the kept tokens, block lists, forward, dQ, dK/dV, and the outputs put
-         back at the original positions (zero rows for dropped tokens);
-      5: compaction of Q, K, V, LSH + sort of the kept Q and K (one call), block lists, forward over the
-         sorted view, and O put back at the original positions.
-    The dense-causal comparator is the same library's dense mode on the original [B,H,T,d] tensors."""
+def workload_setup(scfa, torch, wid):
+    """Inputs of workload 2, 3 or 5 resident in HBM, and its step (see bench_workload).
+
+    Returns (w, step, calls, dense_in): step(timer) runs one step (marking the timer after each call
+    in ``calls`` when one is given) and returns (meta, outputs); dense_in are the full-length (q, k, v,
+    dout) the dense-causal comparator reads."""
     import numpy as np
 
     from gen import WORKLOADS, head_inputs, lsh_rotation
@@ -744,81 +749,96 @@ def bench_workload(scfa, torch, wid, args):
             meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=False, exact=True)
             if t:
                 t.mark()
-            scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=blk, scale=sc, q_rows=pp[:B], k_rows=pp[B:])
+            o, lse = scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=blk, scale=sc, q_rows=pp[:B],
+                                         k_rows=pp[B:])
             if t:
                 t.mark()
-            return meta
+            return meta, dict(o=o, lse=lse, hash=hh, idx=ii, perm=pp)
     elif wid == 3:
         full, keep = _full_length_inputs(w, torch, ("q", "k", "v", "do"), 300 + wid)
-        dense_in = (full["q"], full["k"], full["v"], full["do"])
-        calls = ["compact", "block_meta", "fwd", "bwd_dq", "bwd_dkdv", "uncompact"]
+        drop = _dropped(keep, w.T, torch)
+        q, k, v, do = (full[n] for n in ("q", "k", "v", "do"))
+        dense_in = (q, k, v, do)
+        calls = ["block_meta", "fwd", "bwd_dq", "bwd_dkdv", "clear_dropped"]
+        rows = dict(q_rows=keep, k_rows=keep, flags=scfa.FLAG_ORIG_ROWS, block=blk, scale=sc)
 
         def step(t):
             if t:
                 t.begin()
-            qc, kc, vc, gc = (scfa.gather_rows(full[n], keep) for n in ("q", "k", "v", "do"))
-            if t:
-                t.mark()
             meta = scfa.block_meta(keep, keep, block=blk, with_cols=True, exact=True)
             if t:
                 t.mark()
-            o, lse = scfa.attn_fwd_lists(qc, kc, vc, keep, keep, None, None, meta, block=blk, scale=sc)
+            o, lse = scfa.attn_fwd_lists(q, k, v, keep, keep, None, None, meta, **rows)
             if t:
                 t.mark()
-            dq, delta = scfa.attn_bwd_dq_lists(qc, kc, vc, o, lse, gc, keep, keep, None, None, meta, block=blk,
-                                               scale=sc)
+            dq, delta = scfa.attn_bwd_dq_lists(q, k, v, o, lse, do, keep, keep, None, None, meta, **rows)
             if t:
                 t.mark()
-            dk, dv = scfa.attn_bwd_dkdv_lists(qc, kc, vc, lse, gc, delta, keep, keep, None, None, meta, block=blk,
-                                              scale=sc)
+            dk, dv = scfa.attn_bwd_dkdv_lists(q, k, v, lse, do, delta, keep, keep, None, None, meta, **rows)
             if t:
                 t.mark()
             for x in (o, dq, dk, dv):
-                scfa.scatter_rows(x, keep, w.T)
+                scfa.zero_rows(x, drop)
             if t:
                 t.mark()
-            return meta
+            return meta, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
     elif wid == 5:
         full, keep = _full_length_inputs(w, torch, ("q", "k", "v"), 300 + wid)
-        dense_in = (full["q"], full["k"], full["v"], None)
-        B, n = w.B, w.n_keep
-        qk = torch.empty((2 * B, w.H, n, w.d), dtype=torch.bfloat16, device=dev)
+        B = w.B
+        qk = torch.cat([full.pop("q"), full.pop("k")])  # [2B,H,T,d]: Q and K stacked along the batch
+        v = full["v"]
+        dense_in = (qk[:B], qk[B:], v, None)
         keep2 = torch.cat([keep, keep]).contiguous()
-        calls = ["compact", "lsh_sort_qk", "block_meta", "fwd", "uncompact"]
+        drop = _dropped(keep, w.T, torch)
+        calls = ["lsh_sort_qk", "block_meta", "fwd", "clear_dropped"]
 
         def step(t):
             if t:
                 t.begin()
-            scfa.gather_rows(full["q"], keep, out=qk[:B])
-            scfa.gather_rows(full["k"], keep, out=qk[B:])
-            vc = scfa.gather_rows(full["v"], keep)
-            if t:
-                t.mark()
-            hh, ii, pp, _, _ = scfa.lsh_bucket_sort(qk, R, w.n_buckets, idx=keep2, idx_ascending=True, want_x=False)
+            hh, ii, _, _, _ = scfa.lsh_bucket_sort(qk, R, w.n_buckets, idx=keep2, idx_ascending=True, want_x=False,
+                                                   x_rows=keep2)
             qh, kh, qi, ki = hh[:B], hh[B:], ii[:B], ii[B:]
             if t:
                 t.mark()
             meta = scfa.block_meta(qi, ki, qh, kh, block=blk, with_cols=False, exact=True)
             if t:
                 t.mark()
-            o, _ = scfa.attn_fwd_lists(qk[:B], qk[B:], vc, qi, ki, qh, kh, meta, block=blk, scale=sc,
-                                       q_rows=pp[:B], k_rows=pp[B:])
+            # sorted view row i is the token at original position qi[i]: read and write that row
+            o, lse = scfa.attn_fwd_lists(qk[:B], qk[B:], v, qi, ki, qh, kh, meta, block=blk, scale=sc, q_rows=qi,
+                                         k_rows=ki, flags=scfa.FLAG_ORIG_ROWS)
             if t:
                 t.mark()
-            scfa.scatter_rows(o, qi, w.T)  # view row i holds the query at original position qi[i]
+            scfa.zero_rows(o, drop)
             if t:
                 t.mark()
-            return meta
+            return meta, dict(o=o, lse=lse, hash=hh, idx=ii)
     else:
         raise SystemExit(f"--workload {wid}: choose 2, 3, 5 (4 is the default benchmark line)")
+    return w, step, calls, dense_in
 
+
+
+def bench_workload(scfa, torch, wid, args):
+    """One benchmark line for workload 2 (Hash-sparse forward, 8k tokens), 3 (QK-sparse training step with
+    30 % of the tokens dropped, 8k tokens) or 5 (50 % drop, then Hash-sparse forward, 1M tokens).  The step
+    runs every row of the hot path the workload has, from inputs resident in HBM:
+      2: LSH + sort of Q and K (one call over both), block lists, forward over the sorted view;
+      3: block lists, forward, dQ, dK/dV over the kept rows of the full-length Q, K, V, dO (read in place
+         at the kept positions, outputs written there), and the dropped positions' output rows cleared;
+      5: LSH + sort of the kept rows of the full-length Q and K (one call, rows read in place), block lists,
+         the forward reading Q, K, V at the kept positions and writing O there, and the dropped rows of O
+         cleared.
+    No kept row is copied into a compact tensor: positions double as row indices into the inputs.
+    The dense-causal comparator is the same library's dense mode on the original [B,H,T,d] tensors."""
+    w, step, calls, dense_in = workload_setup(scfa, torch, wid)
+    blk, sc = w.block, w.scale
     steps = args.steps if wid != 5 else max(3, min(args.steps, 5))
     warm = _warm(torch, step, args.warmup if wid != 5 else 1, SETTLE_MS)
     _log(f"[bench] timing {steps} steps")
     timer = Timer(torch, calls)
     t0 = time.perf_counter()
     for _ in range(steps):
-        meta = step(timer)
+        meta, _ = step(timer)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) / steps * 1e3
     timer.collect()
@@ -854,11 +874,10 @@ def bench_workload(scfa, torch, wid, args):
                                                              nd, 1, dcalls)
     nblk = (w.T + blk - 1) // blk
 
-    kern = {"fwd": (f"k_fwd_bf16_ks<{'kQK' if w.mode == 'qk' else 'kHash'},{w.d},{blk},"
-                    f"{'false' if wid == 3 else 'true'}>", 4.0 * units * w.d)}
+    kern = {"fwd": (f"k_fwd_bf16_ks<{'kQK' if w.mode == 'qk' else 'kHash'},{w.d},{blk},true>", 4.0 * units * w.d)}
     if w.train:
-        kern["bwd_dq"] = (f"k_bwd_dq_bf16<kQK,{w.d},{blk},false>", 2.0 * units * w.d)
-        kern["bwd_dkdv"] = (f"k_bwd_dkdv_bf16<kQK,{w.d},{blk},false,false>", 8.0 * units * w.d)
+        kern["bwd_dq"] = (f"k_bwd_dq_bf16<kQK,{w.d},{blk},true>", 2.0 * units * w.d)
+        kern["bwd_dkdv"] = (f"k_bwd_dkdv_bf16<kQK,{w.d},{blk},true,false>", 8.0 * units * w.d)
     dominant = max(kern, key=lambda n: per_call[n])
     out = {
         "metric": "effective TFLOP/s (executed tiles, % bf16 MFMA peak) + speedup vs dense causal",

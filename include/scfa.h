@@ -212,6 +212,13 @@ size_t scfa_noalloc_scratch_bytes(void);
  *   x [B,H,T,d] (dtype) in any row order; idx [B,H,T] int32 original positions
  *   of the rows (NULL = 0..T-1); R [H,d,n_buckets/2] float32, one random
  *   rotation per head shared by the batch.
+ *   x_rows (nullable) [B,H,T] int32 and T_x: token t of sequence (b,h) is row
+ *   x_rows[b,h,t] (clamped into [0, T_x)) of an x of T_x rows per head, e.g.
+ *   the kept tokens of a full-length tensor after dropping ("1. QK-Sparse":
+ *   kept tokens keep their original positions), read without compacting it.
+ *   NULL: token t is row t and T_x must be 0 or T.  With x_rows, x_sorted and
+ *   companion must be NULL (SCFA_ERR_UNSUPPORTED).  B*H*T*d < 2^31 always;
+ *   x itself may hold up to 2^40 elements (its rows are addressed in 64 bits).
  *   bucket(x) = first index of the maximum of [x.R, -x.R], where each x.R[:,c]
  *   is accumulated in float64 in increasing coordinate order (products of a
  *   bf16/fp32 by an fp32 are exact in float64, so the result is bit-exact and
@@ -225,8 +232,8 @@ size_t scfa_noalloc_scratch_bytes(void);
  *   (e.g. V with K's order, or dO with Q's order).
  *   flags: SCFA_FLAG_IDX_ASCENDING as above (implied when idx is NULL).
  */
-int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int n_buckets,
-                         int B, int H, int T, int d, int dtype, unsigned flags,
+int scfa_lsh_bucket_sort(const void *x, const int32_t *x_rows, int T_x, const int32_t *idx, const float *R,
+                         int n_buckets, int B, int H, int T, int d, int dtype, unsigned flags,
                          int32_t *hash_sorted, int32_t *idx_sorted, int32_t *perm,
                          void *x_sorted, const void *companion, void *companion_sorted,
                          void *workspace, size_t workspace_bytes, void *stream);
@@ -300,15 +307,23 @@ int scfa_block_meta_exact(const int32_t *q_idx, const int32_t *k_idx,
  *   permutation of scfa_lsh_bucket_sort) without copying Q, K, V and dO into
  *   that order.  Positions, buckets, lse, o (the forward's output, read by
  *   the dq call), delta and every output stay indexed by the view's rows i
- *   and j.  Indices are clamped into [0, Tq) / [0, Tk) on the device (an
- *   index out of range reads a wrong row, never outside the tensor).  fp32
- *   with row indirection is SCFA_ERR_UNSUPPORTED.
+ *   and j.  fp32 with row indirection is SCFA_ERR_UNSUPPORTED.
+ *   Tq_src, Tk_src: rows per head of q (and dout) and of k (and v), the
+ *   tensors q_rows / k_rows index; 0 means Tq / Tk.  Other values need the
+ *   matching rows array: with dropped tokens ("1. QK-Sparse": the kept
+ *   tokens keep their original positions) the view is the Tq kept queries
+ *   and q_rows = q_idx reads them from the full-length q of Tq_src rows, so
+ *   the kept rows are never copied into compact tensors.  Indices are clamped
+ *   into [0, Tq_src) / [0, Tk_src) on the device (an index out of range reads
+ *   a wrong row, never outside the tensor).  With SCFA_FLAG_ORIG_ROWS the
+ *   outputs (and the backward's o / lse inputs) have Tq_src (dk, dv: Tk_src)
+ *   rows per head; rows that no q_rows (k_rows) entry names are not written.
  *   Other arguments, layouts and flags as in scfa_*_sparse_fwd / _bwd.
  */
 int scfa_attn_fwd_lists(const void *q, const void *k, const void *v,
                         const int32_t *q_idx, const int32_t *k_idx,
                         const int32_t *q_hash, const int32_t *k_hash,
-                        const int32_t *q_rows, const int32_t *k_rows,
+                        const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                         const int32_t *row_count, const int32_t *row_list,
                         void *o, float *lse,
                         int B, int H, int Tq, int Tk, int d, int block, float scale,
@@ -321,7 +336,7 @@ int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v,
                            const void *o, const float *lse, const void *dout,
                            const int32_t *q_idx, const int32_t *k_idx,
                            const int32_t *q_hash, const int32_t *k_hash,
-                           const int32_t *q_rows, const int32_t *k_rows,
+                           const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                            const int32_t *row_count, const int32_t *row_list,
                            void *dq, float *delta,
                            int B, int H, int Tq, int Tk, int d, int block, float scale,
@@ -334,7 +349,7 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v,
                              const float *lse, const void *dout, const float *delta,
                              const int32_t *q_idx, const int32_t *k_idx,
                              const int32_t *q_hash, const int32_t *k_hash,
-                             const int32_t *q_rows, const int32_t *k_rows,
+                             const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                              const int32_t *col_count, const int32_t *col_list,
                              void *dk, void *dv,
                              int B, int H, int Tq, int Tk, int d, int block, float scale,
@@ -438,9 +453,9 @@ int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list,
 /* Backward preprocess: delta [2,B,H,Tq] float32 = (rowsum(dout * o),
  * lse * log2(e)), as scfa_attn_bwd_dq_lists writes it.  o and lse are the
  * forward's outputs (view rows; the caller's rows with SCFA_FLAG_ORIG_ROWS,
- * the only flag), dout [B,H,Tq,d] bf16, read through q_rows when non-NULL
- * (as in the list entry points). */
-int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows,
+ * the only flag), dout [B,H,Tq_src,d] bf16, read through q_rows when non-NULL
+ * (as in the list entry points; Tq_src 0 means Tq). */
+int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows, int Tq_src,
                        float *delta, int B, int H, int Tq, int d, int dtype, unsigned flags, void *stream);
 
 /* dK, dV as scfa_attn_bwd_dkdv_lists (reading delta from scfa_attn_bwd_prep),
@@ -450,7 +465,7 @@ int scfa_attn_bwd_dkdv_ds_lists(const void *q, const void *k, const void *v,
                                 const float *lse, const void *dout, const float *delta,
                                 const int32_t *q_idx, const int32_t *k_idx,
                                 const int32_t *q_hash, const int32_t *k_hash,
-                                const int32_t *q_rows, const int32_t *k_rows,
+                                const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                                 const int32_t *col_count, const int32_t *col_list,
                                 const int32_t *col_base, void *ds, long long ds_tiles,
                                 void *dk, void *dv,
@@ -465,7 +480,7 @@ int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v,
                               const void *o, const float *lse, const void *dout,
                               const int32_t *q_idx, const int32_t *k_idx,
                               const int32_t *q_hash, const int32_t *k_hash,
-                              const int32_t *q_rows, const int32_t *k_rows,
+                              const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                               const int32_t *row_count, const int32_t *row_list,
                               const int32_t *row_slot, const int32_t *col_base,
                               const void *ds, long long ds_tiles,
@@ -500,6 +515,18 @@ int scfa_gather_rows(const void *src, const int32_t *index, void *dst,
                      int B, int H, int T_src, int T_dst, int d, int dtype, void *stream);
 int scfa_scatter_rows(const void *src, const int32_t *index, void *dst,
                       int B, int H, int T_src, int T_dst, int d, int dtype, unsigned flags, void *stream);
+
+/*
+ * Row clear: dst[b,h,index[b,h,i],:] = 0 for i < n.  dst [B,H,T,d], index
+ * [B,H,n] int32; indices outside [0, T) are skipped.  With attention that
+ * reads the kept rows of full-length tensors in place and writes its outputs
+ * at the kept positions (q_rows / k_rows with Tq_src / Tk_src and
+ * SCFA_FLAG_ORIG_ROWS), this gives the dropped positions ("1. QK-Sparse":
+ * dropped tokens take no part) their zero rows, with index = the dropped
+ * positions, so no output is compacted or scattered.  dtype, d, B*H and
+ * alignment limits as for scfa_gather_rows; no workspace.
+ */
+int scfa_zero_rows(void *dst, const int32_t *index, int B, int H, int n, int T, int d, int dtype, void *stream);
 
 /*
  * Bytes of workspace an operation needs (0 for invalid arguments).  For the

@@ -12,7 +12,9 @@ rows.  Definitions, per (b, h), written as plain loops over rows:
   [0, T_src);
 * scatter: dst[index[i]] = src[i] for index[i] in [0, T_dst), other rows
   dropped; destination rows no index names keep their previous value, or
-  are zero with ``zero_fill``.
+  are zero with ``zero_fill``;
+* zero rows: dst[index[i]] = 0 for index[i] in [0, T), other indices
+  skipped (the rows of dropped tokens in a full-length output).
 """
 
 from __future__ import annotations
@@ -51,3 +53,16 @@ def scatter_rows(src: np.ndarray, index: np.ndarray, T_dst: int, zero_fill: bool
                 if 0 <= j < T_dst:
                     dst[b, h, j] = src[b, h, i]
     return dst
+
+
+def zero_rows(dst: np.ndarray, index: np.ndarray) -> np.ndarray:
+    """A copy of dst [B, H, T, d] with rows index[b, h, i] (index [B, H, n]) set to zero."""
+    B, H, T, d = dst.shape
+    out = np.array(dst, copy=True)
+    for b in range(B):
+        for h in range(H):
+            for i in range(index.shape[2]):
+                j = int(index[b, h, i])
+                if 0 <= j < T:
+                    out[b, h, j] = 0
+    return out

@@ -207,19 +207,25 @@ def noalloc_scratch_bytes() -> int:
 
 
 def lsh_bucket_sort(x, R, n_buckets, idx=None, companion=None, *, idx_ascending=False, want_x=True,
-                    workspace=None):
+                    workspace=None, x_rows=None):
     """Bucket ids of x's rows and their (bucket, idx) order.
 
     Returns (hash_sorted, idx_sorted, perm, x_sorted, companion_sorted); the last
-    two are None when not requested.
+    two are None when not requested.  ``x_rows`` (int32 [B,H,T]) makes token t of
+    each sequence row x_rows[t] of x, whose length may differ (e.g. the kept tokens
+    of full-length tensors); x_sorted and companion are then unavailable.
     """
     if x.dim() != 4:
         raise ValueError("x must be [B, H, T, d]")
-    B, H, T, d = x.shape
+    B, H, Tx, d = x.shape
+    T = x_rows.shape[2] if x_rows is not None else Tx
     _need(x, "x")
+    _need(x_rows, "x_rows", torch.int32, (B, H, T))
     _need(R, "R", torch.float32, (H, d, n_buckets // 2))
     _need(idx, "idx", torch.int32, (B, H, T))
     _need(companion, "companion", x.dtype, x.shape)
+    if x_rows is not None and (want_x or companion is not None):
+        raise ValueError("x_rows: pass want_x=False and no companion (gather the rows instead)")
     hs = torch.empty((B, H, T), dtype=torch.int32, device=x.device)
     ids = torch.empty_like(hs)
     perm = torch.empty_like(hs)
@@ -227,9 +233,9 @@ def lsh_bucket_sort(x, R, n_buckets, idx=None, companion=None, *, idx_ascending=
     cs = torch.empty_like(companion) if companion is not None else None
     ws, nws = _workspace(_lib.OP_LSH_SORT, B, H, T, 0, d, 0, x.device, n_buckets=n_buckets, workspace=workspace)
     flags = _lib.FLAG_IDX_ASCENDING if idx_ascending else 0
-    rc = _LIB.scfa_lsh_bucket_sort(_ptr(x), _ptr(idx), _ptr(R), n_buckets, B, H, T, d, _dtype_code(x), flags,
-                                   _ptr(hs), _ptr(ids), _ptr(perm), _ptr(xs), _ptr(companion), _ptr(cs),
-                                   _ptr(ws), nws, _stream())
+    rc = _LIB.scfa_lsh_bucket_sort(_ptr(x), _ptr(x_rows), Tx, _ptr(idx), _ptr(R), n_buckets, B, H, T, d,
+                                   _dtype_code(x), flags, _ptr(hs), _ptr(ids), _ptr(perm), _ptr(xs),
+                                   _ptr(companion), _ptr(cs), _ptr(ws), nws, _stream())
     _lib.check("scfa_lsh_bucket_sort", rc)
     return hs, ids, perm, xs, cs
 
@@ -281,30 +287,52 @@ def _list_args(meta, key_cnt, key_list):
     return meta[key_cnt], meta[key_list]
 
 
-def _rows_args(q_rows, k_rows, q, k):
-    B, H, Tq = q.shape[:3]
+def _view_shapes(q, k, v, q_rows, k_rows):
+    """(B, H, Tq, Tk, d, Tq_src, Tk_src): the attention's view has Tq queries and Tk keys (the lengths
+    of q_rows / k_rows when given, else of q / k); q (dout) and k, v hold Tq_src and Tk_src rows per head."""
+    B, H, Tqs, Tks, d = _attn_shapes(q, k, v)
+    Tq = q_rows.shape[2] if q_rows is not None else Tqs
+    Tk = k_rows.shape[2] if k_rows is not None else Tks
     _need(q_rows, "q_rows", torch.int32, (B, H, Tq))
-    _need(k_rows, "k_rows", torch.int32, (B, H, k.shape[2]))
-    return _ptr(q_rows), _ptr(k_rows)
+    _need(k_rows, "k_rows", torch.int32, (B, H, Tk))
+    return B, H, Tq, Tk, d, Tqs, Tks
+
+
+def _rows_args(q_rows, k_rows, Tqs, Tks):
+    return _ptr(q_rows), _ptr(k_rows), Tqs, Tks
+
+
+def _out_rows(flags, T_view, T_src):
+    """Rows per head of an output: the caller's tensor length with FLAG_ORIG_ROWS, else the view's."""
+    return T_src if int(flags) & _lib.FLAG_ORIG_ROWS else T_view
+
+
+def _kv_grads(k, flags, Tk, Tks):
+    B, H, _, d = k.shape
+    shape = (B, H, _out_rows(flags, Tk, Tks), d)
+    return torch.empty(shape, dtype=k.dtype, device=k.device), torch.empty(shape, dtype=k.dtype, device=k.device)
 
 
 def attn_fwd_lists(q, k, v, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None, flags=0, out=None,
                    q_rows=None, k_rows=None):
     """Forward over lists from ``block_meta`` (one kernel).  Positions None = dense causal.
 
-    ``out`` optionally supplies preallocated (o, lse).  ``q_rows`` / ``k_rows`` (int32 [B,H,T]) make
-    row i of the attention's Q row q_rows[i] of q and row j of K, V row k_rows[j] of k, v (a
-    reordered view without copies; outputs indexed by the view's rows).
+    ``out`` optionally supplies preallocated (o, lse).  ``q_rows`` / ``k_rows`` (int32 [B,H,Tq] /
+    [B,H,Tk]) make row i of the attention's Q row q_rows[i] of q and row j of K, V row k_rows[j] of
+    k, v: a reordered view without copies, or, with q and k longer than the view, the kept rows of
+    full-length tensors read in place.  Outputs are indexed by the view's rows, or with
+    FLAG_ORIG_ROWS by q's rows (rows no q_rows entry names are left unwritten).
     """
-    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    B, H, Tq, Tk, d, Tqs, Tks = _view_shapes(q, k, v, q_rows, k_rows)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o, lse = out if out is not None else (torch.empty_like(q),
-                                          torch.empty((B, H, Tq), dtype=torch.float32, device=q.device))
+    To = _out_rows(flags, Tq, Tqs)
+    o, lse = out if out is not None else (torch.empty((B, H, To, d), dtype=q.dtype, device=q.device),
+                                          torch.empty((B, H, To), dtype=torch.float32, device=q.device))
     rc_, rl_ = _list_args(meta, "row_count", "row_list")
     rc = _LIB.scfa_attn_fwd_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
-                                  *_rows_args(q_rows, k_rows, q, k), _ptr(rc_), _ptr(rl_), _ptr(o), _ptr(lse), B, H,
-                                  Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags), _stream())
+                                  *_rows_args(q_rows, k_rows, Tqs, Tks), _ptr(rc_), _ptr(rl_), _ptr(o), _ptr(lse),
+                                  B, H, Tq, Tk, d, block, float(scale), _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_fwd_lists", rc)
     return o, lse
 
@@ -313,14 +341,15 @@ def attn_bwd_dq_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta,
                       out=None, q_rows=None, k_rows=None):
     """dQ over row lists (one kernel).  Returns (dq, delta) with delta [2,B,H,Tq] float32 scratch
     (rowsum(dout * o), lse * log2 e) for attn_bwd_dkdv_lists."""
-    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    B, H, Tq, Tk, d, Tqs, Tks = _view_shapes(q, k, v, q_rows, k_rows)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, delta = out if out is not None else (torch.empty_like(q),
-                                             torch.empty((2, B, H, Tq), dtype=torch.float32, device=q.device))
+    dq, delta = out if out is not None else (
+        torch.empty((B, H, _out_rows(flags, Tq, Tqs), d), dtype=q.dtype, device=q.device),
+        torch.empty((2, B, H, Tq), dtype=torch.float32, device=q.device))
     rc_, rl_ = _list_args(meta, "row_count", "row_list")
     rc = _LIB.scfa_attn_bwd_dq_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_idx),
-                                     _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, q, k),
+                                     _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, Tqs, Tks),
                                      _ptr(rc_), _ptr(rl_), _ptr(dq), _ptr(delta), B, H, Tq, Tk, d, block, float(scale),
                                      _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_bwd_dq_lists", rc)
@@ -330,13 +359,13 @@ def attn_bwd_dq_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, meta,
 def attn_bwd_dkdv_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash, meta, *, block=64, scale=None,
                         flags=0, out=None, q_rows=None, k_rows=None):
     """dK and dV over column lists (one kernel), reading delta from attn_bwd_dq_lists."""
-    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    B, H, Tq, Tk, d, Tqs, Tks = _view_shapes(q, k, v, q_rows, k_rows)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dk, dv = out if out is not None else (torch.empty_like(k), torch.empty_like(v))
+    dk, dv = out if out is not None else _kv_grads(k, flags, Tk, Tks)
     cc_, cl_ = _list_args(meta, "col_count", "col_list")
     rc = _LIB.scfa_attn_bwd_dkdv_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta), _ptr(q_idx),
-                                       _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, q, k),
+                                       _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, Tqs, Tks),
                                        _ptr(cc_), _ptr(cl_), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, block,
                                        float(scale), _dtype_code(q), int(flags), _stream())
     _lib.check("scfa_attn_bwd_dkdv_lists", rc)
@@ -470,14 +499,18 @@ def ds_buffer(n_tiles, block=64, device="cuda"):
 
 def attn_bwd_prep(o, lse, dout, *, q_rows=None, out=None, flags=0):
     """delta [2,B,H,Tq] float32 = (rowsum(dout * o), lse * log2 e) (scfa_attn_bwd_prep); flags may hold
-    FLAG_ORIG_ROWS (o and lse at the caller's rows)."""
-    B, H, Tq, d = o.shape
-    _need(o, "o", torch.bfloat16)
-    _need(dout, "dout", torch.bfloat16, o.shape)
-    _need(lse, "lse", torch.float32, (B, H, Tq))
+    FLAG_ORIG_ROWS (o and lse at the caller's rows).  dout [B,H,Tq_src,d] is read through q_rows."""
+    if dout.dim() != 4:
+        raise ValueError("dout must be [B, H, T, d]")
+    B, H, Tqs, d = dout.shape
+    Tq = q_rows.shape[2] if q_rows is not None else Tqs
+    To = _out_rows(flags, Tq, Tqs)
+    _need(dout, "dout", torch.bfloat16)
+    _need(o, "o", torch.bfloat16, (B, H, To, d))
+    _need(lse, "lse", torch.float32, (B, H, To))
     _need(q_rows, "q_rows", torch.int32, (B, H, Tq))
     delta = out if out is not None else torch.empty((2, B, H, Tq), dtype=torch.float32, device=o.device)
-    rc = _LIB.scfa_attn_bwd_prep(_ptr(o), _ptr(lse), _ptr(dout), _ptr(q_rows), _ptr(delta), B, H, Tq, d,
+    rc = _LIB.scfa_attn_bwd_prep(_ptr(o), _ptr(lse), _ptr(dout), _ptr(q_rows), Tqs, _ptr(delta), B, H, Tq, d,
                                  _dtype_code(o), int(flags), _stream())
     _lib.check("scfa_attn_bwd_prep", rc)
     return delta
@@ -486,14 +519,14 @@ def attn_bwd_prep(o, lse, dout, *, q_rows=None, out=None, flags=0):
 def attn_bwd_dkdv_ds_lists(q, k, v, lse, dout, delta, q_idx, k_idx, q_hash, k_hash, meta, ds, *, block=64,
                            scale=None, flags=0, out=None, q_rows=None, k_rows=None):
     """dK, dV over column lists, storing every live tile's dS in ``ds`` (needs tile_slots(meta))."""
-    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    B, H, Tq, Tk, d, Tqs, Tks = _view_shapes(q, k, v, q_rows, k_rows)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _need(ds, "ds", torch.bfloat16)
-    dk, dv = out if out is not None else (torch.empty_like(k), torch.empty_like(v))
+    dk, dv = out if out is not None else _kv_grads(k, flags, Tk, Tks)
     rc = _LIB.scfa_attn_bwd_dkdv_ds_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
                                           _ptr(q_idx), _ptr(k_idx), _ptr(q_hash), _ptr(k_hash),
-                                          *_rows_args(q_rows, k_rows, q, k), _ptr(meta["col_count"]),
+                                          *_rows_args(q_rows, k_rows, Tqs, Tks), _ptr(meta["col_count"]),
                                           _ptr(meta["col_list"]), _ptr(meta["col_base"]), _ptr(ds),
                                           ds.shape[0] if ds.dim() == 3 else 0, _ptr(dk), _ptr(dv), B, H, Tq, Tk, d,
                                           block, float(scale), _dtype_code(q), int(flags), _stream())
@@ -505,13 +538,14 @@ def attn_bwd_dq_ds_lists(q, k, v, o, lse, dout, q_idx, k_idx, q_hash, k_hash, me
                          scale=None, flags=0, out=None, q_rows=None, k_rows=None):
     """dQ from the stored dS tiles (after attn_bwd_dkdv_ds_lists); falls back to recomputing when the
     buffer was too small for every live tile."""
-    B, H, Tq, Tk, d = _attn_shapes(q, k, v)
+    B, H, Tq, Tk, d, Tqs, Tks = _view_shapes(q, k, v, q_rows, k_rows)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _need(ds, "ds", torch.bfloat16)
-    dq = out if out is not None else torch.empty_like(q)
+    dq = out if out is not None else torch.empty((B, H, _out_rows(flags, Tq, Tqs), d), dtype=q.dtype,
+                                                 device=q.device)
     rc = _LIB.scfa_attn_bwd_dq_ds_lists(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(q_idx),
-                                        _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, q, k),
+                                        _ptr(k_idx), _ptr(q_hash), _ptr(k_hash), *_rows_args(q_rows, k_rows, Tqs, Tks),
                                         _ptr(meta["row_count"]), _ptr(meta["row_list"]), _ptr(meta["row_slot"]),
                                         _ptr(meta["col_base"]), _ptr(ds), ds.shape[0] if ds.dim() == 3 else 0,
                                         _ptr(dq), _ptr(delta), B, H, Tq, Tk, d, block, float(scale),
@@ -536,6 +570,21 @@ def gather_rows(src, index, *, out=None):
     dst = out if out is not None else torch.empty((B, H, Td, d), dtype=src.dtype, device=src.device)
     rc = _LIB.scfa_gather_rows(_ptr(src), _ptr(index), _ptr(dst), B, H, Ts, Td, d, _dtype_code(src), _stream())
     _lib.check("scfa_gather_rows", rc)
+    return dst
+
+
+def zero_rows(dst, index):
+    """dst[b, h, index[b, h, i]] = 0 in place (out-of-range indices skipped); returns dst.
+
+    Clears the dropped positions of full-length outputs whose kept rows the attention wrote in place
+    (FLAG_ORIG_ROWS with full-length q, k, v).  dst [B,H,T,d]; index [B,H,n] int32.
+    """
+    B, H, T, d = dst.shape
+    _need(dst, "dst")
+    n = index.shape[2]
+    _need(index, "index", torch.int32, (B, H, n))
+    rc = _LIB.scfa_zero_rows(_ptr(dst), _ptr(index), B, H, n, T, d, _dtype_code(dst), _stream())
+    _lib.check("scfa_zero_rows", rc)
     return dst
 
 

@@ -37,6 +37,7 @@ EXPORTED = (
     "scfa_attn_bwd_dq_ds_lists",
     "scfa_gather_rows",
     "scfa_scatter_rows",
+    "scfa_zero_rows",
     "scfa_workspace_size",
     "scfa_last_error",
 )
@@ -80,22 +81,23 @@ _SIGNATURES = {
     "scfa_hash_sparse_bwd": [_p] * 13 + _ATTN_TAIL,
     "scfa_hash_sparse_fwd_noalloc": [_p] * 9 + _LISTS_TAIL,
     "scfa_noalloc_scratch_bytes": [],
-    "scfa_lsh_bucket_sort": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+    "scfa_lsh_bucket_sort": [_p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_block_meta": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p],
     "scfa_block_meta_exact": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
-    "scfa_attn_fwd_lists": [_p] * 13 + _LISTS_TAIL,
-    "scfa_attn_bwd_dq_lists": [_p] * 16 + _LISTS_TAIL,
-    "scfa_attn_bwd_dkdv_lists": [_p] * 16 + _LISTS_TAIL,
+    "scfa_attn_fwd_lists": [_p] * 9 + [_i, _i] + [_p] * 4 + _LISTS_TAIL,
+    "scfa_attn_bwd_dq_lists": [_p] * 12 + [_i, _i] + [_p] * 4 + _LISTS_TAIL,
+    "scfa_attn_bwd_dkdv_lists": [_p] * 12 + [_i, _i] + [_p] * 4 + _LISTS_TAIL,
     "scfa_block_meta_varlen": [_p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
     "scfa_attn_fwd_varlen": [_p, _p, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p] + _LISTS_TAIL,
     "scfa_attn_bwd_dq_varlen": [_p] * 8 + [_i, _i] + [_p] * 8 + _LISTS_TAIL,
     "scfa_attn_bwd_dkdv_varlen": [_p] * 8 + [_i, _i] + [_p] * 8 + _LISTS_TAIL,
     "scfa_tile_slots": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p],
-    "scfa_attn_bwd_prep": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _u, _p],
-    "scfa_attn_bwd_dkdv_ds_lists": [_p] * 16 + [_i64] + [_p, _p] + _LISTS_TAIL,
-    "scfa_attn_bwd_dq_ds_lists": [_p] * 17 + [_i64] + [_p, _p] + _LISTS_TAIL,
+    "scfa_attn_bwd_prep": [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _u, _p],
+    "scfa_attn_bwd_dkdv_ds_lists": [_p] * 12 + [_i, _i] + [_p] * 4 + [_i64] + [_p, _p] + _LISTS_TAIL,
+    "scfa_attn_bwd_dq_ds_lists": [_p] * 12 + [_i, _i] + [_p] * 5 + [_i64] + [_p, _p] + _LISTS_TAIL,
     "scfa_gather_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p],
     "scfa_scatter_rows": [_p, _p, _p, _i, _i, _i, _i, _i, _i, _u, _p],
+    "scfa_zero_rows": [_p, _p, _i, _i, _i, _i, _i, _i, _p],
     "scfa_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],
     "scfa_last_error": [],
 }

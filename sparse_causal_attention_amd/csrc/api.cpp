@@ -107,6 +107,7 @@ struct AttnCall {
   const int32_t *q_idx, *k_idx, *q_hash, *k_hash;
   const int32_t *row_cnt, *row_list, *col_cnt, *col_list;  // list entry points only
   const int32_t *q_rows, *k_rows;                          // list entry points only (nullable)
+  int Tq_src, Tk_src;  // rows per head of q / dout and of k / v (list entry points; 0 = Tq, Tk)
   void *out_o;
   float *out_lse;
   void *dq, *dk, *dv;
@@ -144,11 +145,24 @@ int attention(const AttnCall &c) {
       return fail(SCFA_ERR_INVALID_ARGUMENT, "packed row counts must be >= 0 and rows*d < 2^31");
     if (c.q_rows || c.k_rows || c.ds_path) return fail(SCFA_ERR_UNSUPPORTED, "ragged heads: no row indirection or stored dS");
   }
+  // Rows per head of the caller's tensors: the view's Tq, Tk unless row indirection reads tensors of
+  // another length (q / dout: Tqs, k / v: Tks); the outputs follow them with SCFA_FLAG_ORIG_ROWS.
+  const bool orig_rows = (c.flags & SCFA_FLAG_ORIG_ROWS) != 0;
+  const int Tqs = c.Tq_src > 0 ? c.Tq_src : s.Tq, Tks = c.Tk_src > 0 ? c.Tk_src : s.Tk;
+  if (c.Tq_src < 0 || c.Tk_src < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "Tq_src and Tk_src must be >= 0");
+  if ((c.q_rows == nullptr && Tqs != s.Tq) || (c.k_rows == nullptr && Tks != s.Tk))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "Tq_src / Tk_src other than Tq / Tk need q_rows / k_rows");
+  if ((long long)s.B * s.H * (Tqs > Tks ? Tqs : Tks) * s.d >= (1ll << 31))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*max(Tq_src,Tk_src)*d must be < 2^31");
+  const int Tqo = orig_rows ? Tqs : s.Tq, Tko = orig_rows ? Tks : s.Tk;
   const long long rowsQ = varlen ? c.total_q : BH * s.Tq, rowsK = varlen ? c.total_k : BH * s.Tk;
-  const long long nQ = rowsQ * s.d, nK = rowsK * s.d;
   const long long nQi = rowsQ, nKi = rowsK;
+  // element counts of the caller's inputs (s) and of the outputs (o)
+  const long long nQs = (varlen ? c.total_q : BH * Tqs) * s.d, nKs = (varlen ? c.total_k : BH * Tks) * s.d;
+  const long long nQoi = varlen ? c.total_q : BH * Tqo, nKo = (varlen ? c.total_k : BH * Tko) * s.d;
+  const long long nQo = nQoi * s.d;
   const int nq = nblocks(s.Tq, s.block), nk = nblocks(s.Tk, s.block);
-  if ((rc = check_ptr(c.q, nQ, 16, "q")) || (rc = check_ptr(c.k, nK, 16, "k")) || (rc = check_ptr(c.v, nK, 16, "v")))
+  if ((rc = check_ptr(c.q, nQs, 16, "q")) || (rc = check_ptr(c.k, nKs, 16, "k")) || (rc = check_ptr(c.v, nKs, 16, "v")))
     return rc;
   // Positions and buckets.  A pointer may be NULL when its tensor is empty
   // (T == 0): torch hands out NULL for empty tensors.
@@ -169,21 +183,21 @@ int attention(const AttnCall &c) {
   // tensors of each kind
   switch (c.kind) {
     case kFwd:
-      if ((rc = check_ptr(c.out_o, nQ, 16, "o")) || (rc = check_ptr(c.out_lse, nQi, 4, "lse"))) return rc;
+      if ((rc = check_ptr(c.out_o, nQo, 16, "o")) || (rc = check_ptr(c.out_lse, nQoi, 4, "lse"))) return rc;
       break;
     case kBwdAll:
     case kBwdDq:
-      if ((rc = check_ptr(c.o, nQ, 16, "o")) || (rc = check_ptr(c.lse, nQi, 4, "lse")) ||
-          (rc = check_ptr(c.dout, nQ, 16, "dout")) || (rc = check_ptr(c.dq, nQ, 16, "dq")))
+      if ((rc = check_ptr(c.o, nQo, 16, "o")) || (rc = check_ptr(c.lse, nQoi, 4, "lse")) ||
+          (rc = check_ptr(c.dout, nQs, 16, "dout")) || (rc = check_ptr(c.dq, nQo, 16, "dq")))
         return rc;
-      if (c.kind == kBwdAll && ((rc = check_ptr(c.dk, nK, 16, "dk")) || (rc = check_ptr(c.dv, nK, 16, "dv"))))
+      if (c.kind == kBwdAll && ((rc = check_ptr(c.dk, nKo, 16, "dk")) || (rc = check_ptr(c.dv, nKo, 16, "dv"))))
         return rc;
       if (c.kind == kBwdDq && (rc = check_ptr(c.delta, 2 * nQi, 4, "delta"))) return rc;
       break;
     case kBwdDkdv:
-      if ((rc = check_ptr(c.lse, nQi, 4, "lse")) || (rc = check_ptr(c.dout, nQ, 16, "dout")) ||
-          (rc = check_ptr(c.delta, 2 * nQi, 4, "delta")) || (rc = check_ptr(c.dk, nK, 16, "dk")) ||
-          (rc = check_ptr(c.dv, nK, 16, "dv")))
+      if ((rc = check_ptr(c.lse, nQoi, 4, "lse")) || (rc = check_ptr(c.dout, nQs, 16, "dout")) ||
+          (rc = check_ptr(c.delta, 2 * nQi, 4, "delta")) || (rc = check_ptr(c.dk, nKo, 16, "dk")) ||
+          (rc = check_ptr(c.dv, nKo, 16, "dv")))
         return rc;
       break;
   }
@@ -195,7 +209,6 @@ int attention(const AttnCall &c) {
       return rc;
   }
   const bool no_prune = (c.flags & SCFA_FLAG_NO_PRUNE) != 0;
-  const bool orig_rows = (c.flags & SCFA_FLAG_ORIG_ROWS) != 0;
   if (orig_rows && (c.q_rows == nullptr || c.k_rows == nullptr) && (nQi > 0 || nKi > 0))
     return fail(SCFA_ERR_INVALID_ARGUMENT, "SCFA_FLAG_ORIG_ROWS needs both q_rows and k_rows");
   if (c.ds_path) {
@@ -247,6 +260,10 @@ int attention(const AttnCall &c) {
   a.BH = (int)BH;
   a.Tq = s.Tq;
   a.Tk = s.Tk;
+  a.Tqs = Tqs;
+  a.Tks = Tks;
+  a.Tqo = Tqo;
+  a.Tko = Tko;
   a.nq = nq;
   a.nk = nk;
   a.d = s.d;
@@ -490,14 +507,14 @@ int scfa_hash_sparse_bwd(const void *q, const void *k, const void *v, const void
 }
 
 int scfa_attn_fwd_lists(const void *q, const void *k, const void *v, const int32_t *q_idx, const int32_t *k_idx,
-                        const int32_t *q_hash, const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                        const int32_t *q_hash, const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                         const int32_t *row_count, const int32_t *row_list, void *o, float *lse, int B, int H, int Tq,
                         int Tk, int d, int block, float scale, int dtype, unsigned flags, void *stream) {
   AttnCall c{};
   c.kind = kFwd;
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
-  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.q_rows = q_rows, c.k_rows = k_rows, c.Tq_src = Tq_src, c.Tk_src = Tk_src;
   c.row_cnt = row_count, c.row_list = row_list, c.out_o = o, c.out_lse = lse;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;
@@ -506,7 +523,7 @@ int scfa_attn_fwd_lists(const void *q, const void *k, const void *v, const int32
 
 int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v, const void *o, const float *lse,
                            const void *dout, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
-                           const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                           const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                            const int32_t *row_count, const int32_t *row_list, void *dq, float *delta, int B, int H,
                            int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags, void *stream) {
   AttnCall c{};
@@ -514,7 +531,7 @@ int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v, const vo
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
-  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.q_rows = q_rows, c.k_rows = k_rows, c.Tq_src = Tq_src, c.Tk_src = Tk_src;
   c.row_cnt = row_count, c.row_list = row_list, c.dq = dq, c.delta = delta;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;
@@ -523,7 +540,7 @@ int scfa_attn_bwd_dq_lists(const void *q, const void *k, const void *v, const vo
 
 int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v, const float *lse, const void *dout,
                              const float *delta, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
-                             const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                             const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                              const int32_t *col_count, const int32_t *col_list, void *dk, void *dv, int B, int H,
                              int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags, void *stream) {
   AttnCall c{};
@@ -531,7 +548,7 @@ int scfa_attn_bwd_dkdv_lists(const void *q, const void *k, const void *v, const 
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.lse = lse, c.dout = dout, c.delta = const_cast<float *>(delta);
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
-  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.q_rows = q_rows, c.k_rows = k_rows, c.Tq_src = Tq_src, c.Tk_src = Tk_src;
   c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
   c.flags = flags, c.stream = stream;
@@ -627,19 +644,24 @@ int scfa_tile_slots(const int32_t *row_count, const int32_t *row_list, const int
   return ok();
 }
 
-int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows, float *delta, int B,
-                       int H, int Tq, int d, int dtype, unsigned flags, void *stream) {
-  if (B < 1 || H < 1 || Tq < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq >= 0 required");
+int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const int32_t *q_rows, int Tq_src,
+                       float *delta, int B, int H, int Tq, int d, int dtype, unsigned flags, void *stream) {
+  if (B < 1 || H < 1 || Tq < 0 || Tq_src < 0)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H >= 1 and Tq, Tq_src >= 0 required");
   if (d != 64 && d != 128) return fail(SCFA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
   if (dtype != SCFA_DTYPE_BF16) return fail(SCFA_ERR_UNSUPPORTED, "scfa_attn_bwd_prep needs dtype bf16");
   if (flags & ~SCFA_FLAG_ORIG_ROWS) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
-  if ((flags & SCFA_FLAG_ORIG_ROWS) && q_rows == nullptr && B * H * (long long)Tq > 0)
+  const bool orig_rows = (flags & SCFA_FLAG_ORIG_ROWS) != 0;
+  if (orig_rows && q_rows == nullptr && B * H * (long long)Tq > 0)
     return fail(SCFA_ERR_INVALID_ARGUMENT, "SCFA_FLAG_ORIG_ROWS needs q_rows");
+  const int Tqs = Tq_src > 0 ? Tq_src : Tq, Tqo = orig_rows ? Tqs : Tq;
+  if (q_rows == nullptr && Tqs != Tq) return fail(SCFA_ERR_INVALID_ARGUMENT, "Tq_src other than Tq needs q_rows");
   const long long BH = (long long)B * H;
-  if (BH * Tq * d >= (1ll << 31)) return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*Tq*d must be < 2^31");
+  if (BH * (Tq > Tqs ? Tq : Tqs) * d >= (1ll << 31))
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*max(Tq,Tq_src)*d must be < 2^31");
   int rc;
-  if ((rc = check_ptr(o, BH * Tq * d, 16, "o")) || (rc = check_ptr(lse, BH * Tq, 4, "lse")) ||
-      (rc = check_ptr(dout, BH * Tq * d, 16, "dout")) || (rc = check_ptr(q_rows, q_rows ? BH * Tq : 0, 4, "q_rows")) ||
+  if ((rc = check_ptr(o, BH * Tqo * d, 16, "o")) || (rc = check_ptr(lse, BH * Tqo, 4, "lse")) ||
+      (rc = check_ptr(dout, BH * Tqs * d, 16, "dout")) || (rc = check_ptr(q_rows, q_rows ? BH * Tq : 0, 4, "q_rows")) ||
       (rc = check_ptr(delta, 2 * BH * Tq, 4, "delta")))
     return rc;
   scfa::AttnArgs a{};
@@ -650,9 +672,11 @@ int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const 
   a.delta = delta;
   a.BH = (int)BH;
   a.Tq = Tq;
+  a.Tqs = Tqs;
+  a.Tqo = Tqo;
   a.d = d;
   a.delta_half = BH * Tq;
-  a.orig_rows = (flags & SCFA_FLAG_ORIG_ROWS) ? 1 : 0;
+  a.orig_rows = orig_rows ? 1 : 0;
   const hipError_t e = scfa::launch_attn_bwd_prep(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward preprocess");
   return ok();
@@ -660,7 +684,7 @@ int scfa_attn_bwd_prep(const void *o, const float *lse, const void *dout, const 
 
 int scfa_attn_bwd_dkdv_ds_lists(const void *q, const void *k, const void *v, const float *lse, const void *dout,
                                 const float *delta, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
-                                const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                                const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                                 const int32_t *col_count, const int32_t *col_list, const int32_t *col_base, void *ds,
                                 long long ds_tiles, void *dk, void *dv, int B, int H, int Tq, int Tk, int d, int block,
                                 float scale, int dtype, unsigned flags, void *stream) {
@@ -669,7 +693,7 @@ int scfa_attn_bwd_dkdv_ds_lists(const void *q, const void *k, const void *v, con
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.lse = lse, c.dout = dout, c.delta = const_cast<float *>(delta);
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
-  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.q_rows = q_rows, c.k_rows = k_rows, c.Tq_src = Tq_src, c.Tk_src = Tk_src;
   c.col_cnt = col_count, c.col_list = col_list, c.dk = dk, c.dv = dv;
   c.ds_path = true, c.ds = ds, c.ds_tiles = ds_tiles, c.col_base = col_base;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
@@ -679,7 +703,7 @@ int scfa_attn_bwd_dkdv_ds_lists(const void *q, const void *k, const void *v, con
 
 int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v, const void *o, const float *lse,
                               const void *dout, const int32_t *q_idx, const int32_t *k_idx, const int32_t *q_hash,
-                              const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows,
+                              const int32_t *k_hash, const int32_t *q_rows, const int32_t *k_rows, int Tq_src, int Tk_src,
                               const int32_t *row_count, const int32_t *row_list, const int32_t *row_slot,
                               const int32_t *col_base, const void *ds, long long ds_tiles, void *dq, float *delta,
                               int B, int H, int Tq, int Tk, int d, int block, float scale, int dtype, unsigned flags,
@@ -689,7 +713,7 @@ int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v, const
   c.api = kApiLists;
   c.q = q, c.k = k, c.v = v, c.o = o, c.lse = lse, c.dout = dout;
   c.q_idx = q_idx, c.k_idx = k_idx, c.q_hash = q_hash, c.k_hash = k_hash;
-  c.q_rows = q_rows, c.k_rows = k_rows;
+  c.q_rows = q_rows, c.k_rows = k_rows, c.Tq_src = Tq_src, c.Tk_src = Tk_src;
   c.row_cnt = row_count, c.row_list = row_list, c.dq = dq, c.delta = delta;
   c.ds_path = true, c.ds = const_cast<void *>(ds), c.ds_tiles = ds_tiles, c.row_slot = row_slot, c.col_base = col_base;
   c.s = Shape{B, H, Tq, Tk, d, block, dtype, scale};
@@ -697,20 +721,27 @@ int scfa_attn_bwd_dq_ds_lists(const void *q, const void *k, const void *v, const
   return attention(c);
 }
 
-int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int n_buckets, int B, int H, int T, int d,
-                         int dtype, unsigned flags, int32_t *hash_sorted, int32_t *idx_sorted, int32_t *perm,
-                         void *x_sorted, const void *companion, void *companion_sorted, void *workspace,
-                         size_t workspace_bytes, void *stream) {
-  if (B < 1 || H < 1 || T < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H must be >= 1 and T >= 0");
+int scfa_lsh_bucket_sort(const void *x, const int32_t *x_rows, int T_x, const int32_t *idx, const float *R,
+                         int n_buckets, int B, int H, int T, int d, int dtype, unsigned flags, int32_t *hash_sorted,
+                         int32_t *idx_sorted, int32_t *perm, void *x_sorted, const void *companion,
+                         void *companion_sorted, void *workspace, size_t workspace_bytes, void *stream) {
+  if (B < 1 || H < 1 || T < 0 || T_x < 0) return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H must be >= 1 and T, T_x >= 0");
+  const int Tx = T_x > 0 ? T_x : T;
+  if (x_rows == nullptr && Tx != T) return fail(SCFA_ERR_INVALID_ARGUMENT, "T_x other than T needs x_rows");
+  if (x_rows && (x_sorted || companion))
+    return fail(SCFA_ERR_UNSUPPORTED, "x_rows: no x_sorted / companion copies (gather the rows instead)");
   if (d != 64 && d != 128) return fail(SCFA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
   if (dtype != SCFA_DTYPE_BF16 && dtype != SCFA_DTYPE_FP32) return fail(SCFA_ERR_UNSUPPORTED, "dtype=%d unsupported", dtype);
   if (n_buckets < 2 || n_buckets > 1024 || (n_buckets & 1))
     return fail(SCFA_ERR_UNSUPPORTED, "n_buckets=%d unsupported (even, 2..1024)", n_buckets);
   if (flags & ~SCFA_FLAG_IDX_ASCENDING) return fail(SCFA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
   if ((long long)B * H * T * d >= (1ll << 31)) return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*T*d must be < 2^31");
+  // rows of x are addressed in 64 bits (only the sequences' own arrays need 32-bit indices)
+  if ((long long)B * H * Tx * d >= (1ll << 40)) return fail(SCFA_ERR_INVALID_ARGUMENT, "B*H*T_x*d must be < 2^40");
   const long long nX = (long long)B * H * T * d, nI = (long long)B * H * T;
   int rc;
-  if ((rc = check_ptr(x, nX, 16, "x")) || (rc = check_ptr(idx, idx ? nI : 0, 4, "idx")) ||
+  if ((rc = check_ptr(x, (long long)B * H * Tx * d, 16, "x")) ||
+      (rc = check_ptr(x_rows, x_rows ? nI : 0, 4, "x_rows")) || (rc = check_ptr(idx, idx ? nI : 0, 4, "idx")) ||
       (rc = check_ptr(R, (long long)H * d * (n_buckets / 2), 4, "R")) ||
       (rc = check_ptr(hash_sorted, nI, 4, "hash_sorted")) || (rc = check_ptr(idx_sorted, nI, 4, "idx_sorted")) ||
       (rc = check_ptr(perm, nI, 4, "perm")))
@@ -726,6 +757,8 @@ int scfa_lsh_bucket_sort(const void *x, const int32_t *idx, const float *R, int 
 
   scfa::LshArgs a{};
   a.x = x;
+  a.x_rows = x_rows;
+  a.Tx = Tx;
   a.idx = idx;
   a.R = R;
   a.nb = n_buckets;
@@ -785,6 +818,24 @@ int scfa_gather_rows(const void *src, const int32_t *index, void *dst, int B, in
 int scfa_scatter_rows(const void *src, const int32_t *index, void *dst, int B, int H, int T_src, int T_dst, int d,
                       int dtype, unsigned flags, void *stream) {
   return rows_call(false, src, index, dst, B, H, T_src, T_dst, d, dtype, flags, stream);
+}
+int scfa_zero_rows(void *dst, const int32_t *index, int B, int H, int n, int T, int d, int dtype, void *stream) {
+  if (B < 1 || H < 1 || n < 0 || T < 0 || d < 1)
+    return fail(SCFA_ERR_INVALID_ARGUMENT, "B, H, d >= 1 and n, T >= 0 required");
+  if (dtype != SCFA_DTYPE_BF16 && dtype != SCFA_DTYPE_FP32) return fail(SCFA_ERR_UNSUPPORTED, "dtype=%d unsupported", dtype);
+  const int esize = dtype == SCFA_DTYPE_BF16 ? 2 : 4;
+  if ((d * esize) % 16 != 0) return fail(SCFA_ERR_UNSUPPORTED, "row of %d bytes is not a multiple of 16", d * esize);
+  if (d * esize > 4096) return fail(SCFA_ERR_UNSUPPORTED, "row of %d bytes exceeds 4096", d * esize);
+  if ((long long)B * H > 65535) return fail(SCFA_ERR_UNSUPPORTED, "B*H = %lld exceeds 65535", (long long)B * H);
+  const long long BH = (long long)B * H;
+  const long long Tm = n > T ? n : T;
+  if (BH * Tm >= (1ll << 31) || BH * Tm * d >= (1ll << 40)) return fail(SCFA_ERR_INVALID_ARGUMENT, "tensors too large");
+  int rc;
+  if ((rc = check_ptr(dst, BH * T * d, 16, "dst")) || (rc = check_ptr(index, BH * n, 4, "index"))) return rc;
+  scfa::RowArgs r{nullptr, index, dst, (int)BH, n, T, d * esize / 16};
+  const hipError_t e = scfa::launch_zero_rows(r, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "zero rows");
+  return ok();
 }
 
 size_t scfa_workspace_size(int op, int B, int H, int Tq, int Tk, int d, int block, int n_buckets) {

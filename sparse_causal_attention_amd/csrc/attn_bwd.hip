@@ -167,19 +167,20 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qb * BS + 32 * w + col;
   const bool qvalid = qrow < a.Tq;
-  const size_t qoff = (size_t)bh * a.Tq;
-  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + qoff * D;
-  const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + qoff * D;
-  const uint16_t *O = static_cast<const uint16_t *>(a.o) + qoff * D;
-  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
-  const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
+  const size_t qoff = (size_t)bh * a.Tq;  // view-indexed arrays (positions, buckets, rows)
+  const size_t qoo = (size_t)bh * a.Tqo;  // the forward's outputs (o, lse) and dq
+  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + (size_t)bh * a.Tqs * D;
+  const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + (size_t)bh * a.Tqs * D;
+  const uint16_t *O = static_cast<const uint16_t *>(a.o) + qoo * D;
+  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tks * D;
+  const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tks * D;
 
   // Loads that depend only on this lane's own row go first: issued after the
   // list and chunk copies, a wait for them would also wait for those copies.
   int qsrc_raw = a.q_rows && qvalid ? a.q_rows[qoff + qrow] : qrow;  // clamped where used
   // lse (and O below) are read at the caller's row when outputs live there
-  const int lrow = a.orig_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
-  float lse_raw = qvalid ? a.lse[qoff + lrow] : 0.f;
+  const int lrow = a.orig_rows && qvalid ? min(max(qsrc_raw, 0), a.Tqs - 1) : qrow;
+  float lse_raw = qvalid ? a.lse[qoo + lrow] : 0.f;
   int my_idx = kIdxTailQ, my_hash = 0;
   if (qvalid) {
     my_idx = MODE == kDense ? qrow : a.q_idx[qoff + qrow];
@@ -195,8 +196,8 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
   auto issue = [&](KVBufB<D> &b, const Chunk &c) {
     if constexpr (KROWS) {
-      dma_matrix_rows<D, NW>(b.k, K, a.Tk, drn);
-      dma_matrix_rows<D, NW>(b.v, V, a.Tk, drn);
+      dma_matrix_rows<D, NW>(b.k, K, a.Tks, drn);
+      dma_matrix_rows<D, NW>(b.v, V, a.Tks, drn);
     } else {
       dma_matrix<D, NW>(b.k, K, c.r0, c.nvalid, dmo);
       dma_matrix<D, NW>(b.v, V, c.r0, c.nvalid, dmo);
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.r0, nxt.nvalid);
   }
 
-  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
+  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tqs - 1) : qrow;
   bf16x8 qf[D / 16], dof[D / 16];
   float dsum = 0.f;
 #pragma unroll
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     // The output row: lrow from the prologue (the caller's row with orig_rows)
     // where one more live register costs no spill, else loaded again here.
     const int orow = MODE != kDense ? lrow : out_row_q(a, bh, qrow_e);
-    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoff + orow) * D;
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + (qoo + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -370,12 +371,12 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int col = lane & 31, half = lane >> 5;
   const int krow = kb * BS + 32 * w + col;
   const bool kvalid_row = krow < a.Tk;
-  const size_t koff = (size_t)bh * a.Tk;
+  const size_t koff = (size_t)bh * a.Tk;  // view-indexed arrays (positions, buckets, rows)
   const size_t qoff = (size_t)bh * a.Tq;
-  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + qoff * D;
-  const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + qoff * D;
-  const uint16_t *K = static_cast<const uint16_t *>(a.k) + koff * D;
-  const uint16_t *V = static_cast<const uint16_t *>(a.v) + koff * D;
+  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + (size_t)bh * a.Tqs * D;
+  const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + (size_t)bh * a.Tqs * D;
+  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tks * D;
+  const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tks * D;
   const float *lse2g = a.delta + a.delta_half + qoff;
   const float *delg = a.delta + qoff;
 
@@ -403,8 +404,8 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
   DmaRows<D, NW> drn;  // QROWS: source rows of the next chunk to copy
   auto issue = [&](QGBuf<D> &b, const Chunk &c) {
     if constexpr (QROWS) {
-      dma_matrix_rows<D, NW>(b.q, Q, a.Tq, drn);
-      dma_matrix_rows<D, NW>(b.g, dO, a.Tq, drn);
+      dma_matrix_rows<D, NW>(b.q, Q, a.Tqs, drn);
+      dma_matrix_rows<D, NW>(b.g, dO, a.Tqs, drn);
     } else {
       dma_matrix<D, NW>(b.q, Q, c.r0, c.nvalid, dmo);
       dma_matrix<D, NW>(b.g, dO, c.r0, c.nvalid, dmo);
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (have_next) dma_rows_load<D, NW>(drn, qrows, nxt.r0, nxt.nvalid);
   }
 
-  const int ksrc = a.k_rows && kvalid_row ? min(max(ksrc_raw, 0), a.Tk - 1) : krow;
+  const int ksrc = a.k_rows && kvalid_row ? min(max(ksrc_raw, 0), a.Tks - 1) : krow;
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -594,8 +595,8 @@ __global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(D 
     // clamped k_rows entry, kept from the prologue where one more live
     // register costs no spill, else loaded again here).
     const size_t orow = STORE ? (size_t)out_row_k(a, bh, krow_e) : a.orig_rows ? (size_t)ksrc : (size_t)krow_e;
-    uint16_t *dK = static_cast<uint16_t *>(a.dk) + (koff + orow) * D;
-    uint16_t *dV = static_cast<uint16_t *>(a.dv) + (koff + orow) * D;
+    uint16_t *dK = static_cast<uint16_t *>(a.dk) + ((size_t)bh * a.Tko + orow) * D;
+    uint16_t *dV = static_cast<uint16_t *>(a.dv) + ((size_t)bh * a.Tko + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -627,9 +628,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(AttnArgs a) {
   if (valid) {
     const long long bh = row / a.Tq;
     const int i = (int)(row - bh * a.Tq);
-    const int src = a.q_rows ? min(max(a.q_rows[row], 0), a.Tq - 1) : i;
-    const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + ((size_t)bh * a.Tq + src) * D;
-    const size_t orow = a.orig_rows ? (size_t)bh * a.Tq + src : (size_t)row;  // o and lse at the caller's rows
+    const int src = a.q_rows ? min(max(a.q_rows[row], 0), a.Tqs - 1) : i;
+    const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + ((size_t)bh * a.Tqs + src) * D;
+    const size_t orow = a.orig_rows ? (size_t)bh * a.Tqo + src : (size_t)row;  // o and lse at the caller's rows
     const uint16_t *O = static_cast<const uint16_t *>(a.o) + orow * D;
     lse = a.lse[orow];
 #pragma unroll
@@ -700,7 +701,7 @@ __global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
   const int qb = wg % a.nq;
   const int w = threadIdx.x >> 6;
   const int qw = w % QW, mh = w / QW;
-  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
+  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tks * D;
   const uint16_t *DS = static_cast<const uint16_t *>(a.ds);
   const size_t row = (size_t)bh * a.nq + qb;
   LiveList rl{min(a.row_cnt[row], a.nk), 0, a.row_list + row * a.nk, a.nk, 0, 0};
@@ -718,7 +719,7 @@ __global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
   auto issue = [&](DsBuf<D, BS> &b, const Chunk &c) {
-    if constexpr (KROWS) dma_matrix_rows<D, NW>(b.k, K, a.Tk, drn);
+    if constexpr (KROWS) dma_matrix_rows<D, NW>(b.k, K, a.Tks, drn);
     else dma_matrix<D, NW>(b.k, K, c.r0, c.nvalid, dmk);
     // (an entry without a slot, which lists from the builder never have, reads tile 0)
     const size_t slot = (size_t)max(min(c.slot, (int)min(a.ds_tiles - 1, (long long)INT32_MAX)), 0);
@@ -779,7 +780,7 @@ __global__ __launch_bounds__(BS / 16 * 64) void k_bwd_dq_ds_bf16(AttnArgs a) {
   asm volatile("" : "+v"(tid));
   const int qrow_e = qb * BS + 32 * ((tid >> 6) % QW) + (tid & 31), half_e = (tid >> 5) & 1;
   if (qrow_e < a.Tq) {
-    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + ((size_t)bh * a.Tq + out_row_q(a, bh, qrow_e)) * D;
+    uint16_t *dQ = static_cast<uint16_t *>(a.dq) + ((size_t)bh * a.Tqo + out_row_q(a, bh, qrow_e)) * D;
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll

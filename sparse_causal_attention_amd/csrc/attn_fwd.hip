@@ -114,8 +114,8 @@ constexpr float kRescaleLog2 = 8.f;
 template <int MODE, int D, int NW>
 __device__ __forceinline__ void issue_kv_rows(KVBuf<D> &b, const AttnArgs &a, const uint16_t *K, const uint16_t *V,
                                               int bh, const ChunkPos &c, const DmaRows<D, NW> &dr) {
-  dma_matrix_rows<D, NW>(b.k, K, a.Tk, dr);
-  dma_matrix_rows<D, NW>(b.v, V, a.Tk, dr);
+  dma_matrix_rows<D, NW>(b.k, K, a.Tks, dr);
+  dma_matrix_rows<D, NW>(b.v, V, a.Tks, dr);
   if (MODE != kDense && !(c.free && c.kvalid == kChunk)) {
     const int w = threadIdx.x >> 6;
     if (w == 0) dma_vec(b.idx, a.k_idx + (size_t)bh * a.Tk, c.k0, c.kvalid);
@@ -153,9 +153,9 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qb * BS + 32 * qw + col;
   const bool qvalid = qrow < a.Tq;
-  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + (size_t)bh * a.Tq * D;
-  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tk * D;
-  const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tk * D;
+  const uint16_t *Q = static_cast<const uint16_t *>(a.q) + (size_t)bh * a.Tqs * D;
+  const uint16_t *K = static_cast<const uint16_t *>(a.k) + (size_t)bh * a.Tks * D;
+  const uint16_t *V = static_cast<const uint16_t *>(a.v) + (size_t)bh * a.Tks * D;
 
   // Loads that depend only on this lane's own row go first: issued after the
   // list and chunk copies, a wait for them would also wait for those copies.
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   }
   const LaneOffsets<D> lo = lane_offsets<D>();
 
-  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tq - 1) : qrow;
+  const int qsrc = a.q_rows && qvalid ? min(max(qsrc_raw, 0), a.Tqs - 1) : qrow;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
@@ -323,8 +323,8 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow_e < a.Tq) {
-    const int orow = a.orig_rows ? min(max(orow_raw, 0), a.Tq - 1) : qrow_e;  // as out_row_q
-    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tq + orow) * D;
+    const int orow = a.orig_rows ? min(max(orow_raw, 0), a.Tqs - 1) : qrow_e;  // as out_row_q
+    uint16_t *O = static_cast<uint16_t *>(a.out_o) + ((size_t)bh * a.Tqo + orow) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
                                      pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv));
         *reinterpret_cast<uint2 *>(O + d0) = val;
       }
-    if (half_e == 0) a.out_lse[(size_t)bh * a.Tq + orow] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+    if (half_e == 0) a.out_lse[(size_t)bh * a.Tqo + orow] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
   }
 }
 

@@ -84,6 +84,11 @@ __device__ __forceinline__ void load_r_step(double (&r)[16], const_double *Rs, i
   for (int i = 0; i < 16; ++i) r[i] = p[i];
 }
 
+// Row of x that holds token t of sequence bh (see LshArgs::x_rows).
+__device__ __forceinline__ size_t lsh_row(const LshArgs &a, int bh, int t) {
+  return (size_t)bh * a.Tx + (a.x_rows ? min(max(a.x_rows[(size_t)bh * a.T + t], 0), a.Tx - 1) : t);
+}
+
 template <int D, int CG, bool F32>
 __global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a, const double *R64, int32_t *hist, int nchunks) {
   constexpr int ES = F32 ? 4 : 2;          // bytes per coordinate
@@ -105,15 +110,15 @@ __global__ __launch_bounds__(kHashThreads) void k_lsh_hash(LshArgs a, const doub
   const int half = a.nb / 2;
   const int ngroups = (half + CG - 1) / CG;
   const_double *Rh = (const_double *)(R64 + (size_t)h * ngroups * D * CG);
-  const char *xb = static_cast<const char *>(a.x) + (size_t)bh * a.T * RB;
+  const char *xb = static_cast<const char *>(a.x);
 
   // staging: this thread copies piece (tid & 3) of rows (tid >> 2) + 64j,
   // j = 0..3; rows past the end repeat the last row (never compared)
   const int sr = tid >> 2, sp = (tid & 3) * 16;
-  const char *src0 = xb + (size_t)min(t0 + sr, a.T - 1) * RB + sp;
-  const char *src1 = xb + (size_t)min(t0 + sr + 64, a.T - 1) * RB + sp;
-  const char *src2 = xb + (size_t)min(t0 + sr + 128, a.T - 1) * RB + sp;
-  const char *src3 = xb + (size_t)min(t0 + sr + 192, a.T - 1) * RB + sp;
+  const char *src0 = xb + lsh_row(a, bh, min(t0 + sr, a.T - 1)) * RB + sp;
+  const char *src1 = xb + lsh_row(a, bh, min(t0 + sr + 64, a.T - 1)) * RB + sp;
+  const char *src2 = xb + lsh_row(a, bh, min(t0 + sr + 128, a.T - 1)) * RB + sp;
+  const char *src3 = xb + lsh_row(a, bh, min(t0 + sr + 192, a.T - 1)) * RB + sp;
   const int dst0 = sr * kSlabPitch + sp;  // rows +64j: + 64 * j * kSlabPitch
   uint4 st0 = *reinterpret_cast<const uint4 *>(src0);
   uint4 st1 = *reinterpret_cast<const uint4 *>(src1);
@@ -370,16 +375,17 @@ __global__ __launch_bounds__(kHashThreads) __attribute__((amdgpu_waves_per_eu(4)
 
   // B operands: the wave's 64 tokens as two 32-token tiles (x rows, 8
   // coordinates per lane and k-step).
-  const uint16_t *X = static_cast<const uint16_t *>(a.x) + (size_t)bh * a.T * D;
+  const uint16_t *X = static_cast<const uint16_t *>(a.x);
   bf16x8 xf[2][KK];
   int tok[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     tok[n] = t0 + 64 * w + 32 * n + col;
     const bool tv = tok[n] < a.T;
+    const size_t xr = tv ? lsh_row(a, bh, tok[n]) : 0;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      xf[n][kk] = as_bf16x8(tv ? ld16(X + (size_t)tok[n] * D + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0));
+      xf[n][kk] = as_bf16x8(tv ? ld16(X + xr * D + 16 * kk + 8 * hf) : make_uint4(0, 0, 0, 0));
   }
   // R tiles go straight from global memory to LDS (no registers held for them);
   // each wave copies 64 consecutive fragments per piece, lane l to slot 64 w + l.
@@ -503,7 +509,7 @@ __global__ __launch_bounds__(256) void k_lsh_fallback(LshArgs a, int32_t *hist, 
   for (int i = gw; i < n; i += nw) {
     const int e = a.fb_list[i];
     const int bh = e / a.T, t = e % a.T, h = bh % a.H;
-    const uint16_t *xr = static_cast<const uint16_t *>(a.x) + (size_t)e * D;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x) + lsh_row(a, bh, t) * D;
     // the row, one coordinate per lane (two for D = 128)
     const float x0 = bf16_bits_to_float(xr[lane]);
     const float x1 = D > 64 ? bf16_bits_to_float(xr[(64 + lane) % D]) : 0.f;

@@ -10,7 +10,7 @@
 // Pure data movement, bound by HBM bandwidth: each thread moves 16-byte
 // pieces, consecutive threads consecutive pieces of a row, grid-stride.
 // Index values outside the valid range never address memory: a gather writes
-// zeros for them and a scatter drops them.
+// zeros for them, a scatter and a row clear skip them.
 #include "scfa_device.hpp"
 #include "scfa_internal.hpp"
 
@@ -63,6 +63,25 @@ __global__ __launch_bounds__(kRowThreads) void k_scatter_rows(const uint4 *src, 
   }
 }
 
+// Zero rows: dst[bh, index[bh, i], :] = 0 for i < Ts (indices outside [0, Td)
+// are skipped; src is unused).  Clears the rows of dropped tokens in
+// full-length outputs whose kept rows the attention kernels write directly.
+template <int PPR>
+__global__ __launch_bounds__(kRowThreads) void k_zero_rows(const uint4 *, const int32_t *index, uint4 *dst, int Ts,
+                                                            int Td, int ppr_rt) {
+  const int ppr = PPR > 0 ? PPR : ppr_rt;
+  const int rpb = kRowThreads / ppr;
+  const int sub = (int)threadIdx.x / ppr, piece = (int)threadIdx.x - sub * ppr;
+  if (sub >= rpb) return;
+  const size_t bh = blockIdx.y;
+  uint4 *d = dst + bh * (size_t)Td * ppr;
+  const int32_t *ix = index + bh * (size_t)Ts;
+  for (long long i = (long long)blockIdx.x * rpb + sub; i < Ts; i += (long long)gridDim.x * rpb) {
+    const int j = ix[i];
+    if (j >= 0 && j < Td) d[(size_t)j * ppr + piece] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_zero_pieces(uint4 *dst, long long total) {
   const long long stride = (long long)gridDim.x * kRowThreads;
   for (long long p = (long long)blockIdx.x * kRowThreads + threadIdx.x; p < total; p += stride)
@@ -112,6 +131,13 @@ hipError_t launch_scatter_rows(const RowArgs &r, bool zero_fill, hipStream_t s) 
   }
   if ((long long)r.BH * r.Ts * r.ppr == 0 || r.Td == 0) return hipSuccess;
   SCFA_ROWS_LAUNCH(k_scatter_rows, rows_grid(r.BH, r.Ts, r.ppr), r, r.Ts, r.Td);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(const RowArgs &r, hipStream_t s) {
+  if ((long long)r.BH * r.Ts * r.ppr == 0 || r.Td == 0) return hipSuccess;
+  if (r.ppr > kRowThreads || r.BH > 65535) return hipErrorInvalidValue;
+  SCFA_ROWS_LAUNCH(k_zero_rows, rows_grid(r.BH, r.Ts, r.ppr), r, r.Ts, r.Td);
   return hipGetLastError();
 }
 

@@ -26,6 +26,11 @@ struct AttnArgs {
   // optional row indirection [BH, T]: row i of Q (dO) is row q_rows[i] of q (dout), row j of K, V is
   // row k_rows[j] of k, v (NULL = identity); outputs stay indexed by i and j
   const int32_t *q_rows, *k_rows;
+  // Rows per head of the caller's tensors: q and dout hold Tqs rows per head, k and v Tks (with row
+  // indirection these may differ from the view's Tq, Tk, e.g. full-length tensors read at the kept
+  // positions); the q-side outputs (o, lse, dq, and the backward's o / lse inputs) hold Tqo rows per
+  // head and the k-side ones (dk, dv) Tko: Tqs / Tks with orig_rows, else Tq / Tk.
+  int Tqs, Tks, Tqo, Tko;
   // live-tile lists (NULL in dense mode)
   const int32_t *row_cnt, *row_list;  // [BH, nq], [BH, nq, nk]
   const int32_t *col_cnt, *col_list;  // [BH, nk], [BH, nk, nq]
@@ -57,7 +62,7 @@ struct AttnArgs {
 
 // Packed ragged heads: rebase every per-head pointer of head bh so that the
 // kernels' usual addressing (row bh*Tq + i) lands on packed row q_off[bh] + i,
-// and set Tq, Tk to this head's lengths (clamped into [0, max]).  esize is the
+// and set Tq, Tk (and the caller row counts) to this head's lengths (clamped into [0, max]).  esize is the
 // element size of the [rows, d] tensors.  Returns whether the head is ragged.
 __device__ __forceinline__ bool varlen_head(AttnArgs &a, int bh, int esize) {
   if (a.q_off == nullptr) return false;
@@ -89,18 +94,18 @@ __device__ __forceinline__ bool varlen_head(AttnArgs &a, int bh, int esize) {
   if (a.k_idx) a.k_idx += sk;
   if (a.k_hash) a.k_hash += sk;
   if (a.k_rows) a.k_rows += sk;
-  a.Tq = Tq;
-  a.Tk = Tk;
+  a.Tq = a.Tqs = a.Tqo = Tq;  // ragged heads have no row indirection: every tensor is in view order
+  a.Tk = a.Tks = a.Tko = Tk;
   return true;
 }
 
 // Caller row of view query row i (view key row j): through the permutation when
 // outputs go to the caller's rows, clamped into the head.
 __device__ __forceinline__ int out_row_q(const AttnArgs &a, size_t bh, int i) {
-  return a.orig_rows ? min(max(a.q_rows[bh * a.Tq + i], 0), a.Tq - 1) : i;
+  return a.orig_rows ? min(max(a.q_rows[bh * a.Tq + i], 0), a.Tqs - 1) : i;
 }
 __device__ __forceinline__ int out_row_k(const AttnArgs &a, size_t bh, int j) {
-  return a.orig_rows ? min(max(a.k_rows[bh * a.Tk + j], 0), a.Tk - 1) : j;
+  return a.orig_rows ? min(max(a.k_rows[bh * a.Tk + j], 0), a.Tks - 1) : j;
 }
 
 // Row gather / scatter: [BH, Ts, row] <-> [BH, Td, row], rows of ppr 16-byte
@@ -139,6 +144,10 @@ inline size_t meta_seg_bytes(size_t BH, size_t nq, size_t nk, int block) {
 
 struct LshArgs {
   const void *x;
+  // Row indirection (nullable): token t of sequence bh is row x_rows[bh*T + t] (clamped into
+  // [0, Tx)) of x, which has Tx rows per head; NULL = row t, Tx = T.
+  const int32_t *x_rows;
+  int Tx;
   const int32_t *idx;  // nullable
   const float *R;      // [H, d, nb/2]
   int nb, B, H, T, d, dtype;
@@ -173,6 +182,8 @@ int report_error(int code, const char *msg);
 
 hipError_t launch_gather_rows(const RowArgs &r, hipStream_t s);
 hipError_t launch_scatter_rows(const RowArgs &r, bool zero_fill, hipStream_t s);
+// dst[bh, index[bh, i]] = 0 for i < Ts (src unused)
+hipError_t launch_zero_rows(const RowArgs &r, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const AttnArgs &a, int mode, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs &a, int mode, hipStream_t s);
 // part: bit 0 = dQ (+ D = rowsum(dO * O)), bit 1 = dK/dV (reads D).

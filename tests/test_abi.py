@@ -100,9 +100,10 @@ def test_hash_entry_points_require_hashes_and_positions():
 def test_lsh_sort_validation():
     lib = _lib.load()
 
-    def call(nb=16, d=64, dtype=0, flags=0, x=P, R=P2, comp=None, comp_s=None, nws=1 << 30):
-        return lib.scfa_lsh_bucket_sort(x, None, R, nb, 1, 2, 1000, d, dtype, flags, P2, P2, P2, P, comp, comp_s,
-                                        P, nws, None)
+    def call(nb=16, d=64, dtype=0, flags=0, x=P, R=P2, comp=None, comp_s=None, nws=1 << 30, x_rows=None, T_x=0,
+             xs=P):
+        return lib.scfa_lsh_bucket_sort(x, x_rows, T_x, None, R, nb, 1, 2, 1000, d, dtype, flags, P2, P2, P2, xs,
+                                        comp, comp_s, P, nws, None)
 
     assert call(nb=3) == _lib.ERR_UNSUPPORTED
     assert call(nb=0) == _lib.ERR_UNSUPPORTED
@@ -114,6 +115,11 @@ def test_lsh_sort_validation():
     assert call(R=P2 + 2) == _lib.ERR_INVALID_ARGUMENT
     assert call(comp=P) == _lib.ERR_INVALID_ARGUMENT  # companion without output
     assert call(nws=100) == _lib.ERR_WORKSPACE_TOO_SMALL
+    # row indirection into a longer x: needs x_rows, no row copies, 4-byte aligned rows
+    assert call(T_x=5000) == _lib.ERR_INVALID_ARGUMENT
+    assert call(T_x=-1) == _lib.ERR_INVALID_ARGUMENT
+    assert call(x_rows=P2, T_x=5000) == _lib.ERR_UNSUPPORTED  # x_sorted requested
+    assert call(x_rows=P2 + 2, T_x=5000, xs=None) == _lib.ERR_INVALID_ARGUMENT
 
 
 def test_block_meta_validation():
@@ -149,15 +155,21 @@ def test_block_meta_exact_validation():
 def test_row_indirection_validation():
     lib = _lib.load()
 
-    def fwd(q_rows=None, k_rows=None, dtype=0):
-        return lib.scfa_attn_fwd_lists(P, P, P, P2, P2, None, None, q_rows, k_rows, P2, P2, P, P2, 1, 1, 100, 100,
-                                       64, 64, 0.125, dtype, 0, None)
+    def fwd(q_rows=None, k_rows=None, dtype=0, tqs=0, tks=0, B=1):
+        return lib.scfa_attn_fwd_lists(P, P, P, P2, P2, None, None, q_rows, k_rows, tqs, tks, P2, P2, P, P2, B, 1,
+                                       100, 100, 64, 64, 0.125, dtype, 0, None)
 
     assert fwd(q_rows=P2 + 2) == _lib.ERR_INVALID_ARGUMENT  # 4-byte alignment
     assert fwd(k_rows=P2 + 1) == _lib.ERR_INVALID_ARGUMENT
     assert fwd(q_rows=P2, dtype=1) == _lib.ERR_UNSUPPORTED  # bf16 only
-    assert lib.scfa_attn_bwd_dkdv_lists(P, P, P, P2, P, P2, P2, P2, None, None, None, P2 + 3, P2, P2, P, P, 1, 1,
-                                        100, 100, 64, 64, 0.125, 0, 0, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.scfa_attn_bwd_dkdv_lists(P, P, P, P2, P, P2, P2, P2, None, None, None, P2 + 3, 0, 0, P2, P2, P, P, 1,
+                                        1, 100, 100, 64, 64, 0.125, 0, 0, None) == _lib.ERR_INVALID_ARGUMENT
+    # caller tensors of another length need the matching rows array, and sizes >= 0 within the 2^31 bound
+    assert fwd(tqs=400) == _lib.ERR_INVALID_ARGUMENT
+    assert fwd(k_rows=P2, tqs=400) == _lib.ERR_INVALID_ARGUMENT
+    assert fwd(q_rows=P2, k_rows=P2, tqs=-3) == _lib.ERR_INVALID_ARGUMENT
+    assert fwd(q_rows=P2, k_rows=P2, tqs=1 << 26, B=64) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.scfa_attn_bwd_prep(P, P2, P, None, 400, P2, 1, 1, 100, 64, 0, 0, None) == _lib.ERR_INVALID_ARGUMENT
 
 
 def test_workspace_sizes():
@@ -196,8 +208,8 @@ def test_stored_ds_validation():
     lib = _lib.load()
 
     def dq(qi=P2, dtype=0, flags=0, tiles=10, ds=P):
-        return lib.scfa_attn_bwd_dq_ds_lists(P, P, P, P, P2, P, qi, qi, None, None, None, None, P2, P2, P2, P2, ds,
-                                             tiles, P, P2, 1, 1, 100, 100, 64, 64, 0.125, dtype, flags, None)
+        return lib.scfa_attn_bwd_dq_ds_lists(P, P, P, P, P2, P, qi, qi, None, None, None, None, 0, 0, P2, P2, P2, P2,
+                                             ds, tiles, P, P2, 1, 1, 100, 100, 64, 64, 0.125, dtype, flags, None)
 
     assert dq(qi=None) == _lib.ERR_UNSUPPORTED  # dense: no lists, no slots
     assert dq(dtype=1) == _lib.ERR_UNSUPPORTED  # bf16 only
@@ -206,8 +218,8 @@ def test_stored_ds_validation():
     assert dq(ds=P + 8) == _lib.ERR_INVALID_ARGUMENT  # 16-byte alignment
     assert lib.scfa_tile_slots(P2, P2, P2, P2, 1, 1, 100, 100, 96, P2, P2, None) == _lib.ERR_UNSUPPORTED
     assert lib.scfa_tile_slots(P2, P2, P2, P2, 1, 1, 100, 100, 64, None, P2, None) == _lib.ERR_INVALID_ARGUMENT
-    assert lib.scfa_attn_bwd_prep(P, P2, P, None, P2, 1, 1, 100, 64, 1, 0, None) == _lib.ERR_UNSUPPORTED
-    assert lib.scfa_attn_bwd_prep(P, P2, P, None, P2, 1, 1, 100, 64, 0, _lib.FLAG_ORIG_ROWS, None) == \
+    assert lib.scfa_attn_bwd_prep(P, P2, P, None, 0, P2, 1, 1, 100, 64, 1, 0, None) == _lib.ERR_UNSUPPORTED
+    assert lib.scfa_attn_bwd_prep(P, P2, P, None, 0, P2, 1, 1, 100, 64, 0, _lib.FLAG_ORIG_ROWS, None) == \
         _lib.ERR_INVALID_ARGUMENT  # caller rows need q_rows
 
 
@@ -215,8 +227,8 @@ def test_orig_rows_flag_validation():
     lib = _lib.load()
 
     def fwd(q_rows=None, k_rows=None, flags=_lib.FLAG_ORIG_ROWS):
-        return lib.scfa_attn_fwd_lists(P, P, P, P2, P2, None, None, q_rows, k_rows, P2, P2, P, P2, 1, 1, 100, 100,
-                                       64, 64, 0.125, 0, flags, None)
+        return lib.scfa_attn_fwd_lists(P, P, P, P2, P2, None, None, q_rows, k_rows, 0, 0, P2, P2, P, P2, 1, 1, 100,
+                                       100, 64, 64, 0.125, 0, flags, None)
 
     assert fwd() == _lib.ERR_INVALID_ARGUMENT  # no row indirection
     assert fwd(q_rows=P2) == _lib.ERR_INVALID_ARGUMENT  # both needed
@@ -274,3 +286,14 @@ def test_row_gather_scatter_validation():
     assert g(d=4096) == _lib.ERR_UNSUPPORTED  # 8 KiB rows: more than 256 pieces per row
     assert s(B=256, H=256) == _lib.ERR_UNSUPPORTED  # B*H beyond the grid's second dimension
     assert lib.scfa_last_error().decode()
+
+    def z(dst=P, index=P2, B=1, H=2, n=50, T=100, d=64, dtype=0):
+        return lib.scfa_zero_rows(dst, index, B, H, n, T, d, dtype, None)
+
+    assert z(dtype=3) == _lib.ERR_UNSUPPORTED
+    assert z(d=4) == _lib.ERR_UNSUPPORTED  # 8-byte rows
+    assert z(n=-1) == _lib.ERR_INVALID_ARGUMENT
+    assert z(dst=None) == _lib.ERR_INVALID_ARGUMENT
+    assert z(dst=P + 8) == _lib.ERR_INVALID_ARGUMENT
+    assert z(index=P2 + 2) == _lib.ERR_INVALID_ARGUMENT
+    assert z(B=256, H=256) == _lib.ERR_UNSUPPORTED

@@ -53,3 +53,30 @@ def test_out_of_range_indices():
     np.testing.assert_array_equal(s[0, 0, 0], src[0, 0, 0])
     np.testing.assert_array_equal(s[0, 0, 4], src[0, 0, 3])
     assert np.all(s[0, 0, 1:4] == 0)
+
+
+def test_zero_rows_of_the_dropped_positions_complete_an_uncompaction():
+    """Scattering the kept rows over any prior contents and then clearing the dropped rows gives the
+    zero-filled scatter; the cleared rows equal NumPy boolean-mask assignment."""
+    rng = np.random.default_rng(3)
+    B, H, T, n = 2, 3, 90, 61
+    src = rng.standard_normal((B, H, n, 5))
+    keep = np.stack([np.stack([np.sort(rng.choice(T, n, replace=False)) for _ in range(H)]) for _ in range(B)])
+    drop = np.stack([np.stack([np.setdiff1d(np.arange(T), keep[b, h]) for h in range(H)]) for b in range(B)])
+    base = rng.standard_normal((B, H, T, 5))
+    stale = rows.scatter_rows(src, keep, T, zero_fill=False, base=base)
+    np.testing.assert_array_equal(rows.zero_rows(stale, drop), rows.scatter_rows(src, keep, T))
+    masked = np.array(base, copy=True)
+    for b in range(B):
+        for h in range(H):
+            m = np.zeros(T, bool)
+            m[drop[b, h]] = True
+            masked[b, h][m] = 0.0
+    np.testing.assert_array_equal(rows.zero_rows(base, drop), masked)
+
+
+def test_zero_rows_skips_out_of_range_indices():
+    dst = np.ones((1, 1, 4, 2))
+    out = rows.zero_rows(dst, np.array([[[-1, 4, 2, 9]]]))
+    assert np.all(out[0, 0, 2] == 0) and np.all(out[0, 0, [0, 1, 3]] == 1)
+    assert np.all(dst == 1)  # the input is not modified
