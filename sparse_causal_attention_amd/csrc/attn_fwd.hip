@@ -137,16 +137,25 @@ __device__ __forceinline__ void issue_kv_rows(KVBuf<D> &b, const AttnArgs &a, co
 // first-half wave merges the two, as two partial softmaxes over disjoint key
 // sets combine: m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m) (log2 units),
 // O = (acc0 2^(m0-m) + acc1 2^(m1-m)) / l.
-template <int MODE, int D, int BS, bool KROWS>
+//
+// LB: block size of the lists (LB = BS, or LB = 2 BS: each LB-query block of
+// the lists is run as two BS-query groups that walk the same list, every
+// chunk masked on its own rows).  Each query sees the same chunks in the same
+// order, split into the same key halves, as in one LB-query group, so the
+// results are bit-identical; the smaller group runs at twice the groups per CU.
+template <int MODE, int D, int BS, bool KROWS, int LB = BS>
 __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void k_fwd_bf16_ks(
     AttnArgs a) {
   constexpr int QW = BS / 32;
   constexpr int NW = 2 * QW;
+  static_assert(LB == BS || LB == 2 * BS, "a list block covers one or two query groups");
   __shared__ __attribute__((aligned(16))) KVBuf<D> sb[2];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wg / a.nq;
-  const int qb = wg % a.nq;
+  const int ngroups = LB == BS ? a.nq : (a.Tq + BS - 1) / BS;  // query groups per head
+  const int bh = wg / ngroups;
+  const int qb = wg % ngroups;  // this group's queries: qb*BS ..
+  const int qbl = qb / (LB / BS);  // and its row of the lists
   if (varlen_head(a, bh, 2) && qb * BS >= a.Tq) return;  // past this ragged head's queries
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qw = w % QW, kh = w / QW;
@@ -165,14 +174,14 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
     my_idx = MODE == kDense ? qrow : a.q_idx[(size_t)bh * a.Tq + qrow];
     if (MODE == kHash) my_hash = a.q_hash[(size_t)bh * a.Tq + qrow];
   }
-  LiveList rl = row_list<MODE, BS>(a, bh, qb);
+  LiveList rl = row_list<MODE, LB>(a, bh, qbl);
   // Consumed here, where the list window's wait already covers this older load;
   // first used after the chunk copies, its wait would also drain them.
   asm volatile("" : "+v"(qsrc_raw));
   const DmaOffsets<D, NW> dof = dma_offsets<D, NW>();
   const int32_t *krows = KROWS ? a.k_rows + (size_t)bh * a.Tk : nullptr;
   ChunkPos cur;
-  bool have = find_chunk<MODE, BS>(a, rl, qb, 0, 0, cur);
+  bool have = find_chunk<MODE, LB>(a, rl, qbl, 0, 0, cur);
   DmaRows<D, NW> drn;  // KROWS: source rows of the next chunk to copy
   if (have) {
     if constexpr (KROWS) {
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   ChunkPos nxt;
   bool have_next = false;
   if constexpr (KROWS) {
-    have_next = have && find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    have_next = have && find_chunk<MODE, LB>(a, rl, qbl, cur.t, cur.ch + 1, nxt);
     if (have_next) dma_rows_load<D, NW>(drn, krows, nxt.k0, nxt.kvalid);
   }
   const LaneOffsets<D> lo = lane_offsets<D>();
@@ -208,8 +217,8 @@ __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(D 
   while (have) {
     ChunkPos nxt2;
     bool have_next2 = false;
-    if constexpr (KROWS) have_next2 = have_next && find_chunk<MODE, BS>(a, rl, qb, nxt.t, nxt.ch + 1, nxt2);
-    else have_next = find_chunk<MODE, BS>(a, rl, qb, cur.t, cur.ch + 1, nxt);
+    if constexpr (KROWS) have_next2 = have_next && find_chunk<MODE, LB>(a, rl, qbl, nxt.t, nxt.ch + 1, nxt2);
+    else have_next = find_chunk<MODE, LB>(a, rl, qbl, cur.t, cur.ch + 1, nxt);
     wait_vmem();
     __syncthreads();
     if (have_next) {
@@ -428,10 +437,20 @@ __global__ __launch_bounds__(BS) void k_fwd_f32(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
 static hipError_t run_fwd_bf16(const AttnArgs &a, hipStream_t s) {
-  if (a.k_rows)
-    hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s, a);
+  if constexpr (D == 128 && BS == 128) {
+    // 128-query blocks of the lists run as two 64-query groups: the 4-wave groups fit twice per CU
+    // (the 8-wave group once), the same 8 waves per CU with half as many waiting at each barrier.
+    const unsigned grid = (unsigned)(a.BH * ((a.Tq + 63) / 64));
+    if (a.k_rows) hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, 64, true, 128>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, 64, false, 128>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (a.k_rows)
+      hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, true>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s,
+                         a);
+    else
+      hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, BS, false>), dim3((unsigned)(a.BH * a.nq)), dim3(BS / 16 * 64), 0, s,
+                         a);
+  }
   return hipGetLastError();
 }
 template <int MODE, int D, int BS>

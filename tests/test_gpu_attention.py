@@ -288,6 +288,33 @@ def test_row_indirection_bit_identical(mode, d, block, Tq, Tk):
         assert torch.equal(a_, b_)
 
 
+@pytest.mark.parametrize("mode,Tq,Tk", [("hash", 1500, 1400), ("qk", 777, 1000), ("dense", 650, 650)])
+def test_d128_block128_lists_equal_block64_lists(mode, Tq, Tk):
+    """At d = 128 the forward runs every 128-query block of block-128 lists as two 64-query groups walking
+    the same list.  A coarser list only adds chunks whose keys are all masked for a group's queries
+    (exact zero terms, no change of the running max) and tiles masked although free, so the result
+    equals the block-64 lists' bit for bit, through rows and over copies alike."""
+    scfa = _lib()
+    c = synthetic_case(52, B=2, H=2, Tq=Tq, Tk=Tk, d=128, dtype="bf16", mode="hash" if mode == "hash" else "qk",
+                       nb=5, layout="grouped")
+    note(f"[block-128 lists in 64-query groups] {mode} Tq={Tq} Tk={Tk}")
+    q, k, v = (dev(x).to(torch.bfloat16) for x in (c.q, c.k, c.v))
+    if mode == "dense":
+        qi = ki = qh = kh = None
+    else:
+        qi, ki = dev(c.q_idx), dev(c.k_idx)
+        qh, kh = (dev(c.q_hash), dev(c.k_hash)) if mode == "hash" else (None, None)
+    res = []
+    for block in (64, 128):
+        meta = None if mode == "dense" else scfa.block_meta(qi, ki, qh, kh, block=block, with_cols=False, exact=True)
+        res.append(scfa.attn_fwd_lists(q, k, v, qi, ki, qh, kh, meta, block=block))
+    if mode == "hash":
+        res.append(scfa.hash_sparse_fwd(q, k, v, qi, ki, qh, kh, block=128))
+    torch.cuda.synchronize()
+    for o_, l_ in res[1:]:
+        assert torch.equal(o_, res[0][0]) and torch.equal(l_, res[0][1])
+
+
 @pytest.mark.parametrize("d,block", [(64, 64), (128, 128)])
 def test_key_half_merge_with_one_empty_half_and_wide_scores(d, block):
     """The forward splits every 64-key chunk into two halves handled by different waves and merges
