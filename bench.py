@@ -569,22 +569,42 @@ def sweep_ragged(scfa, torch, args):
         Pq, Pk, Pv, Pdo = (padded_of(x) for x in (q, k, v, do))
         mt = dict(H=H, max_Tq=mx, max_Tk=mx, block=block)
 
-        def packed(_):
+        def marked(t):
+            if t:
+                t.mark()
+
+        def packed(t):
+            if t:
+                t.begin()
             meta = scfa.block_meta_varlen(offs, offs, idx, idx, **mt)
+            marked(t)
             o, lse = scfa.attn_fwd_varlen(q, k, v, offs, offs, idx, idx, None, None, meta, **mt)
+            marked(t)
             dq, delta = scfa.attn_bwd_dq_varlen(q, k, v, o, lse, do, offs, offs, idx, idx, None, None, meta, **mt)
+            marked(t)
             scfa.attn_bwd_dkdv_varlen(q, k, v, lse, do, delta, offs, offs, idx, idx, None, None, meta, **mt)
+            marked(t)
             return o
 
-        def padded(_):
+        def padded(t):
+            if t:
+                t.begin()
             meta = scfa.block_meta(pqi, pki, block=block, with_cols=True, exact=True)
+            marked(t)
             o, lse = scfa.attn_fwd_lists(Pq, Pk, Pv, pqi, pki, None, None, meta, block=block)
+            marked(t)
             dq, delta = scfa.attn_bwd_dq_lists(Pq, Pk, Pv, o, lse, Pdo, pqi, pki, None, None, meta, block=block)
+            marked(t)
             scfa.attn_bwd_dkdv_lists(Pq, Pk, Pv, lse, Pdo, delta, pqi, pki, None, None, meta, block=block)
+            marked(t)
             return o
 
-        ms_packed, o1 = _time_steps(torch, packed, args.steps, args.warmup)
-        ms_padded, o2 = _time_steps(torch, padded, args.steps, args.warmup)
+        calls = ["block_meta", "fwd", "bwd_dq", "bwd_dkdv"]
+        t_packed, t_padded = Timer(torch, calls), Timer(torch, calls)
+        ms_packed, o1 = _time_steps(torch, packed, args.steps, args.warmup, t_packed)
+        ms_padded, o2 = _time_steps(torch, padded, args.steps, args.warmup, t_padded)
+        t_packed.collect()
+        t_padded.collect()
         same = bool(torch.equal(o1[sel[have]], o2.reshape(-1, d)[have]))
         print(json.dumps({"sweep": "ragged_heads", "heads": name, "B": B, "H": H, "T": T, "d": d, "block": block,
                           "kept_min": min(kept), "kept_max": mx, "rows_packed": total, "rows_padded": B * H * mx,
@@ -592,6 +612,9 @@ def sweep_ragged(scfa, torch, args):
                           "speedup_packed_vs_padded": round(ms_padded / ms_packed, 3),
                           "qkvdo_bytes_packed": 4 * total * d * 2, "qkvdo_bytes_padded": 4 * B * H * mx * d * 2,
                           "outputs_equal": same,
+                          "packed_per_call_ms": {n: round(t_packed.median_ms(n), 4) for n in calls},
+                          "padded_per_call_ms": {n: round(t_padded.median_ms(n), 4) for n in calls},
+                          "per_call_stat": f"median of {args.steps} HIP-event samples per call",
                           "step": "block lists + QK-sparse fwd + dQ + dK/dV (compacted tensors resident)"}),
               flush=True)
         del q, k, v, do, Pq, Pk, Pv, Pdo
@@ -874,7 +897,9 @@ def bench_workload(scfa, torch, wid, args):
                                                              nd, 1, dcalls)
     nblk = (w.T + blk - 1) // blk
 
-    kern = {"fwd": (f"k_fwd_bf16_ks<{'kQK' if w.mode == 'qk' else 'kHash'},{w.d},{blk},true>", 4.0 * units * w.d)}
+    # at d = 128 and block 128 the Hash-sparse forward runs each 128-query block as two 64-query groups
+    fwd_tmpl = f"{w.d},64,true,128" if (w.mode != "qk" and w.d == 128 and blk == 128) else f"{w.d},{blk},true"
+    kern = {"fwd": (f"k_fwd_bf16_ks<{'kQK' if w.mode == 'qk' else 'kHash'},{fwd_tmpl}>", 4.0 * units * w.d)}
     if w.train:
         kern["bwd_dq"] = (f"k_bwd_dq_bf16<kQK,{w.d},{blk},true>", 2.0 * units * w.d)
         kern["bwd_dkdv"] = (f"k_bwd_dkdv_bf16<kQK,{w.d},{blk},true,false>", 8.0 * units * w.d)

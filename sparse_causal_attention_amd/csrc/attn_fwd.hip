@@ -437,9 +437,13 @@ __global__ __launch_bounds__(BS) void k_fwd_f32(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int MODE, int D, int BS>
 static hipError_t run_fwd_bf16(const AttnArgs &a, hipStream_t s) {
-  if constexpr (D == 128 && BS == 128) {
+  if constexpr (D == 128 && BS == 128 && MODE == kHash) {
     // 128-query blocks of the lists run as two 64-query groups: the 4-wave groups fit twice per CU
     // (the 8-wave group once), the same 8 waves per CU with half as many waiting at each barrier.
+    // Each chunk is copied once per 64 queries instead of 128, which costs more than it saves on long
+    // lists (dense and QK-sparse: equal or 2 % slower at 32k tokens, 21 % slower for dense causal at
+    // 1M tokens, where a head's K and V outgrow the caches) and pays on the short lists of bucketed
+    // attention (7-9 % faster at 64 and 256 buckets).
     const unsigned grid = (unsigned)(a.BH * ((a.Tq + 63) / 64));
     if (a.k_rows) hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, 64, true, 128>), dim3(grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_fwd_bf16_ks<MODE, D, 64, false, 128>), dim3(grid), dim3(256), 0, s, a);

@@ -290,10 +290,11 @@ def test_row_indirection_bit_identical(mode, d, block, Tq, Tk):
 
 @pytest.mark.parametrize("mode,Tq,Tk", [("hash", 1500, 1400), ("qk", 777, 1000), ("dense", 650, 650)])
 def test_d128_block128_lists_equal_block64_lists(mode, Tq, Tk):
-    """At d = 128 the forward runs every 128-query block of block-128 lists as two 64-query groups walking
-    the same list.  A coarser list only adds chunks whose keys are all masked for a group's queries
-    (exact zero terms, no change of the running max) and tiles masked although free, so the result
-    equals the block-64 lists' bit for bit, through rows and over copies alike."""
+    """At d = 128, block-128 lists run as one 128-query group per block (dense, QK-sparse) or as two
+    64-query groups walking the same list (Hash-sparse).  Either way a query sees the chunks of its
+    block-64 list plus chunks whose keys are all masked for it (exact zero terms, no change of the
+    running max), in the same order and key halves, and some free tiles masked, so the result equals
+    the block-64 lists' bit for bit."""
     scfa = _lib()
     c = synthetic_case(52, B=2, H=2, Tq=Tq, Tk=Tk, d=128, dtype="bf16", mode="hash" if mode == "hash" else "qk",
                        nb=5, layout="grouped")
