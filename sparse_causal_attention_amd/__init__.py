@@ -291,6 +291,9 @@ def _view_shapes(q, k, v, q_rows, k_rows):
     """(B, H, Tq, Tk, d, Tq_src, Tk_src): the attention's view has Tq queries and Tk keys (the lengths
     of q_rows / k_rows when given, else of q / k); q (dout) and k, v hold Tq_src and Tk_src rows per head."""
     B, H, Tqs, Tks, d = _attn_shapes(q, k, v)
+    _need(q, "q")
+    _need(k, "k", q.dtype)
+    _need(v, "v", q.dtype)
     Tq = q_rows.shape[2] if q_rows is not None else Tqs
     Tk = k_rows.shape[2] if k_rows is not None else Tks
     _need(q_rows, "q_rows", torch.int32, (B, H, Tq))

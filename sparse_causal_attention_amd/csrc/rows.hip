@@ -76,9 +76,15 @@ __global__ __launch_bounds__(kRowThreads) void k_zero_rows(const uint4 *, const 
   const size_t bh = blockIdx.y;
   uint4 *d = dst + bh * (size_t)Td * ppr;
   const int32_t *ix = index + bh * (size_t)Ts;
-  for (long long i = (long long)blockIdx.x * rpb + sub; i < Ts; i += (long long)gridDim.x * rpb) {
-    const int j = ix[i];
-    if (j >= 0 && j < Td) d[(size_t)j * ppr + piece] = make_uint4(0, 0, 0, 0);
+  // four rows per thread and pass, their indices loaded before any store (no load waits on a store)
+  const long long stride = (long long)gridDim.x * rpb;
+  for (long long i = (long long)blockIdx.x * rpb + sub; i < Ts; i += 4 * stride) {
+    int j[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) j[u] = i + u * stride < Ts ? ix[i + u * stride] : -1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j[u] >= 0 && j[u] < Td) d[(size_t)j[u] * ppr + piece] = make_uint4(0, 0, 0, 0);
   }
 }
 
