@@ -193,3 +193,47 @@ def test_hash_drop_forward_on_full_length_tensors(d, block):
     O = to_np(O2)[0, h]
     check_forward(O[iq], to_np(l2)[0, h][iq], o_ref, lse_ref, "bf16", f"hash drop in place d={d}")
     assert np.all(O[drop[0, h]] == 0)
+
+
+def test_independent_q_and_k_drops_from_tensors_of_different_lengths():
+    """Q kept from a 900-row tensor, K and V from a 1000-row one, with independent kept sets (600 and 700
+    rows): every row count differs (Tq, Tk, Tq_src, Tk_src), and the forward and both backward kernels in
+    place equal the compaction pipeline bit for bit; outputs land at each side's own kept positions."""
+    rng = np.random.default_rng(97)
+    B, H, Tqf, Tkf, nq, nk, d = 2, 2, 900, 1000, 600, 700, 64
+    qf, dof = (bf16_round(rng.standard_normal((B, H, Tqf, d)).astype(np.float32)) for _ in range(2))
+    kf, vf = (bf16_round(rng.standard_normal((B, H, Tkf, d)).astype(np.float32)) for _ in range(2))
+    kq, dq_drop = _keep_drop(rng, B, H, Tqf, nq)
+    kk, dk_drop = _keep_drop(rng, B, H, Tkf, nk)
+    scfa = _scfa()
+    q, do = (dev(x, torch.bfloat16) for x in (qf, dof))
+    k, v = (dev(x, torch.bfloat16) for x in (kf, vf))
+    qi, ki, qdd, kdd = dev(kq), dev(kk), dev(dq_drop), dev(dk_drop)
+    meta = scfa.block_meta(qi, ki, block=64, with_cols=True, exact=True)
+    note("[full rows] independent drops: compaction path")
+    qc, dc = scfa.gather_rows(q, qi), scfa.gather_rows(do, qi)
+    kc, vc = scfa.gather_rows(k, ki), scfa.gather_rows(v, ki)
+    o1, l1 = scfa.attn_fwd_lists(qc, kc, vc, qi, ki, None, None, meta)
+    dq1, de1 = scfa.attn_bwd_dq_lists(qc, kc, vc, o1, l1, dc, qi, ki, None, None, meta)
+    dk1, dv1 = scfa.attn_bwd_dkdv_lists(qc, kc, vc, l1, dc, de1, qi, ki, None, None, meta)
+    ref = [scfa.scatter_rows(o1, qi, Tqf), scfa.scatter_rows(dq1, qi, Tqf), scfa.scatter_rows(dk1, ki, Tkf),
+           scfa.scatter_rows(dv1, ki, Tkf)]
+    note("[full rows] independent drops: in place")
+    rows = dict(q_rows=qi, k_rows=ki, flags=1 << 4)
+    o2, l2 = scfa.attn_fwd_lists(q, k, v, qi, ki, None, None, meta, **rows)
+    dq2, de2 = scfa.attn_bwd_dq_lists(q, k, v, o2, l2, do, qi, ki, None, None, meta, **rows)
+    dk2, dv2 = scfa.attn_bwd_dkdv_lists(q, k, v, l2, do, de2, qi, ki, None, None, meta, **rows)
+    got = [scfa.zero_rows(o2, qdd), scfa.zero_rows(dq2, qdd), scfa.zero_rows(dk2, kdd), scfa.zero_rows(dv2, kdd)]
+    torch.cuda.synchronize()
+    assert o2.shape == (B, H, Tqf, d) and dk2.shape == (B, H, Tkf, d) and l2.shape == (B, H, Tqf)
+    for name, a_, b_ in zip(("o", "dq", "dk", "dv"), ref, got):
+        assert torch.equal(a_, b_), name
+    assert torch.equal(de1, de2)
+    assert torch.equal(torch.gather(l2, 2, qi.long()), l1)
+    b, h = 0, 1
+    Qc, Gc, Kc, Vc = qf[b, h][kq[b, h]], dof[b, h][kq[b, h]], kf[b, h][kk[b, h]], vf[b, h][kk[b, h]]
+    o_ref, lse_ref = A.forward(Qc, Kc, Vc, kq[b, h], kk[b, h], scale=1.0 / np.sqrt(d))
+    g_ref = A.backward(Qc, Kc, Vc, Gc, kq[b, h], kk[b, h], scale=1.0 / np.sqrt(d))
+    O, L, dQ, dK, dV = (to_np(x) for x in (got[0], l2, got[1], got[2], got[3]))
+    check_forward(O[b, h][kq[b, h]], L[b, h][kq[b, h]], o_ref, lse_ref, "bf16", "independent drops")
+    check_grads([dQ[b, h][kq[b, h]], dK[b, h][kk[b, h]], dV[b, h][kk[b, h]]], g_ref, "bf16", "independent drops")
