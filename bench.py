@@ -718,6 +718,26 @@ def _full_length_inputs(w, torch, names, seed):
     return dict(zip(names, full)), keep
 
 
+def time_graph(torch, step, steps):
+    """ms per step with the whole step captured once as a HIP graph and replayed (the host enqueues one graph
+    launch per step instead of every kernel).  The step is warmed up on the capture stream first."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            step(None)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    _warm(torch, lambda _: g.replay(), 3, SETTLE_MS)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
 def _dropped(keep, T, torch):
     """The positions [B,H,T - n] (ascending) that the kept set [B,H,n] leaves out, per head."""
     B, H, n = keep.shape
@@ -866,6 +886,9 @@ def bench_workload(scfa, torch, wid, args):
     ms_per_step = (time.perf_counter() - t0) / steps * 1e3
     timer.collect()
     per_call = {n: round(timer.median_ms(n), 4) for n in calls}
+    ms_eager = ms_per_step
+    if args.graph:
+        ms_per_step = time_graph(torch, step, steps)
     units, tiles = tile_work(meta, w.Tq, w.Tk, blk, torch)
     per_unit = 14.0 if w.train else 4.0
     step_flops = per_unit * units * w.d
@@ -912,6 +935,8 @@ def bench_workload(scfa, torch, wid, args):
         "steps": steps,
         "warmup": warm,
         "ms_per_step": round(ms_per_step, 4),
+        "step_launch": "one HIP graph replay per step" if args.graph else "eager",
+        "ms_per_step_eager": round(ms_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -930,7 +955,7 @@ def bench_workload(scfa, torch, wid, args):
         "speedup_vs_dense_causal_attention_only": round(dense_ms / attn_ms, 3),
         "per_call_ms": per_call,
         "step_median_ms_events": round(timer.step_median_ms(), 4),
-        "per_call_stat": f"median of {steps} HIP-event samples per call",
+        "per_call_stat": f"median of {steps} HIP-event samples per call" + (" (eager steps)" if args.graph else ""),
         "dense_per_call_ms": {n: round(dtimer.median_ms(n), 4) for n in dcalls},
         "roofline": _roofline(kern[dominant][0], kern[dominant][1], per_call[dominant]),
         "kernel_rooflines": {n: _roofline(kn, fl, per_call[n]) for n, (kn, fl) in kern.items()},
@@ -965,6 +990,8 @@ def main():
                     help="QK-sparse heads with their own kept counts: packed heads against the padded layout")
     ap.add_argument("--measure-rows", action="store_true",
                     help="time the row gather / scatter calls instead of the step (one JSON line)")
+    ap.add_argument("--graph", action="store_true",
+                    help="--workload lines: time the step as one HIP graph replay (per-call times stay eager)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB (fp32) before the warmup, for counter scaling")
     args = ap.parse_args()
