@@ -146,28 +146,42 @@ def tile_work(meta, Tq, Tk, block, torch):
 
 
 class Timer:
-    """HIP events between the calls of one step (torch's current stream, which the library uses)."""
+    """HIP events between the calls of one step (torch's current stream, which the library uses).
 
-    def __init__(self, torch, names):
+    ``only`` (names) restricts the events to the boundaries of those calls: events between all calls of the
+    16k step cost about 4 % of its time, two events around one call about 1 %."""
+
+    def __init__(self, torch, names, only=None):
         self.torch = torch
         self.names = names
+        self.only = set(names if only is None else only)
         self.samples = {n: [] for n in names}
         self.pending = []
+        self.i = 0
+
+    def _boundary(self):
+        # boundary i ends call i - 1 and starts call i
+        i = self.i
+        if (i < len(self.names) and self.names[i] in self.only) or (0 < i <= len(self.names) and
+                                                                     self.names[i - 1] in self.only):
+            ev = self.torch.cuda.Event(enable_timing=True)
+            ev.record()
+            self.pending[-1][i] = ev
 
     def begin(self):
-        ev = self.torch.cuda.Event(enable_timing=True)
-        ev.record()
-        self.pending.append([ev])
+        self.i = 0
+        self.pending.append({})
+        self._boundary()
 
     def mark(self):
-        ev = self.torch.cuda.Event(enable_timing=True)
-        ev.record()
-        self.pending[-1].append(ev)
+        self.i += 1
+        self._boundary()
 
     def collect(self):
         for evs in self.pending:
-            for n, a, b in zip(self.names, evs[:-1], evs[1:]):
-                self.samples[n].append(a.elapsed_time(b))
+            for j, n in enumerate(self.names):
+                if j in evs and j + 1 in evs:
+                    self.samples[n].append(evs[j].elapsed_time(evs[j + 1]))
         self.pending = []
 
     def median_ms(self, n):
@@ -370,6 +384,22 @@ DENSE_BLOCKS = (64, 128)
 # Clocks settle after a few tens of milliseconds of work (measured: the first 20 steps after a short warmup
 # run about 12 % slower than the steady state reached after about 40 steps of the 16k training step).
 SETTLE_MS = 50.0
+
+
+def time_with_breakdown(torch, fn, calls, steps, warmup, timed_only=()):
+    """Warm-up, a breakdown pass of `steps` steps with HIP events between all calls, then the timed `steps`
+    steps with events only around the calls in `timed_only`.  Returns (ms per timed step, the last timed
+    step's result, breakdown Timer, timed Timer)."""
+    _warm(torch, fn, warmup, SETTLE_MS)
+    breakdown = Timer(torch, calls)
+    for _ in range(steps):
+        fn(breakdown)
+    torch.cuda.synchronize()
+    breakdown.collect()
+    timed = Timer(torch, calls, only=timed_only)
+    ms, out = _time_steps(torch, fn, steps, 0, timed)
+    timed.collect()
+    return ms, out, breakdown, timed
 
 
 def _warm(torch, fn, n, min_ms=0.0):
@@ -672,12 +702,9 @@ def sweep_buckets(scfa, torch, w, q, k, v, do, qk, nbs, args):
         ds = prepare_ds(scfa, torch, wn, q, k, R, qk, not args.range_lists, args.copy_sorted) if args.stored_ds \
             else None
         calls = step_calls(args.copy_sorted, ds is not None)
-        timer = Timer(torch, calls)
-        ms, (meta, _) = _time_steps(torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists,
-                                                              args.copy_sorted, qk, ds),
-                                    args.steps,
-                                    args.warmup, timer)
-        timer.collect()
+        ms, (meta, _), timer, _ = time_with_breakdown(
+            torch, lambda t: run_step(scfa, wn, q, k, v, do, R, t, not args.range_lists, args.copy_sorted, qk, ds),
+            calls, args.steps, args.warmup)
         units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
         per_call = {n: round(timer.median_ms(n), 4) for n in calls}
         attn_ms = sum(t for n, t in per_call.items() if not n.startswith("lsh"))
@@ -877,15 +904,24 @@ def bench_workload(scfa, torch, wid, args):
     blk, sc = w.block, w.scale
     steps = args.steps if wid != 5 else max(3, min(args.steps, 5))
     warm = _warm(torch, step, args.warmup if wid != 5 else 1, SETTLE_MS)
+    # breakdown pass (events between all calls), then the timed steps with events around the dominant call only
+    _log(f"[bench] per-call breakdown over {steps} steps")
+    breakdown = Timer(torch, calls)
+    for _ in range(steps):
+        step(breakdown)
+    torch.cuda.synchronize()
+    breakdown.collect()
+    per_call = {n: round(breakdown.median_ms(n), 4) for n in calls}
+    dominant = max((n for n in ("fwd", "bwd_dq", "bwd_dkdv") if n in calls), key=lambda n: per_call[n])
     _log(f"[bench] timing {steps} steps")
-    timer = Timer(torch, calls)
+    timer = Timer(torch, calls, only=(dominant,))
     t0 = time.perf_counter()
     for _ in range(steps):
         meta, _ = step(timer)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) / steps * 1e3
     timer.collect()
-    per_call = {n: round(timer.median_ms(n), 4) for n in calls}
+    dominant_ms = round(timer.median_ms(dominant), 4)
     ms_eager = ms_per_step
     if args.graph:
         ms_per_step = time_graph(torch, step, steps)
@@ -926,7 +962,6 @@ def bench_workload(scfa, torch, wid, args):
     if w.train:
         kern["bwd_dq"] = (f"k_bwd_dq_bf16<kQK,{w.d},{blk},true>", 2.0 * units * w.d)
         kern["bwd_dkdv"] = (f"k_bwd_dkdv_bf16<kQK,{w.d},{blk},true,false>", 8.0 * units * w.d)
-    dominant = max(kern, key=lambda n: per_call[n])
     out = {
         "metric": "effective TFLOP/s (executed tiles, % bf16 MFMA peak) + speedup vs dense causal",
         "value": round(value, 3),
@@ -934,6 +969,7 @@ def bench_workload(scfa, torch, wid, args):
         "n_gpus": 1,
         "steps": steps,
         "warmup": warm,
+        "breakdown_steps": steps,
         "ms_per_step": round(ms_per_step, 4),
         "step_launch": "one HIP graph replay per step" if args.graph else "eager",
         "ms_per_step_eager": round(ms_eager, 4),
@@ -954,10 +990,11 @@ def bench_workload(scfa, torch, wid, args):
         "speedup_vs_dense_causal": round(dense_ms / ms_per_step, 3),
         "speedup_vs_dense_causal_attention_only": round(dense_ms / attn_ms, 3),
         "per_call_ms": per_call,
-        "step_median_ms_events": round(timer.step_median_ms(), 4),
-        "per_call_stat": f"median of {steps} HIP-event samples per call" + (" (eager steps)" if args.graph else ""),
+        "step_median_ms_events": round(breakdown.step_median_ms(), 4),
+        "per_call_stat": f"median of {steps} HIP-event samples per call, from {steps} eager steps run before the "
+                         f"timed ones (the timed steps record events only around {dominant})",
         "dense_per_call_ms": {n: round(dtimer.median_ms(n), 4) for n in dcalls},
-        "roofline": _roofline(kern[dominant][0], kern[dominant][1], per_call[dominant]),
+        "roofline": _roofline(kern[dominant][0], kern[dominant][1], dominant_ms),
         "kernel_rooflines": {n: _roofline(kn, fl, per_call[n]) for n, (kn, fl) in kern.items()},
         "cpu_baseline": None,
     }
@@ -1047,10 +1084,21 @@ def main():
         run_step(scfa, w, q, k, v, do, R, exact=not args.range_lists, copy_sorted=args.copy_sorted, qk=qk, ds=ds)
     torch.cuda.synchronize()
 
-    # HIP events between the calls, on the stream the kernels run on, inside the timed region
-    _log(f"[bench] timing {args.steps} steps")
+    # Per-call breakdown first: HIP events between all calls, on the stream the kernels run on, over
+    # `steps` steps; it also picks the dominant attention kernel.  The timed steps then record events only
+    # around that kernel (events between every call would add about 4 % to the step).
     calls = step_calls(args.copy_sorted, ds is not None)
-    timer = Timer(torch, calls)
+    _log(f"[bench] per-call breakdown over {args.steps} steps")
+    breakdown = Timer(torch, calls)
+    for _ in range(args.steps):
+        run_step(scfa, w, q, k, v, do, R, breakdown, exact=not args.range_lists, copy_sorted=args.copy_sorted,
+                 qk=qk, ds=ds)
+    torch.cuda.synchronize()
+    breakdown.collect()
+    per_call = {n: round(breakdown.median_ms(n), 4) for n in calls}
+    dominant = max(("fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: per_call[n])
+    _log(f"[bench] timing {args.steps} steps")
+    timer = Timer(torch, calls, only=(dominant,))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -1060,6 +1108,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     timer.collect()
+    dominant_ms = round(timer.median_ms(dominant), 4)  # measured inside the timed region
 
     units, tiles = tile_work(meta, w.Tq, w.Tk, w.block, torch)
     step_flops = 14.0 * units * w.d
@@ -1078,7 +1127,6 @@ def main():
             torch, lambda b, t: run_dense(scfa, dataclasses.replace(w, block=b), q, k, v, do, t), DENSE_BLOCKS,
             max(3, args.steps // 4), max(1, min(args.warmup, 3)), DENSE_CALLS)
 
-    per_call = {n: round(timer.median_ms(n), 4) for n in calls}
     attn_ms = sum(t for n, t in per_call.items() if not n.startswith("lsh"))
     rows_flag = "false" if args.copy_sorted else "true"
     if ds is None:
@@ -1095,8 +1143,7 @@ def main():
                  "bwd_dkdv": f"k_bwd_dkdv_bf16<kHash,64,64,{rows_flag},true>"}
     # algorithmic flops per launch: the dQ kernel's share is dS K only (2*d per tile unit)
     alg = {"fwd": 4.0 * units * w.d, "bwd_dq": 2.0 * units * w.d, "bwd_dkdv": 8.0 * units * w.d}
-    dominant = max(kernel_flops, key=lambda n: per_call[n])
-    achieved = alg[dominant] / (per_call[dominant] * 1e-3) / 1e12
+    achieved = alg[dominant] / (dominant_ms * 1e-3) / 1e12
     roofline = {
         "kernel": names[dominant],
         "bound": "mfma",
@@ -1107,7 +1154,8 @@ def main():
         "traffic": (measured_traffic("range" if args.range_lists else "exact", "copied" if args.copy_sorted else
                                      "permuted", "stored_ds" if ds is not None else "recompute")
                     if dominant == "bwd_dkdv" else None),
-        "avg_launch_ms": per_call[dominant],
+        "avg_launch_ms": dominant_ms,
+        "avg_launch_stat": f"median of {args.steps} HIP-event samples around its launch in the timed steps",
         "algorithmic_flops_per_launch": alg[dominant],
     }
 
@@ -1144,6 +1192,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "breakdown_steps": args.steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -1178,8 +1227,10 @@ def main():
         "speedup_vs_dense_causal": None if args.no_dense else round(dense_ms / ms_per_step, 3),
         "speedup_vs_dense_causal_excl_lsh": None if args.no_dense else round(dense_ms / attn_ms, 3),
         "per_call_ms": per_call,
-        "step_median_ms_events": round(timer.step_median_ms(), 4),
-        "per_call_stat": f"median of {args.steps} HIP-event samples per call",
+        "step_median_ms_events": round(breakdown.step_median_ms(), 4),
+        "per_call_stat": f"median of {args.steps} HIP-event samples per call, from {args.steps} steps run just "
+                         f"before the timed ones (these record events between all calls; the timed steps only "
+                         f"around {dominant})",
         "dense_per_call_ms": None if args.no_dense else {n: round(dtimer.median_ms(n), 4) for n in DENSE_CALLS},
         "roofline": roofline,
         "kernel_rooflines": kernel_rooflines,

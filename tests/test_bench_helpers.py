@@ -52,3 +52,52 @@ def test_time_dense_keeps_the_fastest_block():
     assert set(by_block) == {64, 128} and by_block[128] < by_block[64]
     assert abs(ms - by_block[128]) < 1e-3
     assert [b for b, _ in seen].count(64) == 4 and [b for b, _ in seen].count(128) == 4
+
+
+class _Event:
+    clock = [0.0]
+
+    def __init__(self, enable_timing=True):
+        self.t = None
+
+    def record(self):
+        _Event.clock[0] += 1.0
+        self.t = _Event.clock[0]
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+class _CudaEv(_Cuda):
+    Event = _Event
+
+
+class _TorchEv:
+    def __init__(self):
+        self.cuda = _CudaEv()
+
+
+def _step(timer, n_calls):
+    timer.begin()
+    for _ in range(n_calls):
+        timer.mark()
+
+
+def test_timer_records_every_boundary_by_default():
+    t = bench.Timer(_TorchEv(), ["a", "b", "c"])
+    _step(t, 3)
+    assert sorted(t.pending[0]) == [0, 1, 2, 3]  # begin + one event after each call
+    t.collect()
+    assert all(t.samples[n] == [1.0] for n in ("a", "b", "c"))
+
+
+def test_timer_only_records_around_the_chosen_call():
+    t = bench.Timer(_TorchEv(), ["a", "b", "c"], only=("b",))
+    _step(t, 3)
+    _step(t, 3)
+    assert [sorted(p) for p in t.pending] == [[1, 2], [1, 2]]  # two events per step, around call b
+    t.collect()
+    assert t.samples["b"] == [1.0, 1.0] and t.samples["a"] == [] and t.samples["c"] == []
+    none = bench.Timer(_TorchEv(), ["a", "b"], only=())
+    _step(none, 2)
+    assert none.pending == [{}]  # no events at all
