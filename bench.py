@@ -397,7 +397,12 @@ def time_with_breakdown(torch, fn, calls, steps, warmup, timed_only=()):
     torch.cuda.synchronize()
     breakdown.collect()
     timed = Timer(torch, calls, only=timed_only)
-    ms, out = _time_steps(torch, fn, steps, 0, timed)
+    t0 = time.perf_counter()  # the breakdown pass ended synchronised
+    out = None
+    for _ in range(steps):
+        out = fn(timed)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
     timed.collect()
     return ms, out, breakdown, timed
 

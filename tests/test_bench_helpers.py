@@ -101,3 +101,22 @@ def test_timer_only_records_around_the_chosen_call():
     none = bench.Timer(_TorchEv(), ["a", "b"], only=())
     _step(none, 2)
     assert none.pending == [{}]  # no events at all
+
+
+def test_time_with_breakdown_runs_breakdown_then_exactly_the_timed_steps(monkeypatch):
+    monkeypatch.setattr(bench, "SETTLE_MS", 0.0)
+    seen = []
+
+    def fn(timer):
+        seen.append(None if timer is None else id(timer))
+        if timer is not None:
+            _step(timer, 3)
+        return len(seen)
+
+    ms, out, bd, timed = bench.time_with_breakdown(_TorchEv(), fn, ["a", "b", "c"], steps=4, warmup=2,
+                                                   timed_only=("c",))
+    assert seen[:2] == [None, None]  # warm-up without events
+    assert seen[2:6] == [id(bd)] * 4 and seen[6:] == [id(timed)] * 4  # nothing between the two passes
+    assert out == 10 and ms >= 0.0
+    assert all(len(bd.samples[n]) == 4 for n in "abc")
+    assert timed.samples["c"] == [1.0] * 4 and timed.samples["a"] == [] and timed.samples["b"] == []
